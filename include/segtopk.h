@@ -1,0 +1,163 @@
+/*
+ * segtopk.h -- segmented (batched) top-k on AMD Instinct MI355X (gfx950).
+ *
+ * One call, batched_topk(), selects for every segment of a batch the k
+ * largest (or smallest) keys, optionally carrying a 32-bit value payload.
+ * Selection is multi-pass most-significant-digit radix selection: each pass
+ * builds a digit histogram over the surviving candidates, scans it to find the
+ * bucket that holds the k-th key, narrows k and the candidate set to that
+ * bucket and folds the digit into a running splitter; a final filter writes
+ * every key beyond the splitter plus exactly enough splitter-equal keys.
+ *   [PR "Implement Segmented TopK using Thread-Block-Clusters", §1.2 Radix
+ *    (digit) top-k, §1.4 Early stop, §1.5 Final filter and output placement]
+ *
+ * The request model (determinism x tie-break x output ordering, their valid
+ * pairings and defaults) follows the CCCL page "Top-K: Determinism,
+ * Tie-Breaking, and Output Ordering".
+ *
+ * All pointers passed to batched_topk() are DEVICE pointers except the two
+ * descriptor structs themselves, which live in host memory and are read
+ * during the call only.  The library never frees or retains caller memory.
+ */
+#ifndef SEGTOPK_H
+#define SEGTOPK_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---------------------------------------------------- */
+#define SEGTOPK_OK 0
+#define SEGTOPK_INVALID_ARGUMENT 1 /* bad pointer, enum, pairing or size      */
+#define SEGTOPK_NOT_SUPPORTED 2    /* valid request this build does not serve */
+#define SEGTOPK_HIP_ERROR 3        /* a HIP runtime call or launch failed     */
+
+/* ---- key types ------------------------------------------------------- */
+/* Keys are compared by numeric value.  Floating-point keys: -0.0 and +0.0
+ * compare equal (either may be selected; the selected key is written with its
+ * own original bit pattern, so a selected -0.0 comes back as -0.0); +inf and
+ * -inf are the largest and smallest values.  NaN keys are outside the
+ * contract (they are ordered above +inf / below -inf by sign, but no result is
+ * promised for them).
+ *   [PR "Fix BlockTopK +/-0.0 handling", Description: Cause / Fix] */
+typedef enum segtopk_key_type {
+    SEGTOPK_KEY_F32 = 0,  /* IEEE binary32                          */
+    SEGTOPK_KEY_BF16 = 1, /* bfloat16 (upper half of a binary32)    */
+    SEGTOPK_KEY_U32 = 2,  /* unsigned 32-bit integer                */
+    SEGTOPK_KEY_I32 = 3,  /* signed 32-bit integer                  */
+    SEGTOPK_KEY_F16 = 4   /* IEEE binary16                          */
+} segtopk_key_type;
+
+/* ---- request --------------------------------------------------------- */
+/* Which end: the MaxKeys/MaxPairs vs MinKeys/MinPairs entry points. */
+typedef enum segtopk_direction { SEGTOPK_MAX = 0, SEGTOPK_MIN = 1 } segtopk_direction;
+
+/* Determinism of the result SET (not of positions).
+ *   [docs "Top-K: Determinism ...", "Determinism (cuda::execution::determinism)"] */
+typedef enum segtopk_determinism {
+    SEGTOPK_NOT_GUARANTEED = 0, /* ties at the boundary: any valid subset      */
+    SEGTOPK_RUN_TO_RUN = 1,     /* same set on every run on this GPU          */
+    SEGTOPK_GPU_TO_GPU = 2      /* same set on every GPU of this architecture */
+} segtopk_determinism;
+
+/* Which tied boundary keys win.  prefer_smaller_index / prefer_larger_index
+ * are valid only together with SEGTOPK_GPU_TO_GPU; unspecified is valid with
+ * every determinism level.  With a deterministic level and unspecified, this
+ * library resolves ties toward the smaller index.
+ *   [docs "Top-K: Determinism ...", "Tie-break" and "Which items are
+ *    selected?" tables] */
+typedef enum segtopk_tie_break {
+    SEGTOPK_TIE_UNSPECIFIED = 0,
+    SEGTOPK_PREFER_SMALLER_INDEX = 1,
+    SEGTOPK_PREFER_LARGER_INDEX = 2
+} segtopk_tie_break;
+
+/* How the selected set is laid out in each output row.
+ *   unsorted       any permutation of the set
+ *   sorted         by key, best first (descending for MAX, ascending for MIN);
+ *                  this library writes the stable order
+ *   stable_sorted  by key, best first; equal keys by source index ascending
+ *   [docs "Top-K: Determinism ...", "Output ordering" table] */
+typedef enum segtopk_ordering {
+    SEGTOPK_UNSORTED = 0,
+    SEGTOPK_SORTED = 1,
+    SEGTOPK_STABLE_SORTED = 2
+} segtopk_ordering;
+
+/* Largest k served with SEGTOPK_SORTED / SEGTOPK_STABLE_SORTED (the sort runs
+ * on-chip); larger k with a sorted ordering returns SEGTOPK_NOT_SUPPORTED.
+ * Unsorted output has no such limit. */
+#define SEGTOPK_MAX_SORTED_K 4096
+
+/* ---- buffers ---------------------------------------------------------- */
+/* Keys: `in` holds offsets[num_segments] elements of `type` (device memory,
+ * aligned to the element size); `out` receives num_segments * k elements,
+ * row-major with a fixed row stride of k. */
+typedef struct segtopk_keys {
+    const void *in;
+    void *out;
+    int32_t type; /* a segtopk_key_type */
+} segtopk_keys;
+
+/* Values: any 32-bit payload aligned with keys.in, copied bit for bit;
+ * `out` has the same num_segments x k shape as the key output.  Pass NULL
+ * (or in == NULL) for a keys-only request. */
+typedef struct segtopk_values {
+    const void *in;
+    void *out;
+} segtopk_values;
+
+/*
+ * batched_topk -- top-k of every segment.
+ *
+ *   keys             key descriptor (host struct, device buffers), required
+ *   values           value descriptor or NULL for keys only
+ *   segment_offsets  device array of num_segments + 1 int64 offsets; segment
+ *                    i is keys.in[segment_offsets[i] .. segment_offsets[i+1]).
+ *                    A negative size (end < begin) is an empty segment.  Each
+ *                    segment must hold fewer than 2^31 keys; the total may
+ *                    exceed 2^31.
+ *   num_segments     number of segments, >= 0
+ *   k                keys kept per segment and the output row stride,
+ *                    0 <= k <= 2^31 - 1.  Segment i writes k_i = min(k, n_i)
+ *                    items to row i; slots k_i .. k-1 are left untouched.
+ *                    k at or above the segment size selects the whole segment.
+ *   direction        segtopk_direction
+ *   determinism      segtopk_determinism
+ *   tie_break        segtopk_tie_break (see the pairing rule above)
+ *   ordering         segtopk_ordering
+ *   stream           HIP stream the work is queued on (NULL: default stream)
+ *
+ * The call is asynchronous: it validates the request, queues kernels on
+ * `stream` and returns without waiting.  It never copies data to the host.
+ * Internal scratch (only for batches with few, long segments) is taken from
+ * the device's stream-ordered memory pool on `stream` and returned to it on
+ * the same stream.  Outputs must not overlap the inputs.  Calls on different
+ * streams are independent.
+ *
+ * Returns SEGTOPK_OK, or SEGTOPK_INVALID_ARGUMENT for a NULL required pointer,
+ * an out-of-range enum, k or num_segments, values.in without values.out, or a
+ * (determinism, tie_break) pair outside the five valid ones; no work is queued
+ * then.  k == 0 or num_segments == 0 returns SEGTOPK_OK with no work.
+ * Offsets that decrease other than as empty segments, or a segment of 2^31 or
+ * more keys, are precondition violations with undefined results.
+ */
+int batched_topk(const segtopk_keys *keys, const segtopk_values *values,
+                 const int64_t *segment_offsets, int64_t num_segments, int64_t k,
+                 int direction, int determinism, int tie_break, int ordering,
+                 hipStream_t stream);
+
+/* Human-readable name of a status code (static storage). */
+const char *segtopk_status_string(int status);
+
+/* Library version as MAJOR * 10000 + MINOR * 100 + PATCH. */
+int segtopk_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SEGTOPK_H */

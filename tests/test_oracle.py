@@ -1,0 +1,340 @@
+"""Pins for the CPU oracle.  None of these checks reuses the oracle's own code
+path: they compare it with values printed on the pages, with a brute-force
+search over subsets (a different algorithm), with library sorts, and with
+invariants that the definition of top-k fixes.
+"""
+import itertools
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def f32_bits(x):
+    return np.asarray(x, dtype=np.float32).view(np.uint32)
+
+
+def as_keys(vals, key_type):
+    """Numeric values -> raw key array of the given type (exact for the inputs used)."""
+    v = np.asarray(vals, dtype=np.float64)
+    if key_type == "f32":
+        return v.astype(np.float32)
+    if key_type == "bf16":
+        return (torch.tensor(v, dtype=torch.float64).to(torch.bfloat16)
+                .view(torch.int16).numpy().view(np.uint16))
+    if key_type == "f16":
+        return v.astype(np.float16).view(np.uint16)
+    if key_type == "u32":
+        return v.astype(np.uint64).astype(np.uint32)
+    if key_type == "i32":
+        return v.astype(np.int64).astype(np.int32)
+    raise ValueError(key_type)
+
+
+def numeric(keys, key_type):
+    """Raw key array -> float64 values, decoded by numpy / torch (not by the oracle)."""
+    if key_type == "f32":
+        return np.asarray(keys).view(np.float32).astype(np.float64)
+    if key_type == "bf16":
+        return torch.from_numpy(np.asarray(keys).view(np.int16).copy()).view(
+            torch.bfloat16).to(torch.float64).numpy()
+    if key_type == "f16":
+        return np.asarray(keys).view(np.float16).astype(np.float64)
+    if key_type == "u32":
+        return np.asarray(keys).view(np.uint32).astype(np.float64)
+    if key_type == "i32":
+        return np.asarray(keys).view(np.int32).astype(np.float64)
+    raise ValueError(key_type)
+
+
+ALL_TYPES = ["f32", "bf16", "f16", "u32", "i32"]
+
+
+# --------------------------------------------------------------------------
+# 1. The worked example printed on the requirements page.
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("key_type", ALL_TYPES)
+def test_worked_example(key_type):
+    with open(os.path.join(GOLDEN, "worked_example_max_k3.json")) as f:
+        g = json.load(f)
+    keys = as_keys(g["keys"], key_type)
+    vals = np.arange(len(keys), dtype=np.uint32)
+    off = np.array([0, len(keys)], dtype=np.int64)
+    k = g["k"]
+    for case, larger in (("gpu_to_gpu/prefer_smaller_index", False),
+                         ("gpu_to_gpu/prefer_larger_index", True)):
+        ok, ov = oracle.batched_topk(keys, off, k, key_type=key_type, values=vals,
+                                     largest=True, prefer_larger=larger)
+        got = [[float(numeric(ok[0, j:j + 1], key_type)[0]), int(ov[0, j])] for j in range(k)]
+        want = g["cases"][case]["stable_sorted"]
+        assert got == [[float(a), b] for a, b in want], case
+        assert sorted(map(tuple, got)) == sorted((float(a), b) for a, b in g["cases"][case]["set"])
+    # not_guaranteed: any valid choice; the oracle's must be one of them.
+    ok, ov = oracle.batched_topk(keys, off, k, key_type=key_type, values=vals, largest=True)
+    ng = g["cases"]["not_guaranteed/unspecified"]
+    got = {(float(numeric(ok[0, j:j + 1], key_type)[0]), int(ov[0, j])) for j in range(k)}
+    must = {(float(a), b) for a, b in ng["must_contain"]}
+    pool = {(float(a), b) for a, b in ng["choose_from"]}
+    assert must <= got and len(got - must) == ng["choose_count"] and (got - must) <= pool
+
+
+# --------------------------------------------------------------------------
+# 2. Brute force over all k-subsets on tiny segments (a different algorithm).
+# --------------------------------------------------------------------------
+ALPHABET = {
+    "f32": [float("-inf"), -1.5, -0.0, 0.0, 1.5, 2.0, float("inf")],
+    "bf16": [float("-inf"), -1.5, -0.0, 0.0, 1.5, 2.0, float("inf")],
+    "f16": [float("-inf"), -1.5, -0.0, 0.0, 1.5, 2.0, float("inf")],
+    "u32": [0, 1, 2, 2 ** 31, 2 ** 32 - 2, 2 ** 32 - 1],
+    "i32": [-(2 ** 31), -1, 0, 1, 2 ** 31 - 1],
+}
+
+
+def brute_force(vals, k, largest, prefer_larger):
+    """Set of indices chosen by exhaustive search: among all k-subsets whose
+    every member is at least as good as every non-member, the one whose
+    ascending index tuple is lexicographically smallest (prefer_smaller) or
+    largest (prefer_larger)."""
+    n = len(vals)
+    kk = min(k, n)
+    best = None
+    for sub in itertools.combinations(range(n), kk):
+        inside = [vals[i] for i in sub]
+        outside = [vals[i] for i in range(n) if i not in sub]
+        if inside and outside:
+            if largest and min(inside) < max(outside):
+                continue
+            if not largest and max(inside) > min(outside):
+                continue
+        if best is None or (sub > best if prefer_larger else sub < best):
+            best = sub
+    return best
+
+
+@pytest.mark.parametrize("key_type", ALL_TYPES)
+def test_brute_force_tiny(key_type):
+    rng = np.random.default_rng(7)
+    alpha = ALPHABET[key_type]
+    for trial in range(60):
+        n = int(rng.integers(1, 9))
+        vals = [alpha[i] for i in rng.integers(0, len(alpha), n)]
+        keys = as_keys(vals, key_type)
+        num = numeric(keys, key_type)
+        payload = rng.permutation(1000)[:n].astype(np.uint32)
+        # Put the segment behind a non-zero first offset.
+        pad = int(rng.integers(0, 3))
+        keys_full = np.concatenate([as_keys([alpha[0]] * pad, key_type), keys])
+        pay_full = np.concatenate([np.full(pad, 7777, np.uint32), payload])
+        off = np.array([pad, pad + n], dtype=np.int64)
+        for k in range(0, n + 2):
+            for largest in (True, False):
+                for pl in (False, True):
+                    canary_k = as_keys([alpha[0]] * max(k, 1), key_type)[None, :k].copy()
+                    ok, ov = oracle.batched_topk(keys_full, off, k, key_type=key_type,
+                                                 values=pay_full, largest=largest,
+                                                 prefer_larger=pl,
+                                                 out_keys=canary_k if k else None,
+                                                 out_values=np.full((1, k), 0xDEAD, np.uint32))
+                    if k == 0:
+                        continue
+                    want = brute_force(list(num), k, largest, pl)
+                    kk = len(want)
+                    # Map payload back to indices (payload values are unique).
+                    got_idx = sorted(int(np.nonzero(payload == p)[0][0]) for p in ov[0, :kk])
+                    assert tuple(got_idx) == want, (vals, k, largest, pl)
+                    # Keys written with their own bit patterns.
+                    for j in range(kk):
+                        i = int(np.nonzero(payload == ov[0, j])[0][0])
+                        assert ok[0, j].tobytes() == keys[i].tobytes()
+                    # Stable order: better first, equal keys by index ascending.
+                    outv = [num[int(np.nonzero(payload == p)[0][0])] for p in ov[0, :kk]]
+                    outi = [int(np.nonzero(payload == p)[0][0]) for p in ov[0, :kk]]
+                    for j in range(kk - 1):
+                        a, b = outv[j], outv[j + 1]
+                        assert (a > b or a == b) if largest else (a < b or a == b)
+                        if a == b:
+                            assert outi[j] < outi[j + 1]
+                    # Untouched tail.
+                    assert np.all(ov[0, kk:] == 0xDEAD)
+
+
+# --------------------------------------------------------------------------
+# 3. numpy's sort routines on larger random segments.
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("key_type", ALL_TYPES)
+@pytest.mark.parametrize("largest", [True, False])
+@pytest.mark.parametrize("prefer_larger", [False, True])
+def test_against_numpy_lexsort(key_type, largest, prefer_larger):
+    rng = np.random.default_rng(11)
+    sizes = rng.integers(-3, 700, 40)
+    sizes[3] = 0
+    begin = np.zeros(41, dtype=np.int64)
+    ends = np.zeros(41, dtype=np.int64)
+    # Offsets with a few negative-size (empty) segments.
+    off = [5]
+    for s in sizes:
+        off.append(off[-1] + int(s))
+    off = np.array(off, dtype=np.int64)
+    total = int(off.max()) + 10
+    if key_type in ("f32", "bf16", "f16"):
+        levels = rng.integers(-20, 20, total) / 4.0
+        levels[rng.random(total) < 0.05] = -0.0
+        levels[rng.random(total) < 0.02] = np.inf
+        levels[rng.random(total) < 0.02] = -np.inf
+    elif key_type == "u32":
+        levels = rng.integers(0, 2 ** 32, total).astype(np.float64)
+        levels[rng.random(total) < 0.3] = 12345
+    else:
+        levels = rng.integers(-(2 ** 31), 2 ** 31, total).astype(np.float64)
+        levels[rng.random(total) < 0.3] = -5
+    keys = as_keys(levels, key_type)
+    num = numeric(keys, key_type)
+    payload = rng.integers(0, 2 ** 32, total, dtype=np.uint64).astype(np.uint32)
+    k = 37
+    ok, ov = oracle.batched_topk(keys, off, k, key_type=key_type, values=payload,
+                                 largest=largest, prefer_larger=prefer_larger,
+                                 out_values=np.full((40, k), 0xABCD, np.uint32))
+    for i in range(40):
+        b, e = int(off[i]), int(off[i + 1])
+        n = max(0, e - b)
+        kk = min(k, n)
+        if kk == 0:
+            assert np.all(ov[i] == 0xABCD)
+            continue
+        seg = num[b:b + n]
+        idx = np.arange(n)
+        primary = -seg if largest else seg
+        secondary = -idx if prefer_larger else idx
+        order = np.lexsort((secondary, primary))
+        chosen = order[:kk]
+        # stable output order of the chosen set
+        out_order = chosen[np.lexsort((chosen, primary[chosen]))]
+        assert np.array_equal(ov[i, :kk], payload[b + out_order])
+        assert ok[i, :kk].tobytes() == keys[b + out_order].tobytes()
+        assert np.all(ov[i, kk:] == 0xABCD)
+
+
+# --------------------------------------------------------------------------
+# 4. Invariants and special cases fixed by the definition.
+# --------------------------------------------------------------------------
+def test_select_all_when_k_at_least_n():
+    keys = np.array([3, 1, 2, 1], dtype=np.float32)
+    off = np.array([0, 4], dtype=np.int64)
+    for k in (4, 9):
+        ok, ov = oracle.batched_topk(keys, off, k, values=np.arange(4, dtype=np.uint32))
+        assert list(ov[0, :4]) == [0, 2, 1, 3]
+        ok, ov = oracle.batched_topk(keys, off, k, values=np.arange(4, dtype=np.uint32),
+                                     largest=False)
+        assert list(ov[0, :4]) == [1, 3, 2, 0]
+
+
+def test_k_zero_and_empty_segments_write_nothing():
+    keys = np.arange(10, dtype=np.float32)
+    off = np.array([0, 0, 4, 2, 10], dtype=np.int64)  # empty, 4, negative, 8
+    canary = np.full((4, 3), 99, np.uint32)
+    ok, ov = oracle.batched_topk(keys, off, 3, values=np.arange(10, dtype=np.uint32),
+                                 out_values=canary.copy())
+    assert list(ov[0]) == [99, 99, 99]
+    assert list(ov[1]) == [3, 2, 1]
+    assert list(ov[2]) == [99, 99, 99]
+    assert list(ov[3]) == [9, 8, 7]
+    ok, ov = oracle.batched_topk(keys, off, 0, values=np.arange(10, dtype=np.uint32))
+    assert ov.shape == (4, 0)
+
+
+@pytest.mark.parametrize("prefer_larger", [False, True])
+def test_all_equal_keys_take_index_extremes(prefer_larger):
+    n, k = 50, 7
+    keys = np.full(n, 0.5, np.float32)
+    off = np.array([0, n], dtype=np.int64)
+    for largest in (True, False):
+        _, ov = oracle.batched_topk(keys, off, k, values=np.arange(n, dtype=np.uint32),
+                                    largest=largest, prefer_larger=prefer_larger)
+        want = list(range(n - k, n)) if prefer_larger else list(range(k))
+        assert list(ov[0]) == want  # stable order: index ascending
+
+
+def test_negative_zero_kept_bitwise():
+    keys = np.array([-0.0, 0.0, -1.0, -0.0], dtype=np.float32)
+    off = np.array([0, 4], dtype=np.int64)
+    ok, ov = oracle.batched_topk(keys, off, 1, values=np.arange(4, dtype=np.uint32))
+    assert ov[0, 0] == 0 and f32_bits(ok[0, 0]) == 0x80000000
+    ok, ov = oracle.batched_topk(keys, off, 1, values=np.arange(4, dtype=np.uint32),
+                                 prefer_larger=True)
+    assert ov[0, 0] == 3 and f32_bits(ok[0, 0]) == 0x80000000
+    ok, ov = oracle.batched_topk(keys, off, 3, values=np.arange(4, dtype=np.uint32))
+    assert list(ov[0]) == [0, 1, 3]
+    assert [int(b) for b in f32_bits(ok[0])] == [0x80000000, 0, 0x80000000]
+    ok, ov = oracle.batched_topk(keys, off, 2, values=np.arange(4, dtype=np.uint32),
+                                 largest=False)
+    assert list(ov[0]) == [2, 0]
+
+
+def test_infinities_are_the_ends():
+    keys = np.array([np.inf, 1e38, -np.inf, -1e38, np.inf], dtype=np.float32)
+    off = np.array([0, 5], dtype=np.int64)
+    _, ov = oracle.batched_topk(keys, off, 3, values=np.arange(5, dtype=np.uint32))
+    assert list(ov[0]) == [0, 4, 1]
+    _, ov = oracle.batched_topk(keys, off, 2, values=np.arange(5, dtype=np.uint32),
+                                largest=False)
+    assert list(ov[0]) == [2, 3]
+
+
+@pytest.mark.parametrize("key_type", ["bf16", "f16"])
+def test_every_16bit_pattern_in_order(key_type):
+    """All 2^16 patterns minus NaNs, select-all + stable order, against the
+    ordering of numpy / torch decoded values."""
+    pats = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    num = numeric(pats, key_type)
+    pats = pats[~np.isnan(num)]
+    num = num[~np.isnan(num)]
+    n = len(pats)
+    off = np.array([0, n], dtype=np.int64)
+    for largest in (True, False):
+        ok, ov = oracle.batched_topk(pats, off, n, key_type=key_type,
+                                     values=np.arange(n, dtype=np.uint32), largest=largest)
+        primary = -num if largest else num
+        want = np.lexsort((np.arange(n), primary))
+        assert np.array_equal(ov[0], want.astype(np.uint32))
+
+
+def test_front_tie_decomposition_random():
+    rng = np.random.default_rng(5)
+    n, k = 3000, 100
+    keys = (rng.integers(0, 40, n) / 8.0).astype(np.float32)
+    off = np.array([0, n], dtype=np.int64)
+    for largest in (True, False):
+        ok, ov = oracle.batched_topk(keys, off, k, values=np.arange(n, dtype=np.uint32),
+                                     largest=largest)
+        s = ok[0, k - 1]  # k-th best value (stable order: last one)
+        front = np.sum(keys > s) if largest else np.sum(keys < s)
+        ties = np.sum(keys == s)
+        assert front < k <= front + ties
+        sel = set(int(v) for v in ov[0])
+        rest = [i for i in range(n) if i not in sel]
+        worst_in = min(keys[list(sel)]) if largest else max(keys[list(sel)])
+        best_out = max(keys[rest]) if largest else min(keys[rest])
+        assert (worst_in >= best_out) if largest else (worst_in <= best_out)
+        # ties taken toward smaller indices
+        tie_sel = sorted(i for i in sel if keys[i] == s)
+        tie_all = [i for i in range(n) if keys[i] == s]
+        assert tie_sel == tie_all[:len(tie_sel)]
+
+
+def test_rejects_bad_arguments():
+    lib = oracle._load()
+    keys = np.zeros(4, np.float32)
+    off = np.array([0, 4], dtype=np.int64)
+    out = np.zeros(4, np.float32)
+    args = lambda k, s, t: (keys.ctypes.data, t, None, off.ctypes.data, s, k, 1, 0,
+                            out.ctypes.data, None, 1)
+    assert lib.oracle_batched_topk(*args(-1, 1, 0)) == 1
+    assert lib.oracle_batched_topk(*args(1, -1, 0)) == 1
+    assert lib.oracle_batched_topk(*args(1, 1, 9)) == 1
+    assert lib.oracle_batched_topk(*args(1, 1, 0)) == 0
