@@ -1,0 +1,222 @@
+"""Segmented top-k benchmark on one MI355X.
+
+One step = one batched_topk call over one batch of synthetic input (all of the
+hot path: pass-0 streaming, radix passes, tie selection, sort, output).  The
+headline workload is 4096 segments x 4096 float32 keys ~ N(0,1) with uint32
+index values, k = 64, MaxPairs, gpu_to_gpu + prefer_smaller_index,
+stable_sorted.  Its inputs (128 MiB) would fit the 256 MiB Infinity Cache, so
+steps rotate over enough copies of the input that each step reads its keys
+from HBM.  The other workloads are measured the same way and reported under
+"workloads".
+
+Prints one JSON line.  Usage:  python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
+HEADLINE = "normal_f32_4096x4096_k64"
+KEY_BYTES = {"f32": 4, "bf16": 2, "f16": 2, "u32": 4, "i32": 4}
+CACHE_BYTES = 256 << 20  # Infinity Cache
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor()
+
+
+def workload_sizes(off_np, k):
+    import numpy as np
+    n = np.maximum(off_np[1:] - off_np[:-1], 0)
+    return int(n.sum()), int(np.minimum(n, k).sum())
+
+
+def measure(name, steps, warmup, stream_rotate=True):
+    """Times `steps` back-to-back calls (after `warmup`) with HIP events on the
+    stream the library launches on.  Returns a dict of figures."""
+    import numpy as np
+    import torch
+
+    import segmented_top_selection_amd as st
+    import workloads
+
+    w = workloads.WORKLOADS[name]
+    keys, vals, off = w["gen"](device="cuda", **w["args"])
+    if not w["pairs"]:
+        vals = None
+    off_np = off.cpu().numpy()
+    N, KK = workload_sizes(off_np, w["k"])
+    sk = KEY_BYTES[w["key_type"]]
+    sv = 4 if vals is not None else 0
+    in_bytes = keys.numel() * sk + (vals.numel() * 4 if vals is not None else 0)
+    # Copies so that every step reads inputs that are not cache-resident.
+    copies = 1
+    if stream_rotate and in_bytes < 4 * CACHE_BYTES:
+        copies = max(2, int(np.ceil(4 * CACHE_BYTES / in_bytes)))
+    ins = [(keys, vals)] + [(keys.clone(), vals.clone() if vals is not None else None)
+                            for _ in range(copies - 1)]
+    s = off.numel() - 1
+    out_k = torch.empty((s, w["k"]), dtype=keys.dtype, device="cuda")
+    out_v = torch.empty((s, w["k"]), dtype=torch.int32, device="cuda") if vals is not None else None
+
+    def step(i):
+        kk, vv = ins[i % copies]
+        st.batched_topk(kk, off, w["k"], values=vv, largest=w["largest"],
+                        determinism=w["determinism"], tie_break=w["tie_break"],
+                        ordering=w["ordering"], key_type=w["key_type"], out_keys=out_k,
+                        out_values=out_v)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(steps):
+        step(warmup + i)
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]  # ms
+    total_ms = ev[0].elapsed_time(ev[steps])
+    ms = total_ms / steps
+    t = ms / 1e3
+    bytes_roof = N * (sk + sv) + KK * (sk + sv)          # metric's single-read roofline
+    bytes_alg = N * sk + KK * sv + KK * (sk + sv)         # what the method must move
+    res = dict(
+        workload=name, segments=s, keys=N, k=w["k"], key_type=w["key_type"],
+        mode=f"{'Max' if w['largest'] else 'Min'}{'Pairs' if vals is not None else 'Keys'} "
+             f"{w['determinism']}/{w['tie_break']}/{w['ordering']}",
+        ms_per_step=ms, ms_min=min(per), ms_median=float(np.median(per)), wall_s=wall,
+        keys_per_s=N / t, input_copies=copies,
+        bytes_roof=bytes_roof, hbm_roof_frac=(bytes_roof / (HBM_PEAK_GBS * 1e9)) / t,
+        bytes_alg=bytes_alg, alg_gbs=bytes_alg / t / 1e9,
+    )
+    del ins, keys, vals, out_k, out_v
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(name, budget_s=15.0):
+    """The oracle, as it stands, on a bounded sample of the workload's segments
+    (whole segments, taken from the start), on all host cores."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import workloads
+
+    w = workloads.WORKLOADS[name]
+    args = dict(w["args"])
+    keys, vals, off = w["gen"](device="cuda", **args)
+    s = off.numel() - 1
+    threads = oracle.default_threads()
+    # Grow the sample until it takes about `budget_s` seconds.
+    rows = min(s, 64)
+    elapsed = 0.0
+    while True:
+        b, e = int(off[0]), int(off[rows])
+        kb = keys[b:e].cpu()
+        kb = kb.view(torch.int16).numpy().view(np.uint16) if kb.element_size() == 2 else \
+            kb.view(torch.int32).numpy().view(np.uint32)
+        kb = kb.view(np.float32) if w["key_type"] == "f32" else kb
+        vb = vals[b:e].cpu().numpy().view(np.uint32) if w["pairs"] else None
+        o = off[:rows + 1].cpu().numpy() - b
+        t0 = time.perf_counter()
+        oracle.batched_topk(kb, o, w["k"], key_type=w["key_type"], values=vb,
+                            largest=w["largest"],
+                            prefer_larger=w["tie_break"] == "prefer_larger_index",
+                            threads=threads)
+        elapsed = time.perf_counter() - t0
+        if rows >= s or elapsed > budget_s / 4:
+            break
+        rows = min(s, rows * 4)
+    n = int(o[-1])
+    return dict(value=n / elapsed, unit="keys/s", cores=threads, kind="oracle",
+                sample=f"{rows} of {s} segments ({n} keys) of {name}, {elapsed:.2f} s",
+                cpu=cpu_model())
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--only-headline", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {a.gpus}); segments are "
+              f"independent, so N GPUs would each run this call on their own shard.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+
+    head = measure(a.workload, a.steps, a.warmup)
+    log("headline", json.dumps(head))
+    others = {}
+    if not a.only_headline:
+        for name in workloads.WORKLOADS:
+            if name == a.workload:
+                continue
+            others[name] = measure(name, max(5, a.steps // 2), 2)
+            log(name, json.dumps(others[name]))
+    cpu = None if a.no_cpu_baseline else cpu_baseline(a.workload)
+
+    kernel_ms = head["ms_per_step"]
+    line = {
+        "metric": "segmented top-k keys/sec + % of single-read HBM roofline (fp32, k=64)",
+        "value": head["keys_per_s"],
+        "unit": "keys/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": head["key_type"],
+        "data": "synthetic",
+        "config": {"workload": a.workload, "segments": head["segments"],
+                   "segment_len": head["keys"] // max(1, head["segments"]), "k": head["k"],
+                   "mode": head["mode"]},
+        "hbm_single_read_roofline_frac": head["hbm_roof_frac"],
+        "roofline": {"bound": "hbm", "achieved": head["bytes_alg"] / (kernel_ms / 1e3) / 1e9,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": head["bytes_alg"] / (kernel_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+                     "traffic": None},
+        "cpu_baseline": cpu,
+        "workloads": {n: {kk: (round(v, 6) if isinstance(v, float) else v)
+                          for kk, v in r.items()} for n, r in others.items()},
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

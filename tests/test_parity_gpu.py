@@ -1,0 +1,304 @@
+"""GPU-vs-oracle parity through the C-ABI (needs an MI355X).
+
+Every case runs the HIP library on seeded synthetic input, runs the CPU oracle
+on host copies of the same input and compares rows as described in
+tests/parity.py: bitwise in the deterministic modes, key multiset plus validity
+in not_guaranteed, and untouched slots past min(k, n_i) everywhere.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from parity import check, run_gpu, KEY_CANARY
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+MODES = [("not_guaranteed", "unspecified"), ("run_to_run", "unspecified"),
+         ("gpu_to_gpu", "unspecified"), ("gpu_to_gpu", "prefer_smaller_index"),
+         ("gpu_to_gpu", "prefer_larger_index")]
+ORDERINGS = ["unsorted", "sorted", "stable_sorted"]
+KEY_TYPES = ["f32", "bf16", "f16", "u32", "i32"]
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev_keys(vals, key_type):
+    """Numeric values -> device key tensor of the type (exact for test values)."""
+    t = torch.tensor(np.asarray(vals, dtype=np.float64))
+    if key_type == "f32":
+        return t.float().to(DEV)
+    if key_type == "bf16":
+        return t.to(torch.bfloat16).to(DEV)
+    if key_type == "f16":
+        return t.to(torch.float16).to(DEV)
+    if key_type == "u32":
+        return torch.tensor(np.asarray(vals, dtype=np.uint64).astype(np.uint32).view(np.int32)).to(DEV)
+    return torch.tensor(np.asarray(vals, dtype=np.int64).astype(np.int32)).to(DEV)
+
+
+def index_values(offsets):
+    off = offsets.cpu().numpy()
+    total = int(off.max()) if off.size else 0
+    v = np.zeros(total, dtype=np.int32)
+    for i in range(len(off) - 1):
+        b, e = int(off[i]), int(off[i + 1])
+        if e > b:
+            v[b:e] = np.arange(e - b, dtype=np.int32)
+    return torch.from_numpy(v).to(DEV)
+
+
+def random_keys(total, key_type, gen, levels=None):
+    if key_type in ("f32", "bf16", "f16"):
+        if levels:
+            x = torch.randint(-levels, levels, (total,), generator=gen, device=DEV).float() / 4
+        else:
+            x = torch.randn(total, generator=gen, device=DEV) * 3
+        x = x.to({"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[key_type])
+        return x
+    if levels:
+        return torch.randint(-levels, levels, (total,), generator=gen, device=DEV,
+                             dtype=torch.int64).to(torch.int32)
+    return torch.randint(-(2 ** 31), 2 ** 31, (total,), generator=gen, device=DEV,
+                         dtype=torch.int64).to(torch.int32)
+
+
+# ---------------------------------------------------------------------------
+# The requirements page's worked example, every mode and ordering.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("key_type", KEY_TYPES)
+def test_worked_example(key_type):
+    keys = dev_keys([10, 8, 8, 8, 6, 5], key_type)
+    off = torch.tensor([0, 6], dtype=torch.int64, device=DEV)
+    vals = index_values(off)
+    for det, tb in MODES:
+        for ordering in ORDERINGS:
+            gk, gv = check(keys, vals, off, 3, key_type, True, det, tb, ordering)
+            got = sorted(int(v) for v in gv[0])
+            if tb == "prefer_larger_index":
+                assert got == [0, 2, 3]
+            elif det != "not_guaranteed":
+                assert got == [0, 1, 2]
+            else:
+                assert 0 in got and len(set(got)) == 3
+            if ordering == "stable_sorted" and det == "gpu_to_gpu" and tb != "unspecified":
+                assert list(gv[0]) == ([0, 2, 3] if tb == "prefer_larger_index" else [0, 1, 2])
+
+
+# ---------------------------------------------------------------------------
+# The benchmark workloads (full size where the oracle keeps up, else sampled
+# rows), each in its own request mode.
+# ---------------------------------------------------------------------------
+def _workload(name, **shape):
+    w = workloads.WORKLOADS[name]
+    args = dict(w["args"])
+    args.update(shape)
+    keys, vals, off = w["gen"](device=DEV, **args)
+    if not w["pairs"]:
+        vals = None
+    return w, keys, vals, off
+
+
+def _run_workload(name, rows=None, **shape):
+    w, keys, vals, off = _workload(name, **shape)
+    say(f"[{name}] {shape or 'full size'} segments={off.numel() - 1} keys={keys.numel()}")
+    check(keys, vals, off, w["k"], w["key_type"], w["largest"], w["determinism"],
+          w["tie_break"], w["ordering"], rows=rows)
+
+
+def test_uniform_f32_16x1000_k10():
+    _run_workload("uniform_f32_16x1000_k10")
+
+
+def test_normal_f32_k64_reduced():
+    _run_workload("normal_f32_4096x4096_k64", num_segments=300)
+
+
+def test_normal_f32_4096x4096_k64_full():
+    _run_workload("normal_f32_4096x4096_k64")
+
+
+def test_quantized_reduced_multi_workgroup():
+    # 96 segments -> several workgroups per long segment.
+    _run_workload("quantized_f32_1024xU65536_k256", num_segments=96)
+
+
+def test_quantized_full_sampled():
+    w, keys, vals, off = _workload("quantized_f32_1024xU65536_k256")
+    sizes = (off[1:] - off[:-1]).cpu().numpy()
+    rng = np.random.default_rng(0)
+    rows = sorted(set(rng.choice(len(sizes), 48, replace=False).tolist()
+                      + np.argsort(sizes)[-4:].tolist() + np.argsort(sizes)[:4].tolist()))
+    say(f"[quantized full] rows {rows[:8]}...")
+    check(keys, vals, off, w["k"], w["key_type"], w["largest"], w["determinism"],
+          w["tie_break"], w["ordering"], rows=rows)
+
+
+@pytest.mark.parametrize("name", ["uniform_u32_32x4Mi_k2048", "normal10_f32_32x4Mi_k2048"])
+def test_large_segments_reduced(name):
+    _run_workload(name, num_segments=4, seg_len=1 << 20)
+
+
+@pytest.mark.parametrize("name", ["uniform_u32_32x4Mi_k2048", "normal10_f32_32x4Mi_k2048"])
+def test_large_segments_full_sampled(name):
+    _run_workload(name, rows=[0, 13, 31])
+
+
+def test_logits_bf16_reduced():
+    _run_workload("logits_bf16_16384x128Ki_k50", num_segments=256)
+
+
+def test_logits_bf16_full_sampled():
+    rows = [0, 1, 777, 8191, 12345, 16383]
+    _run_workload("logits_bf16_16384x128Ki_k50", rows=rows)
+    torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------------------
+# Sizes around k, empty and negative segments, unaligned starts, every key
+# type, direction, mode and ordering.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("key_type", KEY_TYPES)
+def test_edge_sizes_all_modes(key_type):
+    g = torch.Generator(device=DEV)
+    g.manual_seed(42)
+    k = 33
+    sizes = [0, 1, 2, k - 1, k, k + 1, 3, 100, 257, 1000, 4095, 4096, 4097, 9000, 40000,
+             -5, 0, 70000, 33, 5]
+    off = [3]  # unaligned start
+    for s_ in sizes:
+        off.append(off[-1] + s_)
+    off_t = torch.tensor(off, dtype=torch.int64, device=DEV)
+    total = max(off) + 7
+    for levels in (None, 6):
+        keys = random_keys(total, key_type, g, levels)
+        vals = index_values(off_t)
+        vals = torch.cat([vals, torch.zeros(total - vals.numel(), dtype=torch.int32, device=DEV)])
+        for largest in (True, False):
+            for det, tb in MODES:
+                for ordering in ORDERINGS:
+                    check(keys, vals, off_t, k, key_type, largest, det, tb, ordering)
+
+
+@pytest.mark.parametrize("key_type", ["f32", "bf16"])
+def test_keys_only(key_type):
+    g = torch.Generator(device=DEV)
+    g.manual_seed(3)
+    off = torch.tensor([0, 5000, 5001, 20000, 20100], dtype=torch.int64, device=DEV)
+    keys = random_keys(20100, key_type, g, 8)
+    for ordering in ORDERINGS:
+        check(keys, None, off, 40, key_type, True, "gpu_to_gpu", "prefer_larger_index", ordering)
+        check(keys, None, off, 40, key_type, False, "gpu_to_gpu", "prefer_smaller_index", ordering)
+
+
+# ---------------------------------------------------------------------------
+# Ties: all-equal segments (more candidates than the on-chip stash holds),
+# signed zeros, infinities, many copies of the boundary key.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("key_type", ["f32", "bf16"])
+def test_heavy_ties(key_type):
+    segs = []
+    n = 20000
+    segs.append(np.full(n, 1.5))                       # all equal
+    segs.append(np.where(np.arange(n) % 2, 0.0, -0.0))  # +-0 only
+    z = np.zeros(n)
+    z[::3] = -0.0
+    z[::7] = np.inf
+    z[::11] = -np.inf
+    segs.append(z)                                      # zeros and infinities
+    rng = np.random.default_rng(9)
+    b = rng.integers(-3, 4, n) * 0.5                    # many copies of each level
+    segs.append(b)
+    vals_np = np.concatenate(segs)
+    off = torch.tensor(np.cumsum([0] + [len(s) for s in segs]), dtype=torch.int64, device=DEV)
+    t = torch.tensor(vals_np)
+    # keep the sign of -0.0 through the conversion
+    keys = (t.float() if key_type == "f32" else t.to(torch.bfloat16)).to(DEV)
+    vals = index_values(off)
+    for k in (1, 100, 5000):
+        for largest in (True, False):
+            for det, tb in MODES:
+                for ordering in (["unsorted", "stable_sorted"] if k <= 4096 else ["unsorted"]):
+                    check(keys, vals, off, k, key_type, largest, det, tb, ordering)
+
+
+def test_negative_zero_comes_back_bitwise():
+    keys = torch.tensor([-0.0, 0.0, -1.0, -0.0, -2.0], device=DEV)
+    off = torch.tensor([0, 5], dtype=torch.int64, device=DEV)
+    vals = index_values(off)
+    gk, gv = check(keys, vals, off, 1, "f32", True, "gpu_to_gpu", "prefer_smaller_index",
+                   "stable_sorted")
+    assert gk[0, 0] == 0x80000000 and gv[0, 0] == 0
+    gk, gv = check(keys, vals, off, 1, "f32", True, "gpu_to_gpu", "prefer_larger_index",
+                   "stable_sorted")
+    assert gk[0, 0] == 0x80000000 and gv[0, 0] == 3
+    gk, gv = check(keys, vals, off, 2, "f32", True, "gpu_to_gpu", "prefer_larger_index",
+                   "stable_sorted")
+    assert list(gv[0]) == [1, 3]
+
+
+# ---------------------------------------------------------------------------
+# Ordered inputs: the running bound keeps falling, so the stash is compacted.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("descending", [False, True])
+def test_monotone_inputs(descending):
+    n = 300000
+    x = torch.arange(n, device=DEV, dtype=torch.float32)
+    if descending:
+        x = x.flip(0)
+    keys = torch.cat([x, x[:50000] * 0.5])
+    off = torch.tensor([0, n, n + 50000], dtype=torch.int64, device=DEV)
+    vals = index_values(off)
+    for k in (64, 1000):
+        for largest in (True, False):
+            check(keys, vals, off, k, "f32", largest, "gpu_to_gpu", "prefer_smaller_index",
+                  "stable_sorted")
+
+
+# ---------------------------------------------------------------------------
+# Large k: direct (unstaged) output, select-all, the sorted-k limit.
+# ---------------------------------------------------------------------------
+def test_large_k_unsorted_and_sorted_limit():
+    g = torch.Generator(device=DEV)
+    g.manual_seed(5)
+    off = torch.tensor([0, 2000, 12000, 60000], dtype=torch.int64, device=DEV)
+    keys = random_keys(60000, "f32", g, 50)
+    vals = index_values(off)
+    check(keys, vals, off, 3000, "f32", True, "gpu_to_gpu", "prefer_smaller_index", "unsorted")
+    check(keys, vals, off, 3000, "f32", False, "not_guaranteed", "unspecified", "unsorted")
+    check(keys, vals, off, 4096, "f32", True, "gpu_to_gpu", "prefer_larger_index", "stable_sorted")
+    import segmented_top_selection_amd as st
+    with pytest.raises(st.SegTopKError) as e:
+        st.batched_topk(keys, off, 4097, values=vals, ordering="sorted")
+    assert e.value.status == 2
+
+
+def test_invalid_pairings_rejected_without_work():
+    import segmented_top_selection_amd as st
+    keys = torch.zeros(10, device=DEV)
+    off = torch.tensor([0, 10], dtype=torch.int64, device=DEV)
+    for det in ("not_guaranteed", "run_to_run"):
+        for tb in ("prefer_smaller_index", "prefer_larger_index"):
+            with pytest.raises(st.SegTopKError) as e:
+                st.batched_topk(keys, off, 3, determinism=det, tie_break=tb)
+            assert e.value.status == 1
+
+
+# ---------------------------------------------------------------------------
+# Run-to-run: deterministic modes return identical sets (stable_sorted:
+# identical buffers) on repeated calls.
+# ---------------------------------------------------------------------------
+def test_repeat_runs_identical():
+    w, keys, vals, off = _workload("quantized_f32_1024xU65536_k256", num_segments=64)
+    first = run_gpu(keys, vals, off, 256, "f32", False, "gpu_to_gpu", "prefer_smaller_index",
+                    "stable_sorted")
+    for _ in range(3):
+        again = run_gpu(keys, vals, off, 256, "f32", False, "gpu_to_gpu",
+                        "prefer_smaller_index", "stable_sorted")
+        assert np.array_equal(first[0], again[0]) and np.array_equal(first[1], again[1])
