@@ -9,40 +9,45 @@
 //   [PR "Implement Segmented TopK using Thread-Block-Clusters", §1.2 Radix
 //    (digit) top-k, §1.4 Early stop, §1.5 Final filter and output placement]
 //
-// How it is laid out on gfx950 (differences from the pages' cluster design):
+// How it maps onto gfx950 (where it departs from the pages' cluster design):
 //
-//  * One read of the keys.  Pass 0 streams the keys from HBM once.  A key is
-//    counted in the pass-0 histogram and copied, with its index, into an LDS
-//    "stash" only if its bucket can still hold the k-th key: the bound is the
-//    k-th best bucket of the keys seen so far, which can only improve as more
-//    keys arrive, so every key that the final result needs is counted and
-//    stashed, and the counts of all buckets at or before the final k-th bucket
-//    are exact.  Later passes, the tie selection and the output read only the
-//    stash.  If a segment's candidates do not fit the stash (heavy ties, huge k)
-//    the later passes re-stream the keys from memory instead.
+//  * One workgroup of four wave64 serves a segment (or a slice of one).  The
+//    four waves stream disjoint quarters of the keys from HBM once each, with
+//    no workgroup barrier inside the streaming loop.
+//  * Pass 0 counts a key in the workgroup's LDS histogram, and copies it with
+//    its index into its wave's LDS stash, only if its bucket can still hold the
+//    k-th key.  The bound each wave uses is the k-th best bucket of what the
+//    shared histogram held when the wave last looked: counts only grow, so a
+//    bound read from a histogram other waves are still filling is merely loose,
+//    never wrong.  Hence every key the answer needs is counted and stashed, and
+//    the counts of every bucket up to the final k-th bucket are exact.  Later
+//    passes, the tie selection and the output read only the stashes; a wave
+//    whose stash overflows (heavy ties, large k) has its quarter re-read.
+//  * After one barrier, wave 0 finishes the segment alone, synchronising its
+//    lanes with wave fences only.
 //  * Buckets are reversed for MAX (bucket = B-1-digit) instead of inverting the
 //    key bits, after -0.0 has been folded onto +0.0 in the order-preserving bit
 //    transform.   [PR "Fix BlockTopK +/-0.0 handling", Fix]
-//  * Deterministic tie-break: the splitter-equal keys are narrowed further by
-//    radix passes over their source index (ascending digits for
-//    prefer_smaller_index, reversed for prefer_larger_index), so exactly the
-//    required number of ties is picked without an index-ordered scan.
-//    not_guaranteed takes ties in arrival order behind an `out < k` guard.
+//  * Deterministic tie-break: the splitter-equal keys are narrowed by further
+//    radix passes over their source index (digits ascending for
+//    prefer_smaller_index, reversed for prefer_larger_index), which picks
+//    exactly the required ties without an index-ordered scan; not_guaranteed
+//    takes ties in arrival order behind an `out < k` guard.
 //    [PR "Implement Segmented TopK ...", §1.6 Determinism / tie-breaking]
 //  * A batch of few, long segments spreads each segment over several
-//    workgroups.  Each streams its slice with the scheme above, adds its
-//    histogram to a per-segment global histogram with atomics, writes its
-//    stash to a global slot and takes a ticket; the last arriver scans the merged
-//    histogram and finishes the segment from the slots.  (CDNA4 has no thread
-//    block clusters; this replaces the cluster's DSMEM merge into a leader.)
-//  * sorted / stable_sorted output is a bitonic sort of the k results in LDS on
+//    workgroups (CDNA4 has no thread-block clusters).  Each finishes pass 0 on
+//    its slice, adds its histogram to a per-segment global histogram with
+//    atomics, and writes its candidates to a global slot sorted by bucket
+//    together with their cumulative bucket counts; the last workgroup to take
+//    the segment's ticket scans the merged histogram and reads from every slot
+//    only the prefix that can still win.
+//  * sorted / stable_sorted output is a bitonic sort in LDS of the k results on
 //    (ordered key best-first, source index ascending).
 //    [docs "Top-K: Determinism, Tie-Breaking, and Output Ordering", Output
 //     ordering]
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
-#include <stdio.h>
 #include <stdlib.h>
 
 #include <mutex>
@@ -51,46 +56,143 @@
 
 namespace {
 
-constexpr int kThreads = 256;           // four wave64 per workgroup
+constexpr int kWave = 64;               // wave64
+constexpr int kWaves = 4;               // waves per workgroup
+constexpr int kThreads = kWave * kWaves;
 constexpr int kDigit = 11;              // digit width of every radix pass
 constexpr int kBuckets = 1 << kDigit;   // 2048 histogram buckets
-constexpr uint32_t kNone = 0xFFFFFFFFu; // "no element" / sort sentinel
+constexpr uint32_t kNone = 0xFFFFFFFFu; // "no element" / sort padding
 
 // ---------------------------------------------------------------------------
-// Order-preserving bit transform.  ord(a) < ord(b) exactly when a < b, and
+// Order-preserving bit transform: ord(a) < ord(b) exactly when a < b, and
 // ord(-0.0) == ord(+0.0).  The original bits are kept for output.
 // ---------------------------------------------------------------------------
 template <int KT> struct Key;
 
+// Besides ord(), each key type defines how a loaded key is held in a register
+// ("word": bfloat16 sits in the upper half so that it reads as the float32 of
+// the same value) and a native comparison used to pre-filter keys against a
+// bucket bound (see fast_bound below).
 template <> struct Key<SEGTOPK_KEY_F32> {
     static constexpr int kBits = 32, kBytes = 4;
+    static constexpr bool kFloat = true;
+    static constexpr uint32_t kOrdNegInf = 0x007FFFFFu, kOrdPosInf = 0xFF800000u;
     __device__ __forceinline__ static uint32_t ord(uint32_t r) {
         r = (r == 0x80000000u) ? 0u : r;  // -0.0 joins +0.0
         return r ^ ((uint32_t)((int32_t)r >> 31) | 0x80000000u);
     }
+    __device__ __forceinline__ static uint32_t inv_ord(uint32_t o) {
+        return (o & 0x80000000u) ? (o ^ 0x80000000u) : ~o;
+    }
+    __device__ __forceinline__ static uint32_t word(uint32_t r) { return r; }
+    __device__ __forceinline__ static uint32_t raw(uint32_t w) { return w; }
+    __device__ __forceinline__ static float value(uint32_t w) { return __uint_as_float(w); }
+    __device__ __forceinline__ static uint32_t value_bits(uint32_t r) { return r; }
 };
 template <> struct Key<SEGTOPK_KEY_BF16> {
     static constexpr int kBits = 16, kBytes = 2;
+    static constexpr bool kFloat = true;
+    static constexpr uint32_t kOrdNegInf = 0x007Fu, kOrdPosInf = 0xFF80u;
     __device__ __forceinline__ static uint32_t ord(uint32_t r) {
         r = (r == 0x8000u) ? 0u : r;
         return r ^ ((r & 0x8000u) ? 0xFFFFu : 0x8000u);
     }
+    __device__ __forceinline__ static uint32_t inv_ord(uint32_t o) {
+        return (o & 0x8000u) ? (o ^ 0x8000u) : (~o & 0xFFFFu);
+    }
+    __device__ __forceinline__ static uint32_t word(uint32_t r) { return r << 16; }
+    __device__ __forceinline__ static uint32_t raw(uint32_t w) { return w >> 16; }
+    __device__ __forceinline__ static float value(uint32_t w) { return __uint_as_float(w); }
+    __device__ __forceinline__ static uint32_t value_bits(uint32_t r) { return r << 16; }
 };
 template <> struct Key<SEGTOPK_KEY_F16> {
     static constexpr int kBits = 16, kBytes = 2;
+    static constexpr bool kFloat = true;
+    static constexpr uint32_t kOrdNegInf = 0x03FFu, kOrdPosInf = 0xFC00u;
     __device__ __forceinline__ static uint32_t ord(uint32_t r) {
         r = (r == 0x8000u) ? 0u : r;
         return r ^ ((r & 0x8000u) ? 0xFFFFu : 0x8000u);
+    }
+    __device__ __forceinline__ static uint32_t inv_ord(uint32_t o) {
+        return (o & 0x8000u) ? (o ^ 0x8000u) : (~o & 0xFFFFu);
+    }
+    __device__ __forceinline__ static uint32_t word(uint32_t r) { return r; }
+    __device__ __forceinline__ static uint32_t raw(uint32_t w) { return w; }
+    __device__ __forceinline__ static float value(uint32_t w) {
+        return (float)__builtin_bit_cast(_Float16, (uint16_t)w);
+    }
+    __device__ __forceinline__ static uint32_t value_bits(uint32_t r) {
+        return __float_as_uint((float)__builtin_bit_cast(_Float16, (uint16_t)r));
     }
 };
 template <> struct Key<SEGTOPK_KEY_U32> {
     static constexpr int kBits = 32, kBytes = 4;
+    static constexpr bool kFloat = false;
     __device__ __forceinline__ static uint32_t ord(uint32_t r) { return r; }
+    __device__ __forceinline__ static uint32_t word(uint32_t r) { return r; }
+    __device__ __forceinline__ static uint32_t raw(uint32_t w) { return w; }
 };
 template <> struct Key<SEGTOPK_KEY_I32> {
     static constexpr int kBits = 32, kBytes = 4;
+    static constexpr bool kFloat = false;
     __device__ __forceinline__ static uint32_t ord(uint32_t r) { return r ^ 0x80000000u; }
+    __device__ __forceinline__ static uint32_t word(uint32_t r) { return r; }
+    __device__ __forceinline__ static uint32_t raw(uint32_t w) { return w; }
 };
+
+// Pass-0 bucket rank of an ordered key: 0 is the best bucket.
+template <int KT, bool LARGEST> __device__ __forceinline__ uint32_t rank0(uint32_t o) {
+    constexpr int sh = Key<KT>::kBits - kDigit;
+    const uint32_t d = o >> sh;
+    return LARGEST ? (uint32_t)(kBuckets - 1) - d : d;
+}
+// Ordered-key threshold of "rank0 <= R": for MAX o >= thr, for MIN o <= thr.
+template <int KT, bool LARGEST> __device__ __forceinline__ uint32_t rank_thr(uint32_t R) {
+    constexpr int sh = Key<KT>::kBits - kDigit;
+    return LARGEST ? ((uint32_t)(kBuckets - 1) - R) << sh : (R << sh) | ((1u << sh) - 1u);
+}
+template <bool LARGEST> __device__ __forceinline__ bool within(uint32_t o, uint32_t thr) {
+    return LARGEST ? o >= thr : o <= thr;
+}
+
+// Pre-filter for "rank0 <= R" in the keys' own domain: one float or integer
+// comparison per key instead of the ordered-bits transform.  The bucket's
+// first (MAX) or last (MIN) ordered value is turned back into a key; float
+// comparison agrees with the ordered bits except that it holds -0.0 and +0.0
+// equal, which can only let a few more keys through, never fewer.  The exact
+// test follows for the keys that pass.  mode: 0 every key passes, 1 compare
+// against T, 2 no (non-NaN) key passes.
+struct FastBound {
+    uint32_t mode, T;
+};
+template <int KT, bool LARGEST> __device__ __forceinline__ FastBound fast_bound(uint32_t R) {
+    const uint32_t thr = rank_thr<KT, LARGEST>(R);
+    FastBound f;
+    f.mode = 1;
+    if constexpr (!Key<KT>::kFloat) {
+        f.T = (KT == SEGTOPK_KEY_I32) ? (thr ^ 0x80000000u) : thr;
+    } else {
+        f.T = 0;
+        if (LARGEST ? thr <= Key<KT>::kOrdNegInf : thr >= Key<KT>::kOrdPosInf)
+            f.mode = 0;
+        else if (LARGEST ? thr > Key<KT>::kOrdPosInf : thr < Key<KT>::kOrdNegInf)
+            f.mode = 2;
+        else
+            f.T = Key<KT>::value_bits(Key<KT>::inv_ord(thr));
+    }
+    return f;
+}
+template <int KT, bool LARGEST>
+__device__ __forceinline__ bool fast_pass(uint32_t w, const FastBound &f) {
+    if constexpr (Key<KT>::kFloat) {
+        const float v = Key<KT>::value(w), t = __uint_as_float(f.T);
+        return f.mode == 0 || (f.mode == 1 && (LARGEST ? v >= t : v <= t));
+    } else if constexpr (KT == SEGTOPK_KEY_I32) {
+        return LARGEST ? (int32_t)w >= (int32_t)f.T : (int32_t)w <= (int32_t)f.T;
+    } else {
+        return LARGEST ? w >= f.T : w <= f.T;
+    }
+}
 
 // ---------------------------------------------------------------------------
 // Wave helpers (wave64).
@@ -102,30 +204,131 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
                                      __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
+// Inclusive prefix sum over the wave with DPP row shifts (within each row of
+// 16 lanes), then row broadcasts of lane 15 and lane 31 across rows.  Lanes
+// with no source lane add 0.
 __device__ __forceinline__ uint32_t wave_incl_sum(uint32_t x) {
-    const int ln = (int)lane_id();
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        uint32_t y = __shfl_up(x, (unsigned)d, 64);
-        if (ln >= d) x += y;
-    }
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, false);  // row_shr:1
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, false);  // row_shr:2
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, false);  // row_shr:4
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, false);  // row_shr:8
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);  // row_bcast:31
     return x;
 }
 
-// Reserves one slot per lane with `pred` from an LDS counter, with one atomic
-// per wave; returns this lane's slot (meaningless where !pred).
-__device__ __forceinline__ uint32_t wave_reserve(uint32_t *ctr, bool pred) {
-    const uint64_t m = __ballot(pred);
-    if (m == 0) return 0;
-    const uint32_t leader = (uint32_t)__ffsll((unsigned long long)m) - 1u;
-    uint32_t base = 0;
-    if (lane_id() == leader) base = atomicAdd(ctr, (uint32_t)__popcll(m));
-    base = __shfl(base, (int)leader, 64);
-    return base + lanes_below(m);
+// Value of x in lane `src` (a wave-uniform lane index), in a scalar register.
+__device__ __forceinline__ uint32_t wave_bcast(uint32_t x, uint32_t src) {
+    return (uint32_t)__builtin_amdgcn_readlane((int)x, (int)src);
+}
+
+// Orders this wave's LDS accesses across lanes (lanes run in lockstep; this
+// keeps the compiler from moving LDS traffic across the point).
+__device__ __forceinline__ void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+struct Kth {
+    uint32_t found;   // 0: the buckets hold fewer than `target` keys
+    uint32_t b;       // the bucket holding the target-th key
+    uint32_t before;  // keys in buckets before b
+    uint32_t count;   // keys in bucket b
+};
+
+// Smallest bucket b < nb with hist[0] + ... + hist[b] >= target, by one wave:
+// every lane sums a run of buckets, a wave scan finds the lane whose run
+// crosses the target, then the lanes take one bucket each of that run.
+// hist may be filled concurrently by other waves: every count read is at most
+// the final count, so the bucket found is at or after the final one.
+__device__ __forceinline__ Kth wave_find(const uint32_t *hist, uint32_t nb, uint32_t target) {
+    const uint32_t ln = lane_id();
+    uint32_t per = (nb + 63u) >> 6;
+    per = (per + 3u) & ~3u;  // 4 .. 32 buckets per lane
+    const uint32_t b0 = ln * per;
+    uint32_t s = 0;
+#pragma unroll
+    for (uint32_t q = 0; q < 32; q += 4) {
+        const uint32_t b = b0 + q;
+        if (q < per && b < nb) {
+            const uint4 h = *reinterpret_cast<const uint4 *>(&hist[b]);
+            s += h.x + (b + 1 < nb ? h.y : 0u) + (b + 2 < nb ? h.z : 0u) + (b + 3 < nb ? h.w : 0u);
+        }
+    }
+    const uint32_t incl = wave_incl_sum(s);
+    const uint32_t excl = incl - s;
+    const uint64_t hit = __ballot(excl < target && incl >= target);
+    Kth r;
+    if (hit == 0) {
+        r.found = 0;
+        r.b = nb - 1;
+        r.before = 0;
+        r.count = 0;
+        return r;
+    }
+    const uint32_t L = (uint32_t)__ffsll((unsigned long long)hit) - 1u;
+    const uint32_t baseL = wave_bcast(excl, L);
+    const uint32_t bl = L * per + ln;
+    const uint32_t v = (ln < per && bl < nb) ? hist[bl] : 0u;
+    const uint32_t vi = wave_incl_sum(v);
+    const uint64_t hit2 = __ballot(ln < per && baseL + vi >= target);
+    const uint32_t j = (uint32_t)__ffsll((unsigned long long)hit2) - 1u;
+    r.found = 1;
+    r.b = L * per + j;
+    r.count = wave_bcast(v, j);
+    r.before = baseL + wave_bcast(vi, j) - r.count;
+    return r;
+}
+
+// wave_find over a histogram in global memory that other workgroups are still
+// adding to (relaxed agent-scope loads; any count read is at most the final
+// count, so the bucket found is at or after the final one).
+__device__ __forceinline__ Kth wave_find_global(const uint32_t *g, uint32_t nb, uint32_t target) {
+    const uint32_t ln = lane_id();
+    const uint32_t per = (nb + 63u) >> 6;  // 1 .. 32 buckets per lane
+    const uint32_t b0 = ln * per;
+    uint32_t s = 0;
+    for (uint32_t q = 0; q < per; ++q) {
+        const uint32_t b = b0 + q;
+        if (b < nb) s += __hip_atomic_load(&g[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    const uint32_t incl = wave_incl_sum(s);
+    const uint32_t excl = incl - s;
+    const uint64_t hit = __ballot(excl < target && incl >= target);
+    Kth r;
+    r.found = 0;
+    r.b = nb - 1;
+    r.before = 0;
+    r.count = 0;
+    if (hit == 0) return r;
+    const uint32_t L = (uint32_t)__ffsll((unsigned long long)hit) - 1u;
+    const uint32_t baseL = wave_bcast(excl, L);
+    const uint32_t bl = L * per + ln;
+    const uint32_t v = (ln < per && bl < nb)
+                           ? __hip_atomic_load(&g[bl], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                           : 0u;
+    const uint32_t vi = wave_incl_sum(v);
+    const uint64_t hit2 = __ballot(ln < per && baseL + vi >= target);
+    if (hit2 == 0) return r;  // the counts grew between the two reads: no tighter bound now
+    const uint32_t j = (uint32_t)__ffsll((unsigned long long)hit2) - 1u;
+    r.found = 1;
+    r.b = L * per + j;
+    return r;
+}
+
+__device__ __forceinline__ void wave_clear(uint32_t *hist, uint32_t nb) {
+    const uint32_t ln = lane_id();
+    if (nb >= 256) {
+        for (uint32_t i = ln * 4; i < nb; i += 4 * kWave)
+            *reinterpret_cast<uint4 *>(&hist[i]) = make_uint4(0u, 0u, 0u, 0u);
+    } else {
+        for (uint32_t i = ln; i < nb; i += kWave) hist[i] = 0u;
+    }
 }
 
 // ---------------------------------------------------------------------------
-// Kernel arguments and per-workgroup LDS.
+// Kernel arguments.
 // ---------------------------------------------------------------------------
 struct Params {
     const void *keys_in;
@@ -138,27 +341,16 @@ struct Params {
     uint32_t det;            // deterministic tie-break requested
     uint32_t prefer_larger;  // ties toward larger source indices
     uint32_t sorted;         // sorted or stable_sorted output
-    uint32_t stash_cap;      // LDS stash entries
+    uint32_t stash_cap;      // LDS stash entries per workgroup (four equal wave regions)
     uint32_t out_cap;        // LDS output staging entries (power of two), 0 = none
     uint32_t wg_per_seg;     // workgroups per segment (1: one workgroup each)
     uint32_t min_slice;      // smallest slice a segment is split into
-    uint32_t *ws_hist;       // [num_segments][kBuckets]   merged pass-0 histograms
-    uint32_t *ws_ticket;     // [num_segments]             arrival tickets
-    uint32_t *ws_slot_info;  // [num_segments][wg_per_seg][2] (count, overflowed)
-    uint2 *ws_slot_data;     // [num_segments][wg_per_seg][stash_cap]
-};
-
-struct alignas(16) Smem {
-    uint32_t hist[kBuckets];
-    uint32_t touched[3];     // a chunk changed the histogram (rotating flags)
-    uint32_t pending[3];     // stash entries a chunk wants to add (rotating)
-    uint32_t stash_count;
-    uint32_t stash_bad;      // the stash lost candidates: re-stream instead
-    uint32_t res[4];         // find_kth result: found, bucket, count before, count in
-    uint32_t ctr[2];         // output placement counters (better, tie)
-    uint32_t compact_ctr;
-    uint32_t snap;           // stash_count as seen before a chunk's pushes
-    uint32_t flag;
+    uint32_t *ws_hist;       // [segments][kBuckets]    merged pass-0 histograms
+    uint32_t *ws_early;      // [segments][kBuckets]    early snapshots (bound sharing)
+    uint32_t *ws_ticket;     // [segments]              arrival tickets
+    uint32_t *ws_slot_info;  // [segments][P][4]        (count, overflowed, bound, -)
+    uint32_t *ws_slot_cum;   // [segments][P][kBuckets] entries with rank <= r
+    uint2 *ws_slot_data;     // [segments][P][stash_cap] candidates sorted by rank
 };
 
 struct Seg {
@@ -169,69 +361,22 @@ struct Seg {
 };
 
 // ---------------------------------------------------------------------------
-// Smallest bucket b < nb with hist[0] + ... + hist[b] >= target, found by
-// wave 0 alone.  res = {found, b, sum before b, hist[b]}; found = 0 when the
-// buckets hold fewer than `target` keys.
+// Coalesced reader of the keys [lo, hi) of one segment by NT threads: an
+// unaligned head and tail (under 16 bytes each) element by element, the
+// aligned body with 16-byte loads, U loads per thread per chunk.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void find_kth(const uint32_t *hist, uint32_t nb, uint32_t target, uint32_t *res) {
-    const uint32_t ln = lane_id();
-    uint32_t per = (nb + 63u) >> 6;
-    per = (per + 3u) & ~3u;
-    const uint32_t b0 = ln * per;
-    uint32_t s = 0;
-    for (uint32_t q = 0; q < per; q += 4) {
-        const uint32_t b = b0 + q;
-        if (b < nb) {
-            const uint4 h = *reinterpret_cast<const uint4 *>(&hist[b]);
-            s += h.x + (b + 1 < nb ? h.y : 0u) + (b + 2 < nb ? h.z : 0u) + (b + 3 < nb ? h.w : 0u);
-        }
-    }
-    const uint32_t incl = wave_incl_sum(s);
-    const uint32_t excl = incl - s;
-    const uint64_t hit = __ballot(excl < target && incl >= target);
-    if (hit == 0) {
-        if (ln == 0) {
-            res[0] = 0;
-            res[1] = nb - 1;
-            res[2] = 0;
-            res[3] = 0;
-        }
-        return;
-    }
-    const uint32_t L = (uint32_t)__ffsll((unsigned long long)hit) - 1u;
-    if (ln == L) {
-        uint32_t acc = excl;
-        for (uint32_t q = 0; q < per; ++q) {
-            const uint32_t h = hist[b0 + q];
-            if (acc + h >= target) {
-                res[0] = 1;
-                res[1] = b0 + q;
-                res[2] = acc;
-                res[3] = h;
-                break;
-            }
-            acc += h;
-        }
-    }
-}
-
-// ---------------------------------------------------------------------------
-// Coalesced reader of the keys [lo, hi) of one segment: an unaligned head and
-// tail (fewer than 16 bytes each) are read element by element, the aligned body
-// with 16-byte loads, kU loads per thread per chunk.
-// ---------------------------------------------------------------------------
-template <int KT> struct Range {
+template <int KT, int NT, int U> struct Range {
     static constexpr int kBytes = Key<KT>::kBytes;
     static constexpr int kVec = 16 / kBytes;  // keys per 16-byte load
-    static constexpr int kU = 4;              // loads per thread per chunk
+    static constexpr int kU = U;
     static constexpr int kKpt = kU * kVec;    // keys per thread per chunk
-    static constexpr uint32_t kChunkVecs = kThreads * kU;
+    static constexpr uint32_t kChunkVecs = NT * kU;
 
     const unsigned char *ebase;  // element 0 of the segment
     const uint4 *vbase;          // first aligned vector of the range
     uint32_t lo, head, nvec, tail_lo, nscalar, nchunks;
 
-    __device__ void init(const void *keys, int64_t begin, uint32_t lo_, uint32_t hi_) {
+    __device__ __forceinline__ void init(const void *keys, int64_t begin, uint32_t lo_, uint32_t hi_) {
         ebase = static_cast<const unsigned char *>(keys) + begin * kBytes;
         lo = lo_;
         const uint32_t len = hi_ - lo_;
@@ -251,13 +396,13 @@ template <int KT> struct Range {
         if (kBytes == 4) return reinterpret_cast<const uint32_t *>(ebase)[idx];
         return reinterpret_cast<const uint16_t *>(ebase)[idx];
     }
-    // Thread t's part of chunk c: raw[u * kVec + e] is element vidx[u] + e;
-    // vidx[u] == kNone marks a load past the end.
+    // Thread t's part of chunk c: raw[u * kVec + e] holds element vidx[u] + e
+    // (as a word of its key type); vidx[u] == kNone marks a load past the end.
     __device__ __forceinline__ void load_chunk(uint32_t c, uint32_t t, uint32_t (&raw)[kKpt],
                                                uint32_t (&vidx)[kU]) const {
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
-            const uint32_t vj = c * kChunkVecs + (uint32_t)u * kThreads + t;
+            const uint32_t vj = c * kChunkVecs + (uint32_t)u * NT + t;
             uint4 v = make_uint4(0u, 0u, 0u, 0u);
             vidx[u] = kNone;
             if (vj < nvec) {
@@ -270,19 +415,18 @@ template <int KT> struct Range {
                 raw[u * 4 + 2] = v.z;
                 raw[u * 4 + 3] = v.w;
             } else {
-                raw[u * 8 + 0] = v.x & 0xFFFFu;
-                raw[u * 8 + 1] = v.x >> 16;
-                raw[u * 8 + 2] = v.y & 0xFFFFu;
-                raw[u * 8 + 3] = v.y >> 16;
-                raw[u * 8 + 4] = v.z & 0xFFFFu;
-                raw[u * 8 + 5] = v.z >> 16;
-                raw[u * 8 + 6] = v.w & 0xFFFFu;
-                raw[u * 8 + 7] = v.w >> 16;
+                // Two 16-bit keys per dword, as words of their type.
+                const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int h = 0; h < 4; ++h) {
+                    raw[u * 8 + 2 * h] = Key<KT>::word(d[h] & 0xFFFFu);
+                    raw[u * 8 + 2 * h + 1] = Key<KT>::word(d[h] >> 16);
+                }
             }
         }
     }
     // Calls f(raw, idx, active) for every element, chunk by chunk; every lane
-    // of every wave makes the same sequence of calls.
+    // of the thread group makes the same sequence of calls.
     template <class F> __device__ __forceinline__ void for_each(uint32_t t, F &&f) const {
         {
             const bool act = t < nscalar;
@@ -296,241 +440,267 @@ template <int KT> struct Range {
             for (int u = 0; u < kU; ++u)
 #pragma unroll
                 for (int e = 0; e < kVec; ++e)
-                    f(raw[u * kVec + e], vidx[u] + (uint32_t)e, vidx[u] != kNone);
+                    f(Key<KT>::raw(raw[u * kVec + e]), vidx[u] + (uint32_t)e, vidx[u] != kNone);
         }
     }
 };
 
-// Pass-0 bucket rank of an ordered key: 0 is the best bucket.
-template <int KT, bool LARGEST> __device__ __forceinline__ uint32_t rank0(uint32_t o) {
-    constexpr int sh = Key<KT>::kBits - kDigit;
-    const uint32_t d = o >> sh;
-    return LARGEST ? (uint32_t)(kBuckets - 1) - d : d;
-}
-
-// Ordered-key threshold of "rank0 <= R": for MAX o >= thr, for MIN o <= thr.
-template <int KT, bool LARGEST> __device__ __forceinline__ uint32_t rank_thr(uint32_t R) {
-    constexpr int sh = Key<KT>::kBits - kDigit;
-    return LARGEST ? ((uint32_t)(kBuckets - 1) - R) << sh
-                   : (R << sh) | ((1u << sh) - 1u);
-}
-template <bool LARGEST> __device__ __forceinline__ bool within(uint32_t o, uint32_t thr) {
-    return LARGEST ? o >= thr : o <= thr;
-}
+template <int KT> using WaveRange = Range<KT, kWave, 4>;
 
 // ---------------------------------------------------------------------------
-// Stash maintenance.
+// Pass 0 of one wave over keys [lo, hi) of a segment into a histogram shared
+// with the other waves of the workgroup and into the wave's own stash.
 // ---------------------------------------------------------------------------
+// Bound sharing between the workgroups of one segment (slice mode): the
+// workgroup adds an early snapshot of its histogram to a per-segment global
+// "early" histogram once, and its waves periodically turn that histogram
+// into a bound, published to the other waves through an LDS word.
+struct Share {
+    uint32_t *rg;        // LDS: best bound known to the workgroup
+    uint32_t *flag;      // LDS: the workgroup has contributed its snapshot
+    uint32_t *gearly;    // global: the segment's early histogram, or nullptr
+    uint32_t wave;       // this wave's index in the workgroup
+};
 
-// Drops, in place, every stash entry whose pass-0 rank is beyond R.
-// All threads call it; it contains barriers.
+struct Pass0 {
+    uint32_t R;      // the wave's final bound (rank)
+    uint32_t count;  // stash entries
+    bool bad;        // the stash lost candidates: re-read [lo, hi) instead
+};
+
+// Drops, in place, the stash entries whose pass-0 rank is beyond the bound.
 template <int KT, bool LARGEST>
-__device__ __forceinline__ uint32_t compact_stash(Smem &sm, uint2 *stash, uint32_t cnt, uint32_t R) {
-    const uint32_t t = threadIdx.x;
-    const uint32_t thr = rank_thr<KT, LARGEST>(R);
-    if (t == 0) sm.compact_ctr = 0;
-    __syncthreads();
-    constexpr int kR = 4;
-    for (uint32_t base = 0; base < cnt; base += kR * kThreads) {
-        uint2 e[kR];
-        bool keep[kR];
-#pragma unroll
-        for (int r = 0; r < kR; ++r) {
-            const uint32_t i = base + (uint32_t)r * kThreads + t;
-            keep[r] = false;
-            if (i < cnt) {
-                e[r] = stash[i];
-                keep[r] = within<LARGEST>(Key<KT>::ord(e[r].x), thr);
-            }
-        }
-        __syncthreads();  // every read of this round precedes every write
-#pragma unroll
-        for (int r = 0; r < kR; ++r) {
-            const uint32_t pos = wave_reserve(&sm.compact_ctr, keep[r]);
-            if (keep[r]) stash[pos] = e[r];
-        }
+__device__ __forceinline__ uint32_t wave_compact(uint2 *stash, uint32_t cnt, uint32_t thr) {
+    const uint32_t ln = lane_id();
+    uint32_t out = 0;
+    for (uint32_t base = 0; base < cnt; base += kWave) {
+        const uint32_t i = base + ln;
+        const bool act = i < cnt;
+        const uint2 e = act ? stash[i] : make_uint2(0u, 0u);
+        const bool keep = act && within<LARGEST>(Key<KT>::ord(e.x), thr);
+        const uint64_t m = __ballot(keep);
+        wave_sync();  // this round's reads come before its writes
+        if (keep) stash[out + lanes_below(m)] = e;
+        out += (uint32_t)__popcll(m);
+        wave_sync();
     }
-    __syncthreads();
-    if (t == 0) sm.stash_count = sm.compact_ctr;
-    __syncthreads();
-    return sm.compact_ctr;  // unchanged until the next compaction
+    return out;
 }
 
-// ---------------------------------------------------------------------------
-// Pass 0 over the keys [lo, hi) of a segment: the filtered histogram and the
-// stash.  Returns the final bound R; sm.res holds the find result for R
-// (res[0] == 0 when the range holds fewer than `target` keys, then R is the
-// last bucket and every key was kept).  sm.stash_bad says whether the stash
-// holds every key with rank <= R.
-// ---------------------------------------------------------------------------
 template <int KT, bool LARGEST>
-__device__ __forceinline__ uint32_t pass0(Smem &sm, uint2 *stash, uint32_t cap, const Params &p, const Seg &sg,
-                          uint32_t lo, uint32_t hi, uint32_t target) {
-    using Rg = Range<KT>;
+__device__ __forceinline__ Pass0 wave_pass0(uint32_t *hist, uint2 *stash, uint32_t cap,
+                                            const void *keys, int64_t begin, uint32_t lo,
+                                            uint32_t hi, uint32_t target, const Share &sh) {
+    using Rg = WaveRange<KT>;
     constexpr int K = Rg::kKpt;
-    const uint32_t t = threadIdx.x;
-    const uint32_t wave = t >> 6;
-
-    for (uint32_t i = t; i < (uint32_t)kBuckets; i += kThreads) sm.hist[i] = 0;
-    if (t == 0) {
-        sm.touched[0] = sm.touched[1] = sm.touched[2] = 0;
-        sm.pending[0] = sm.pending[1] = sm.pending[2] = 0;
-        sm.stash_count = 0;
-        sm.stash_bad = 0;
-        sm.res[0] = 0;
-        sm.res[1] = kBuckets - 1;
-        sm.res[2] = 0;
-        sm.res[3] = 0;
-    }
-
+    const uint32_t ln = lane_id();
     Rg L;
-    L.init(p.keys_in, sg.begin, lo, hi);
+    L.init(keys, begin, lo, hi);
     const uint32_t nch = L.nchunks > 0 ? L.nchunks : 1u;
-
-    uint32_t R = kBuckets - 1;  // until `target` keys are seen every bucket may hold the k-th
-    bool bad = false;
+    Pass0 r;
+    r.R = kBuckets - 1;  // until `target` keys are counted any bucket may hold the k-th
+    r.count = 0;
+    r.bad = false;
+    bool bounded = false;
+    FastBound fb;
+    fb.mode = 0;
+    fb.T = 0;
     uint32_t raw[K], vidx[Rg::kU];
-    L.load_chunk(0, t, raw, vidx);
-    __syncthreads();
-
+    L.load_chunk(0, ln, raw, vidx);
     for (uint32_t c = 0; c < nch; ++c) {
-        // This chunk's keys, and in chunk 0 one key of the unaligned head/tail.
         uint32_t cur[K], cv[Rg::kU];
 #pragma unroll
         for (int j = 0; j < K; ++j) cur[j] = raw[j];
 #pragma unroll
         for (int u = 0; u < Rg::kU; ++u) cv[u] = vidx[u];
-        const bool sv = (c == 0) && t < L.nscalar;
-        const uint32_t si = sv ? L.scalar_idx(t) : 0u;
-        const uint32_t sr = sv ? L.load_scalar(si) : 0u;
+        // The unaligned head and tail ride along with chunk 0.
+        const bool sv = (c == 0) && ln < L.nscalar;
+        const uint32_t si = sv ? L.scalar_idx(ln) : 0u;
+        const uint32_t sw = sv ? Key<KT>::word(L.load_scalar(si)) : 0u;
+        if (c + 1 < nch) L.load_chunk(c + 1, ln, raw, vidx);  // prefetch
 
-        // Prefetch the next chunk while this one is counted.
-        if (c + 1 < nch) L.load_chunk(c + 1, t, raw, vidx);
-
-        // 1. Count keys whose bucket can still hold the k-th key.
-        const uint32_t thr = rank_thr<KT, LARGEST>(R);
-        bool any = false;
-#pragma unroll
-        for (int u = 0; u < Rg::kU; ++u)
-#pragma unroll
-            for (int e = 0; e < Rg::kVec; ++e) {
-                const uint32_t o = Key<KT>::ord(cur[u * Rg::kVec + e]);
-                if (cv[u] != kNone && within<LARGEST>(o, thr)) {
-                    atomicAdd(&sm.hist[rank0<KT, LARGEST>(o)], 1u);
-                    any = true;
+        if (sh.gearly) {
+            // Adopt a tighter bound found by another wave of this workgroup.
+            const uint32_t rg = __hip_atomic_load(sh.rg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            if (rg < r.R) {
+                r.R = rg;
+                bounded = true;
+                fb = fast_bound<KT, LARGEST>(r.R);
+            }
+            if (bounded && c >= 1) {
+                // Once per workgroup: add the histogram so far to the segment's
+                // early histogram.  Every fourth chunk one wave reads it back.
+                uint32_t first = 0;
+                if (c == 1 && ln == 0) first = atomicCAS(sh.flag, 0u, 1u) == 0u ? 1u : 0u;
+                if (wave_bcast(first, 0)) {
+                    for (uint32_t b = ln; b <= r.R; b += kWave) {
+                        const uint32_t v = hist[b];
+                        if (v) atomicAdd(&sh.gearly[b], v);
+                    }
+                }
+                if ((c & 3u) == 3u && ((c >> 2) & 3u) == (sh.wave & 3u)) {
+                    const Kth g = wave_find_global(sh.gearly, r.R + 1, target);
+                    if (g.found && g.b < r.R) {
+                        r.R = g.b;
+                        fb = fast_bound<KT, LARGEST>(r.R);
+                        if (ln == 0) atomicMin(sh.rg, g.b);
+                    }
                 }
             }
-        if (sv) {
-            const uint32_t o = Key<KT>::ord(sr);
-            if (within<LARGEST>(o, thr)) {
-                atomicAdd(&sm.hist[rank0<KT, LARGEST>(o)], 1u);
-                any = true;
-            }
         }
-        if (__any(any) && lane_id() == 0) sm.touched[c % 3] = 1;
-        if (t == 0) {
-            sm.touched[(c + 1) % 3] = 0;
-            sm.pending[(c + 1) % 3] = 0;
-        }
-        __syncthreads();
-        if (!sm.touched[c % 3]) continue;  // uniform: bound and stash unchanged
 
-        // 2. New bound: the k-th best bucket of everything counted so far.
-        if (wave == 0) find_kth(sm.hist, R + 1, target, sm.res);
-        __syncthreads();
-        if (sm.res[0]) R = sm.res[1];
-        if (bad) continue;
-
-        // 3. Stash this chunk's keys within the new bound.
-        const uint32_t thr2 = rank_thr<KT, LARGEST>(R);
-        uint32_t cnt = (sv && within<LARGEST>(Key<KT>::ord(sr), thr2)) ? 1u : 0u;
-#pragma unroll
-        for (int u = 0; u < Rg::kU; ++u)
-#pragma unroll
-            for (int e = 0; e < Rg::kVec; ++e)
-                cnt += (cv[u] != kNone && within<LARGEST>(Key<KT>::ord(cur[u * Rg::kVec + e]), thr2))
-                           ? 1u : 0u;
-        {
-            const uint32_t wsum = __shfl(wave_incl_sum(cnt), 63, 64);
-            if (lane_id() == 0 && wsum) atomicAdd(&sm.pending[c % 3], wsum);
-        }
-        // No push has started yet, so every thread sees the same count.
-        if (t == 0) sm.snap = sm.stash_count;
-        __syncthreads();
-        const uint32_t need = sm.pending[c % 3];
-        uint32_t have = sm.snap;
-        if (have + need > cap) {
-            have = compact_stash<KT, LARGEST>(sm, stash, have, R);
-            if (have + need > cap) {
-                bad = true;  // uniform: every thread read the same counts
-                if (t == 0) sm.stash_bad = 1;
-                continue;
-            }
-        }
-        // Append (one LDS atomic per wave).
-        const uint32_t incl = wave_incl_sum(cnt);
-        const uint32_t total = __shfl(incl, 63, 64);
-        if (total) {
-            uint32_t base = 0;
-            if (lane_id() == 0) base = atomicAdd(&sm.stash_count, total);
-            uint32_t pos = __shfl(base, 0, 64) + incl - cnt;
-            if (sv && within<LARGEST>(Key<KT>::ord(sr), thr2)) stash[pos++] = make_uint2(sr, si);
+        if (!bounded) {
+            // No bound yet: count every key, find the bound, then stash the
+            // keys within it.
+            bool any = false;
 #pragma unroll
             for (int u = 0; u < Rg::kU; ++u)
 #pragma unroll
                 for (int e = 0; e < Rg::kVec; ++e) {
-                    const uint32_t r = cur[u * Rg::kVec + e];
-                    if (cv[u] != kNone && within<LARGEST>(Key<KT>::ord(r), thr2))
-                        stash[pos++] = make_uint2(r, cv[u] + (uint32_t)e);
+                    if (cv[u] != kNone) {
+                        atomicAdd(&hist[rank0<KT, LARGEST>(Key<KT>::ord(Key<KT>::raw(cur[u * Rg::kVec + e])))], 1u);
+                        any = true;
+                    }
                 }
+            if (sv) {
+                atomicAdd(&hist[rank0<KT, LARGEST>(Key<KT>::ord(Key<KT>::raw(sw)))], 1u);
+                any = true;
+            }
+            if (!__any(any)) continue;
+            wave_sync();
+            const Kth f = wave_find(hist, kBuckets, target);
+            if (f.found) {
+                r.R = f.b;
+                bounded = true;
+                fb = fast_bound<KT, LARGEST>(r.R);
+            }
+            if (r.bad) continue;
+            const uint32_t thr2 = rank_thr<KT, LARGEST>(r.R);
+            uint32_t cnt = (sv && within<LARGEST>(Key<KT>::ord(Key<KT>::raw(sw)), thr2)) ? 1u : 0u;
+#pragma unroll
+            for (int u = 0; u < Rg::kU; ++u)
+#pragma unroll
+                for (int e = 0; e < Rg::kVec; ++e)
+                    cnt += (cv[u] != kNone &&
+                            within<LARGEST>(Key<KT>::ord(Key<KT>::raw(cur[u * Rg::kVec + e])), thr2))
+                               ? 1u : 0u;
+            const uint32_t incl = wave_incl_sum(cnt);
+            const uint32_t total = wave_bcast(incl, kWave - 1);
+            if (r.count + total > cap) {
+                wave_sync();
+                r.count = wave_compact<KT, LARGEST>(stash, r.count, thr2);
+                if (r.count + total > cap) {
+                    r.bad = true;
+                    continue;
+                }
+            }
+            uint32_t pos = r.count + incl - cnt;
+            if (sv && within<LARGEST>(Key<KT>::ord(Key<KT>::raw(sw)), thr2))
+                stash[pos++] = make_uint2(Key<KT>::raw(sw), si);
+#pragma unroll
+            for (int u = 0; u < Rg::kU; ++u)
+#pragma unroll
+                for (int e = 0; e < Rg::kVec; ++e) {
+                    const uint32_t x = Key<KT>::raw(cur[u * Rg::kVec + e]);
+                    if (cv[u] != kNone && within<LARGEST>(Key<KT>::ord(x), thr2))
+                        stash[pos++] = make_uint2(x, cv[u] + (uint32_t)e);
+                }
+            r.count += total;
+            continue;
+        }
+
+        // Bounded: one native comparison per key; only a slot in which some
+        // lane passes takes the exact test, the count and the stash push.
+        bool anyp = sv && fast_pass<KT, LARGEST>(sw, fb);
+#pragma unroll
+        for (int u = 0; u < Rg::kU; ++u)
+#pragma unroll
+            for (int e = 0; e < Rg::kVec; ++e)
+                anyp = anyp || (cv[u] != kNone && fast_pass<KT, LARGEST>(cur[u * Rg::kVec + e], fb));
+        if (!__any(anyp)) continue;
+        uint32_t counted = 0;
+        auto take = [&](uint32_t w, uint32_t idx, bool valid) {
+            const bool pv = valid && fast_pass<KT, LARGEST>(w, fb);
+            if (!__any(pv)) return;
+            const uint32_t x = Key<KT>::raw(w);
+            const uint32_t rk = rank0<KT, LARGEST>(Key<KT>::ord(x));
+            const bool ex = pv && rk <= r.R;
+            if (ex) atomicAdd(&hist[rk], 1u);
+            const uint64_t m = __ballot(ex);
+            const uint32_t n = (uint32_t)__popcll(m);
+            counted += n;
+            if (r.bad || n == 0) return;
+            if (r.count + n > cap) {
+                wave_sync();
+                r.count = wave_compact<KT, LARGEST>(stash, r.count, rank_thr<KT, LARGEST>(r.R));
+                if (r.count + n > cap) {
+                    r.bad = true;
+                    return;
+                }
+            }
+            if (ex) stash[r.count + lanes_below(m)] = make_uint2(x, idx);
+            r.count += n;
+        };
+        take(sw, si, sv);
+#pragma unroll
+        for (int u = 0; u < Rg::kU; ++u)
+#pragma unroll
+            for (int e = 0; e < Rg::kVec; ++e)
+                take(cur[u * Rg::kVec + e], cv[u] + (uint32_t)e, cv[u] != kNone);
+        if (counted) {
+            // Tighten the bound from everything counted so far.
+            wave_sync();
+            const Kth f = wave_find(hist, r.R + 1, target);
+            if (f.found && f.b < r.R) {
+                r.R = f.b;
+                fb = fast_bound<KT, LARGEST>(r.R);
+            }
         }
     }
-    __syncthreads();
-    return R;
+    return r;
 }
 
 // ---------------------------------------------------------------------------
-// Candidate sources for the passes after pass 0.
+// Candidates after pass 0, visited by wave 0: an LDS list, or (when a stash
+// overflowed) global sources -- per slice either the first `cnt` entries of a
+// global slot or, for an overflowed slot, the slice's keys again.
 // ---------------------------------------------------------------------------
 template <int KT> struct Cands {
-    // LDS stash ...
-    const uint2 *stash;
+    const uint2 *list;      // LDS list ...
     uint32_t count;
     bool lds;
-    // ... or global memory: nslots slices of `slice` keys; a slice whose slot
-    // overflowed (or every slice, when there are no slots) is re-read from the
-    // keys.
-    const void *keys_in;
+    const void *keys_in;    // ... or global sources
     int64_t begin;
-    uint32_t n, nslots, slice, slot_cap;
-    const uint32_t *slot_info;  // nullptr: no slots, stream the keys
+    uint32_t n, nslices, slice;
+    const uint32_t *slot_info;  // nullptr: every slice is re-read from the keys
+    const uint32_t *slot_cum;
     const uint2 *slot_data;
+    uint32_t slot_cap, bstar;
 
     template <class F> __device__ __forceinline__ void visit(F &&f) const {
-        const uint32_t t = threadIdx.x;
+        const uint32_t ln = lane_id();
         if (lds) {
-            for (uint32_t base = 0; base < count; base += kThreads) {
-                const uint32_t i = base + t;
+            for (uint32_t base = 0; base < count; base += kWave) {
+                const uint32_t i = base + ln;
                 const bool act = i < count;
-                const uint2 e = act ? stash[i] : make_uint2(0u, 0u);
+                const uint2 e = act ? list[i] : make_uint2(0u, 0u);
                 f(e.x, e.y, act);
             }
             return;
         }
-        for (uint32_t q = 0; q < nslots; ++q) {
+        for (uint32_t q = 0; q < nslices; ++q) {
             const uint32_t lo = q * slice;
             const uint32_t hi = (n - lo) > slice ? lo + slice : n;
-            const bool stream = slot_info == nullptr || slot_info[2 * q + 1] != 0;
-            if (stream) {
-                Range<KT> L;
+            if (slot_info == nullptr || slot_info[4 * q + 1] != 0) {
+                WaveRange<KT> L;
                 L.init(keys_in, begin, lo, hi);
-                L.for_each(t, f);
+                L.for_each(ln, f);
             } else {
-                uint32_t cnt = slot_info[2 * q];
+                uint32_t cnt = slot_cum[(size_t)q * kBuckets + bstar];
                 cnt = cnt < slot_cap ? cnt : slot_cap;
                 const uint2 *d = slot_data + (size_t)q * slot_cap;
-                for (uint32_t base = 0; base < cnt; base += kThreads) {
-                    const uint32_t i = base + t;
+                for (uint32_t base = 0; base < cnt; base += kWave) {
+                    const uint32_t i = base + ln;
                     const bool act = i < cnt;
                     const uint2 e = act ? d[i] : make_uint2(0u, 0u);
                     f(e.x, e.y, act);
@@ -568,17 +738,17 @@ __device__ __forceinline__ bool out_before(uint2 a, uint2 b) {
     return a.y < b.y;
 }
 
-// Bitonic sort of buf[0, cnt) in LDS.  All threads call it.
+// Bitonic sort of buf[0, cnt) in LDS by one wave.
 template <int KT, bool LARGEST>
-__device__ __forceinline__ void bitonic_sort(uint2 *buf, uint32_t cnt) {
-    const uint32_t t = threadIdx.x;
+__device__ __forceinline__ void wave_bitonic(uint2 *buf, uint32_t cnt) {
+    const uint32_t ln = lane_id();
     uint32_t P = 1;
     while (P < cnt) P <<= 1;
-    for (uint32_t i = cnt + t; i < P; i += kThreads) buf[i] = make_uint2(0u, kNone);
-    __syncthreads();
+    for (uint32_t i = cnt + ln; i < P; i += kWave) buf[i] = make_uint2(0u, kNone);
+    wave_sync();
     for (uint32_t size = 2; size <= P; size <<= 1) {
         for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
-            for (uint32_t i = t; i < (P >> 1); i += kThreads) {
+            for (uint32_t i = ln; i < (P >> 1); i += kWave) {
                 const uint32_t lo = 2 * i - (i & (stride - 1));
                 const uint32_t hi = lo + stride;
                 const bool asc = (lo & size) == 0;
@@ -588,59 +758,172 @@ __device__ __forceinline__ void bitonic_sort(uint2 *buf, uint32_t cnt) {
                     buf[hi] = a;
                 }
             }
-            __syncthreads();
+            wave_sync();
         }
     }
 }
 
+// Output of up to 64*E staged results held in registers, E per lane (lane l
+// holds results l*E .. l*E+E-1).  The values are gathered first so their
+// latency overlaps the sort; sorted output is a bitonic network on
+// (key best-first, index ascending) using lane shuffles for strides of E and
+// more and register swaps below that.
+template <int KT, bool LARGEST, int E>
+__device__ __forceinline__ void out_regs(const uint2 *outbuf, const Params &p, const Seg &sg) {
+    const uint32_t ln = lane_id();
+    uint32_t sk[E], id[E], rw[E], vv[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const uint32_t j = ln * E + e;
+        sk[e] = kNone;
+        id[e] = kNone;
+        rw[e] = 0;
+        vv[e] = 0;
+        if (j < sg.k_i) {
+            const uint2 x = outbuf[j];
+            const uint32_t o = Key<KT>::ord(x.x);
+            sk[e] = LARGEST ? ~o : o;
+            id[e] = x.y;
+            rw[e] = x.x;
+            if (p.vals_in) vv[e] = x.y < sg.n ? p.vals_in[sg.begin + x.y] : kNone;
+        }
+    }
+    if (p.sorted) {
+        for (uint32_t size = 2; size <= (uint32_t)(kWave * E); size <<= 1) {
+            for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
+                if (stride >= (uint32_t)E) {
+                    const int lm = (int)(stride / E);
+#pragma unroll
+                    for (int e = 0; e < E; ++e) {
+                        const uint32_t j = ln * E + e;
+                        const uint32_t psk = __shfl_xor(sk[e], lm, kWave);
+                        const uint32_t pid = __shfl_xor(id[e], lm, kWave);
+                        const uint32_t prw = __shfl_xor(rw[e], lm, kWave);
+                        const uint32_t pvv = __shfl_xor(vv[e], lm, kWave);
+                        const bool asc = (j & size) == 0;
+                        const bool lower = (j & stride) == 0;
+                        const bool pfirst = psk < sk[e] || (psk == sk[e] && pid < id[e]);
+                        if ((lower == asc) ? pfirst : !pfirst) {
+                            sk[e] = psk;
+                            id[e] = pid;
+                            rw[e] = prw;
+                            vv[e] = pvv;
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < E; ++e) {
+                        if (e & stride) continue;
+                        const int f = e | (int)stride;
+                        const uint32_t j = ln * E + e;
+                        const bool asc = (j & size) == 0;
+                        const bool ffirst = sk[f] < sk[e] || (sk[f] == sk[e] && id[f] < id[e]);
+                        if (ffirst == asc) {
+                            uint32_t t0 = sk[e]; sk[e] = sk[f]; sk[f] = t0;
+                            t0 = id[e]; id[e] = id[f]; id[f] = t0;
+                            t0 = rw[e]; rw[e] = rw[f]; rw[f] = t0;
+                            t0 = vv[e]; vv[e] = vv[f]; vv[f] = t0;
+                        }
+                    }
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const uint32_t j = ln * E + e;
+        if (j < sg.k_i) {
+            const size_t o = (size_t)sg.row * p.k + j;
+            if (Key<KT>::kBytes == 4)
+                static_cast<uint32_t *>(p.keys_out)[o] = rw[e];
+            else
+                static_cast<uint16_t *>(p.keys_out)[o] = (uint16_t)rw[e];
+            if (p.vals_in) p.vals_out[o] = vv[e];
+        }
+    }
+}
+
+// The staged results outbuf[0, k_i): registers for small k, else an LDS sort.
+template <int KT, bool LARGEST>
+__device__ __forceinline__ void write_staged(uint2 *outbuf, const Params &p, const Seg &sg) {
+    if (sg.k_i <= 64) {
+        out_regs<KT, LARGEST, 1>(outbuf, p, sg);
+    } else if (sg.k_i <= 128) {
+        out_regs<KT, LARGEST, 2>(outbuf, p, sg);
+    } else if (sg.k_i <= 256) {
+        out_regs<KT, LARGEST, 4>(outbuf, p, sg);
+    } else {
+        if (p.sorted) wave_bitonic<KT, LARGEST>(outbuf, sg.k_i);
+        for (uint32_t j = lane_id(); j < sg.k_i; j += kWave)
+            write_out<KT>(p, sg, j, outbuf[j].x, outbuf[j].y);
+    }
+}
+
+// k >= n: every key of the segment is selected (one wave).
+template <int KT, bool LARGEST>
+__device__ __forceinline__ void wave_select_all(uint2 *outbuf, const Params &p, const Seg &sg) {
+    const uint32_t ln = lane_id();
+    WaveRange<KT> L;
+    L.init(p.keys_in, sg.begin, 0u, sg.n);
+    if (p.sorted) {  // n <= k <= out_cap
+        L.for_each(ln, [&](uint32_t raw, uint32_t idx, bool act) {
+            if (act) outbuf[idx] = make_uint2(raw, idx);
+        });
+        wave_sync();
+        write_staged<KT, LARGEST>(outbuf, p, sg);
+    } else {
+        L.for_each(ln, [&](uint32_t raw, uint32_t idx, bool act) {
+            if (act) write_out<KT>(p, sg, idx, raw, idx);
+        });
+    }
+}
+
 // ---------------------------------------------------------------------------
-// Passes 1.. over the candidates, the tie selection and the output, given the
-// pass-0 result (bucket b0, keys before it E0, keys in it c0).
+// Passes 1.., the tie selection and the output, by one wave, given the
+// pass-0 result (bucket k0.b holds the k-th key, k0.before keys precede it,
+// k0.count keys are in it).  hist is scratch.
 // ---------------------------------------------------------------------------
 template <int KT, bool LARGEST>
-__device__ __forceinline__ void finish(Smem &sm, uint2 *outbuf, const Params &p, const Seg &sg,
-                       const Cands<KT> &cand, uint32_t b0, uint32_t E0, uint32_t c0) {
+__device__ __forceinline__ void wave_finish(uint32_t *hist, uint2 *outbuf, const Params &p,
+                                            const Seg &sg, const Cands<KT> &cand, Kth k0) {
     constexpr int KB = Key<KT>::kBits;
-    const uint32_t t = threadIdx.x;
-    const uint32_t wave = t >> 6;
+    const uint32_t ln = lane_id();
     const bool pl = p.prefer_larger != 0;
 
     int hi = KB - kDigit;
     uint32_t kmask = (uint32_t)(kBuckets - 1) << hi;
-    uint32_t kpref = (LARGEST ? (uint32_t)(kBuckets - 1) - b0 : b0) << hi;
-    uint32_t krem = sg.k_i - E0;
-    uint32_t front = E0;
-    bool done = (c0 == krem);
+    uint32_t kpref = (LARGEST ? (uint32_t)(kBuckets - 1) - k0.b : k0.b) << hi;
+    uint32_t krem = sg.k_i - k0.before;
+    uint32_t front = k0.before;
+    bool done = (k0.count == krem);
 
     // Key digits.
     while (!done && hi > 0) {
         const int w = hi < kDigit ? hi : kDigit;
         const int sh = hi - w;
         const uint32_t nb = 1u << w;
-        for (uint32_t i = t; i < nb; i += kThreads) sm.hist[i] = 0;
-        __syncthreads();
-        cand.visit([&](uint32_t raw, uint32_t idx, bool act) {
-            const uint32_t o = Key<KT>::ord(raw);
+        wave_clear(hist, nb);
+        wave_sync();
+        cand.visit([&](uint32_t r, uint32_t idx, bool act) {
+            const uint32_t o = Key<KT>::ord(r);
             if (act && (o & kmask) == kpref) {
                 const uint32_t d = (o >> sh) & (nb - 1);
-                atomicAdd(&sm.hist[LARGEST ? nb - 1 - d : d], 1u);
+                atomicAdd(&hist[LARGEST ? nb - 1 - d : d], 1u);
             }
         });
-        __syncthreads();
-        if (wave == 0) find_kth(sm.hist, nb, krem, sm.res);
-        __syncthreads();
-        const uint32_t b = sm.res[1], E = sm.res[2], cnt = sm.res[3];
-        krem -= E;
-        front += E;
-        kpref |= (LARGEST ? nb - 1 - b : b) << sh;
+        wave_sync();
+        const Kth f = wave_find(hist, nb, krem);
+        krem -= f.before;
+        front += f.before;
+        kpref |= (LARGEST ? nb - 1 - f.b : f.b) << sh;
         kmask |= (nb - 1) << sh;
-        done = (cnt == krem);
+        done = (f.count == krem);
         hi = sh;
+        wave_sync();
     }
 
-    // Index digits among the splitter-equal keys (deterministic modes).  The
-    // tie winners are the `ties` best of them by index; `krem` now counts
-    // within the narrowing index prefix and `front` is left alone.
+    // Deterministic modes: narrow the splitter-equal keys by source index.
+    // The `ties` winners are the best of them by index; `front` stays.
     const uint32_t ties = krem;
     bool by_index = false;
     uint32_t imask = 0, ipref = 0;
@@ -651,92 +934,81 @@ __device__ __forceinline__ void finish(Smem &sm, uint2 *outbuf, const Params &p,
             const int w = hi < kDigit ? hi : kDigit;
             const int sh = hi - w;
             const uint32_t nb = 1u << w;
-            for (uint32_t i = t; i < nb; i += kThreads) sm.hist[i] = 0;
-            __syncthreads();
-            cand.visit([&](uint32_t raw, uint32_t idx, bool act) {
-                if (act && (Key<KT>::ord(raw) & kmask) == kpref && (idx & imask) == ipref) {
+            wave_clear(hist, nb);
+            wave_sync();
+            cand.visit([&](uint32_t r, uint32_t idx, bool act) {
+                if (act && (Key<KT>::ord(r) & kmask) == kpref && (idx & imask) == ipref) {
                     const uint32_t d = (idx >> sh) & (nb - 1);
-                    atomicAdd(&sm.hist[pl ? nb - 1 - d : d], 1u);
+                    atomicAdd(&hist[pl ? nb - 1 - d : d], 1u);
                 }
             });
-            __syncthreads();
-            if (wave == 0) find_kth(sm.hist, nb, krem, sm.res);
-            __syncthreads();
-            const uint32_t b = sm.res[1], E = sm.res[2], cnt = sm.res[3];
-            krem -= E;
-            ipref |= (pl ? nb - 1 - b : b) << sh;
+            wave_sync();
+            const Kth f = wave_find(hist, nb, krem);
+            krem -= f.before;
+            ipref |= (pl ? nb - 1 - f.b : f.b) << sh;
             imask |= (nb - 1) << sh;
-            done = (cnt == krem);
+            done = (f.count == krem);
             hi = sh;
+            wave_sync();
         }
     }
 
-    // Final filter: everything better than the splitter, then the ties.
-    if (t == 0) {
-        sm.ctr[0] = 0;
-        sm.ctr[1] = 0;
-    }
-    __syncthreads();
-    cand.visit([&](uint32_t raw, uint32_t idx, bool act) {
-        const uint32_t km = Key<KT>::ord(raw) & kmask;
+    // Final filter: keys better than the splitter to [0, front), the chosen
+    // ties to [front, k_i).
+    uint32_t nf = 0, nt = 0;
+    cand.visit([&](uint32_t r, uint32_t idx, bool act) {
+        const uint32_t km = Key<KT>::ord(r) & kmask;
         const bool better = act && (LARGEST ? km > kpref : km < kpref);
         bool tie = act && km == kpref;
         if (by_index) {
             const uint32_t im = idx & imask;
             tie = tie && (pl ? im >= ipref : im <= ipref);
         }
-        const uint32_t pb = wave_reserve(&sm.ctr[0], better);
-        const uint32_t pt = wave_reserve(&sm.ctr[1], tie);
+        const uint64_t mb = __ballot(better);
+        const uint64_t mt = __ballot(tie);
+        const uint32_t pb = nf + lanes_below(mb);
+        const uint32_t pt = nt + lanes_below(mt);
+        nf += (uint32_t)__popcll(mb);
+        nt += (uint32_t)__popcll(mt);
         uint32_t pos = kNone;
         if (better && pb < front) pos = pb;
         if (tie && pt < ties) pos = front + pt;
         if (pos != kNone) {
             if (outbuf)
-                outbuf[pos] = make_uint2(raw, idx);
+                outbuf[pos] = make_uint2(r, idx);
             else
-                write_out<KT>(p, sg, pos, raw, idx);
+                write_out<KT>(p, sg, pos, r, idx);
         }
     });
-    __syncthreads();
     if (outbuf) {
-        if (p.sorted) bitonic_sort<KT, LARGEST>(outbuf, sg.k_i);
-        for (uint32_t j = t; j < sg.k_i; j += kThreads) write_out<KT>(p, sg, j, outbuf[j].x, outbuf[j].y);
-    }
-}
-
-// k >= n: every key of the segment is selected.
-template <int KT, bool LARGEST>
-__device__ __forceinline__ void select_all(uint2 *outbuf, const Params &p, const Seg &sg) {
-    Range<KT> L;
-    L.init(p.keys_in, sg.begin, 0u, sg.n);
-    if (p.sorted) {
-        // n <= k <= out_cap: stage, sort, write.
-        L.for_each(threadIdx.x, [&](uint32_t raw, uint32_t idx, bool act) {
-            if (act) outbuf[idx] = make_uint2(raw, idx);
-        });
-        __syncthreads();
-        bitonic_sort<KT, LARGEST>(outbuf, sg.n);
-        for (uint32_t j = threadIdx.x; j < sg.n; j += kThreads)
-            write_out<KT>(p, sg, j, outbuf[j].x, outbuf[j].y);
-    } else {
-        L.for_each(threadIdx.x, [&](uint32_t raw, uint32_t idx, bool act) {
-            if (act) write_out<KT>(p, sg, idx, raw, idx);
-        });
+        wave_sync();
+        write_staged<KT, LARGEST>(outbuf, p, sg);
     }
 }
 
 // ---------------------------------------------------------------------------
-// The kernel.  Grid: ceil(S / 8) * 8 * wg_per_seg workgroups.  Workgroup b
-// serves segment (b / 8 / P) * 8 + b % 8, slice (b / 8) % P, so that all the
-// workgroups of one segment share b % 8 (the XCD a workgroup is dispatched to)
-// and their atomics and slots stay within one L2.
+// The kernel.  Grid: ceil(S / 8) * 8 * P workgroups of four waves.
+// Workgroup b serves segment (b / 8 / P) * 8 + b % 8, slice (b / 8) % P, so all
+// workgroups of one segment share b % 8 -- the XCD they are dispatched to --
+// and their atomics and slots stay in one L2.
 // ---------------------------------------------------------------------------
+struct alignas(16) Shared {
+    uint32_t hist[kBuckets];
+    uint32_t wcount[kWaves];
+    uint32_t wbad[kWaves];
+    uint32_t flag;
+    uint32_t rg;
+};
+
 template <int KT, bool LARGEST>
 __global__ __launch_bounds__(kThreads) void topk_kernel(Params p) {
-    __shared__ Smem sm;
-    extern __shared__ uint2 dyn[];
-    uint2 *stash = dyn;
-    uint2 *outbuf = p.out_cap ? dyn + p.stash_cap : nullptr;
+    __shared__ Shared sh;
+    extern __shared__ uint4 dyn[];
+    uint2 *stash = reinterpret_cast<uint2 *>(dyn);  // kWaves regions of capw entries
+    uint2 *outbuf = p.out_cap ? stash + p.stash_cap : nullptr;
+    const uint32_t t = threadIdx.x;
+    const uint32_t w = t / kWave;
+    const uint32_t ln = lane_id();
 
     const uint32_t P = p.wg_per_seg;
     const uint32_t b = blockIdx.x;
@@ -758,116 +1030,171 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(Params p) {
     if (P > 1 && sg.n > p.k) {
         uint32_t sl = (uint32_t)(((uint64_t)sg.n + P - 1) / P);
         if (sl < p.min_slice) sl = p.min_slice;
-        sl = (sl + 63u) & ~63u;
+        sl = (sl + 255u) & ~255u;
         ps = (uint32_t)(((uint64_t)sg.n + sl - 1) / sl);
         slice = sl;
     }
     if (q >= ps) return;
 
-    if (sg.n <= p.k) {  // select-all
-        if (q == 0) select_all<KT, LARGEST>(outbuf, p, sg);
+    if (sg.n <= p.k) {  // select-all: one wave does it
+        if (w == 0) wave_select_all<KT, LARGEST>(outbuf, p, sg);
         return;
     }
 
+    // ---- pass 0: each wave streams a quarter of this workgroup's keys ----
     const uint32_t lo = q * slice;
     const uint32_t hi = (sg.n - lo) > slice ? lo + slice : sg.n;
-    const uint32_t R = pass0<KT, LARGEST>(sm, stash, p.stash_cap, p, sg, lo, hi, sg.k_i);
+    const uint32_t len = hi - lo;
+    uint32_t part = (len + kWaves - 1) / kWaves;
+    part = (part + 63u) & ~63u;
+    const uint32_t wlo = lo + (w * part < len ? w * part : len);
+    const uint32_t whi = lo + ((w + 1) * part < len ? (w + 1) * part : len);
+    const uint32_t capw = p.stash_cap / kWaves;
+    for (uint32_t i = t * 4; i < (uint32_t)kBuckets; i += 4 * kThreads)
+        *reinterpret_cast<uint4 *>(&sh.hist[i]) = make_uint4(0u, 0u, 0u, 0u);
+    if (t == 0) {
+        sh.flag = 0;
+        sh.rg = kBuckets - 1;
+    }
+    __syncthreads();
+    Share share;
+    share.rg = &sh.rg;
+    share.flag = &sh.flag;
+    share.gearly = ps > 1 ? p.ws_early + (size_t)s * kBuckets : nullptr;
+    share.wave = w;
+    const Pass0 r0 = wave_pass0<KT, LARGEST>(sh.hist, stash + w * capw, capw, p.keys_in,
+                                             sg.begin, wlo, whi, sg.k_i, share);
+    if (ln == 0) {
+        sh.wcount[w] = r0.count;
+        sh.wbad[w] = r0.bad ? 1u : 0u;
+    }
+    __syncthreads();
+    if (w != 0) return;  // wave 0 finishes the workgroup's work alone
+
+    // ---- wave 0: this workgroup's k-th bucket, then its candidates ----
+    const Kth kw = wave_find(sh.hist, kBuckets, sg.k_i);
+    const uint32_t R = kw.b;  // the last bucket when the range holds fewer keys
+    bool bad = false;
+    for (uint32_t v = 0; v < (uint32_t)kWaves; ++v) bad = bad || sh.wbad[v] != 0;
+    // Gather, in place, every stash entry with rank <= R (wave regions are
+    // visited in order, so writes never pass reads).
+    uint32_t ncand = 0;
+    if (!bad) {
+        const uint32_t thr = rank_thr<KT, LARGEST>(R);
+        for (uint32_t v = 0; v < (uint32_t)kWaves; ++v) {
+            const uint32_t cnt = sh.wcount[v];
+            const uint2 *src = stash + v * capw;
+            for (uint32_t base = 0; base < cnt; base += kWave) {
+                const uint32_t i = base + ln;
+                const bool act = i < cnt;
+                const uint2 e = act ? src[i] : make_uint2(0u, 0u);
+                const bool keep = act && within<LARGEST>(Key<KT>::ord(e.x), thr);
+                const uint64_t m = __ballot(keep);
+                wave_sync();
+                if (keep) stash[ncand + lanes_below(m)] = e;
+                ncand += (uint32_t)__popcll(m);
+                wave_sync();
+            }
+        }
+    }
 
     Cands<KT> cand;
-    cand.stash = stash;
+    cand.list = stash;
+    cand.count = ncand;
+    cand.lds = !bad;
     cand.keys_in = p.keys_in;
     cand.begin = sg.begin;
     cand.n = sg.n;
+    cand.nslices = 1;
+    cand.slice = sg.n;
+    cand.slot_info = nullptr;
+    cand.slot_cum = nullptr;
+    cand.slot_data = nullptr;
     cand.slot_cap = p.stash_cap;
+    cand.bstar = 0;
 
     if (ps == 1) {
-        cand.lds = sm.stash_bad == 0;
-        cand.count = sm.stash_count;
-        cand.nslots = 1;
-        cand.slice = sg.n;
-        cand.slot_info = nullptr;
-        cand.slot_data = nullptr;
-        finish<KT, LARGEST>(sm, outbuf, p, sg, cand, R, sm.res[2], sm.res[3]);
+        wave_finish<KT, LARGEST>(sh.hist, outbuf, p, sg, cand, kw);
         return;
     }
 
     // ---- several workgroups per segment: publish this slice ----
-    const uint32_t t = threadIdx.x;
     uint32_t *gh = p.ws_hist + (size_t)s * kBuckets;
-    for (uint32_t r = t; r <= R; r += kThreads) {
-        const uint32_t h = sm.hist[r];
-        if (h) atomicAdd(&gh[r], h);
+    uint32_t *info = p.ws_slot_info + (size_t)s * P * 4;
+    uint32_t *cum = p.ws_slot_cum + ((size_t)s * P + q) * kBuckets;
+    uint2 *slot = p.ws_slot_data + ((size_t)s * P + q) * p.stash_cap;
+    for (uint32_t i = ln; i <= R; i += kWave) {
+        const uint32_t h = sh.hist[i];
+        if (h) atomicAdd(&gh[i], h);
     }
-    uint32_t *info = p.ws_slot_info + ((size_t)s * P) * 2;
-    uint2 *slots = p.ws_slot_data + ((size_t)s * P) * p.stash_cap;
-    const bool bad = sm.stash_bad != 0;
-    if (t == 0) sm.ctr[0] = 0;
-    __syncthreads();
     if (!bad) {
-        const uint32_t thr = rank_thr<KT, LARGEST>(R);
-        const uint32_t cnt = sm.stash_count;
-        uint2 *mine = slots + (size_t)q * p.stash_cap;
-        for (uint32_t base = 0; base < cnt; base += kThreads) {
-            const uint32_t i = base + t;
-            const bool act = i < cnt;
-            const uint2 e = act ? stash[i] : make_uint2(0u, 0u);
-            const bool keep = act && within<LARGEST>(Key<KT>::ord(e.x), thr);
-            const uint32_t pos = wave_reserve(&sm.ctr[0], keep);
-            if (keep) mine[pos] = e;
+        // Counting sort of the candidates by rank into the slot: hist becomes
+        // the exclusive prefix (a cursor per rank); after the scatter each
+        // cursor holds the number of entries with rank <= r.
+        uint32_t carry = 0;
+        for (uint32_t base = 0; base <= R; base += kWave) {
+            const uint32_t i = base + ln;
+            const uint32_t h = i <= R ? sh.hist[i] : 0u;
+            const uint32_t incl = wave_incl_sum(h);
+            if (i <= R) sh.hist[i] = carry + incl - h;
+            carry += wave_bcast(incl, kWave - 1);
         }
+        wave_sync();
+        for (uint32_t base = 0; base < ncand; base += kWave) {
+            const uint32_t i = base + ln;
+            if (i < ncand) {
+                const uint2 e = stash[i];
+                const uint32_t pos = atomicAdd(&sh.hist[rank0<KT, LARGEST>(Key<KT>::ord(e.x))], 1u);
+                if (pos < p.stash_cap) slot[pos] = e;
+            }
+        }
+        wave_sync();
+        for (uint32_t i = ln; i <= R; i += kWave) cum[i] = sh.hist[i];
     }
-    __syncthreads();
-    if (t == 0) {
-        info[2 * q] = bad ? 0u : sm.ctr[0];
-        info[2 * q + 1] = bad ? 1u : 0u;
+    if (ln == 0) {
+        info[4 * q + 0] = bad ? 0u : ncand;
+        info[4 * q + 1] = bad ? 1u : 0u;
+        info[4 * q + 2] = R;
     }
     __threadfence();
-    __syncthreads();
-    if (t == 0) sm.flag = (atomicAdd(&p.ws_ticket[s], 1u) == ps - 1) ? 1u : 0u;
-    __syncthreads();
-    if (!sm.flag) return;
+    uint32_t last = 0;
+    if (ln == 0) last = (atomicAdd(&p.ws_ticket[s], 1u) == ps - 1) ? 1u : 0u;
+    last = wave_bcast(last, 0);
+    if (!last) return;
     __threadfence();
 
-    // ---- last arriver: merged histogram, then the segment's candidates ----
-    for (uint32_t r = t; r < (uint32_t)kBuckets; r += kThreads)
-        sm.hist[r] = __hip_atomic_load(&gh[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    if ((t >> 6) == 0) find_kth(sm.hist, kBuckets, sg.k_i, sm.res);
-    __syncthreads();
-    const uint32_t bstar = sm.res[1], E0 = sm.res[2], c0 = sm.res[3];
-
+    // ---- last arriver: the segment's k-th bucket, then only the slot
+    // prefixes that can still win ----
+    for (uint32_t i = ln; i < (uint32_t)kBuckets; i += kWave)
+        sh.hist[i] = __hip_atomic_load(&gh[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    wave_sync();
+    const Kth ks = wave_find(sh.hist, kBuckets, sg.k_i);
     cand.lds = false;
-    cand.nslots = ps;
+    cand.nslices = ps;
     cand.slice = slice;
     cand.slot_info = info;
-    cand.slot_data = slots;
-    // Gather the candidates into the LDS stash when they fit.
-    if (t == 0) {
-        sm.stash_count = 0;
-        sm.stash_bad = 0;
-    }
-    __syncthreads();
+    cand.slot_cum = p.ws_slot_cum + (size_t)s * P * kBuckets;
+    cand.slot_data = p.ws_slot_data + (size_t)s * P * p.stash_cap;
+    cand.bstar = ks.b;
+    // Pull the candidates into LDS when they fit.
     {
-        const uint32_t thr = rank_thr<KT, LARGEST>(bstar);
+        const uint32_t thr = rank_thr<KT, LARGEST>(ks.b);
         const uint32_t cap = p.stash_cap;
-        cand.visit([&](uint32_t raw, uint32_t idx, bool act) {
-            const bool keep = act && within<LARGEST>(Key<KT>::ord(raw), thr);
-            const uint32_t pos = wave_reserve(&sm.stash_count, keep);
-            if (keep) {
-                if (pos < cap)
-                    stash[pos] = make_uint2(raw, idx);
-                else
-                    sm.stash_bad = 1;
-            }
+        uint32_t got = 0;
+        cand.visit([&](uint32_t r, uint32_t idx, bool act) {
+            const bool keep = act && within<LARGEST>(Key<KT>::ord(r), thr);
+            const uint64_t m = __ballot(keep);
+            const uint32_t pos = got + lanes_below(m);
+            if (keep && pos < cap) stash[pos] = make_uint2(r, idx);
+            got += (uint32_t)__popcll(m);
         });
+        wave_sync();
+        if (got <= cap) {
+            cand.lds = true;
+            cand.count = got;
+        }
     }
-    __syncthreads();
-    if (sm.stash_bad == 0) {
-        cand.lds = true;
-        cand.count = sm.stash_count;
-    }
-    __syncthreads();
-    finish<KT, LARGEST>(sm, outbuf, p, sg, cand, bstar, E0, c0);
+    wave_finish<KT, LARGEST>(sh.hist, outbuf, p, sg, cand, ks);
 }
 
 __global__ void zero_kernel(uint32_t *p, size_t n) {
@@ -882,11 +1209,9 @@ __global__ void zero_kernel(uint32_t *p, size_t n) {
 constexpr uint32_t kTargetWorkgroups = 2048;  // enough to fill 256 CUs several times
 constexpr uint32_t kMaxWgPerSeg = 256;
 constexpr uint32_t kMinSlice = 16384;
-constexpr size_t kMaxLds = 64 * 1024;
+constexpr size_t kMaxDynLds = 120 * 1024;
 
-int key_bytes(int type) {
-    return (type == SEGTOPK_KEY_BF16 || type == SEGTOPK_KEY_F16) ? 2 : 4;
-}
+int key_bytes(int type) { return (type == SEGTOPK_KEY_BF16 || type == SEGTOPK_KEY_F16) ? 2 : 4; }
 
 uint32_t next_pow2(uint32_t x) {
     uint32_t p = 1;
@@ -909,12 +1234,23 @@ void prepare_pool(int dev) {
     g_pool_ready[dev] = true;
 }
 
+// Dynamic LDS above 64 KiB has to be allowed per kernel.
+template <typename K> hipError_t allow_lds(K kernel, size_t lds) {
+    if (lds <= 64 * 1024) return hipSuccess;
+    return hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxDynLds);
+}
+
 template <int KT>
 hipError_t launch(const Params &p, bool largest, uint32_t grid, size_t lds, hipStream_t st) {
-    if (largest)
+    hipError_t e;
+    if (largest) {
+        if ((e = allow_lds(topk_kernel<KT, true>, lds)) != hipSuccess) return e;
         hipLaunchKernelGGL((topk_kernel<KT, true>), dim3(grid), dim3(kThreads), lds, st, p);
-    else
+    } else {
+        if ((e = allow_lds(topk_kernel<KT, false>, lds)) != hipSuccess) return e;
         hipLaunchKernelGGL((topk_kernel<KT, false>), dim3(grid), dim3(kThreads), lds, st, p);
+    }
     return hipGetLastError();
 }
 
@@ -969,16 +1305,17 @@ extern "C" int batched_topk(const segtopk_keys *keys, const segtopk_values *valu
     p.sorted = sorted;
 
     const uint32_t k32 = (uint32_t)k;
-    const size_t fixed = sizeof(Smem);
-    // Sorted output is staged and sorted in LDS; unsorted output is staged only
-    // for small k (coalesced row writes) and otherwise written in place.
+    // Output staging: sorted output is staged and sorted in LDS; unsorted
+    // output only for small k (coalesced row writes), else written in place.
     uint32_t out_cap = next_pow2(k32 < 2 ? 2 : k32);
     if (!sorted && out_cap > 256) out_cap = 0;
-    uint32_t stash_cap = next_pow2(4 * k32);
+    // Stash: room for about eight times k candidates in four wave regions, so
+    // a wave's first chunk fits even before the bound has settled.
+    uint32_t stash_cap = next_pow2(8 * k32);
     if (stash_cap < 1024) stash_cap = 1024;
-    if (stash_cap > 4096) stash_cap = 4096;
-    while (stash_cap > 256 && fixed + 8 * (size_t)(stash_cap + out_cap) > kMaxLds) stash_cap >>= 1;
-    if (fixed + 8 * (size_t)(stash_cap + out_cap) > kMaxLds) return SEGTOPK_NOT_SUPPORTED;
+    if (stash_cap > 8192) stash_cap = 8192;
+    while (stash_cap > 1024 && 8 * (size_t)(stash_cap + out_cap) > kMaxDynLds) stash_cap >>= 1;
+    if (8 * (size_t)(stash_cap + out_cap) > kMaxDynLds) return SEGTOPK_NOT_SUPPORTED;
     p.stash_cap = stash_cap;
     p.out_cap = out_cap;
     const size_t lds = 8 * (size_t)(stash_cap + out_cap);
@@ -1006,31 +1343,35 @@ extern "C" int batched_topk(const segtopk_keys *keys, const segtopk_values *valu
         prepare_pool(dev);
         const size_t S = (size_t)num_segments;
         const size_t n_hist = S * kBuckets, n_ticket = S;
-        const size_t zero_words = n_hist + n_ticket;
-        const size_t info_words = S * P * 2;
-        size_t bytes = (zero_words + info_words) * 4;
+        const size_t zero_words = 2 * n_hist + n_ticket;
+        const size_t info_words = S * P * 4;
+        const size_t cum_words = S * P * kBuckets;
+        size_t bytes = (zero_words + info_words + cum_words) * 4;
         bytes = (bytes + 255) & ~(size_t)255;
         const size_t data_off = bytes;
         bytes += S * P * (size_t)stash_cap * sizeof(uint2);
         if (hipMallocAsync(&ws, bytes, stream) != hipSuccess) return SEGTOPK_HIP_ERROR;
-        uint32_t *w = static_cast<uint32_t *>(ws);
-        p.ws_hist = w;
-        p.ws_ticket = w + n_hist;
-        p.ws_slot_info = w + zero_words;
+        uint32_t *wsw = static_cast<uint32_t *>(ws);
+        p.ws_hist = wsw;
+        p.ws_early = wsw + n_hist;
+        p.ws_ticket = wsw + 2 * n_hist;
+        p.ws_slot_info = wsw + zero_words;
+        p.ws_slot_cum = wsw + zero_words + info_words;
         p.ws_slot_data = reinterpret_cast<uint2 *>(static_cast<char *>(ws) + data_off);
         size_t zb = (zero_words + 255) / 256;
         if (zb > 1024) zb = 1024;
-        hipLaunchKernelGGL(zero_kernel, dim3((unsigned)zb), dim3(256), 0, stream, w, zero_words);
+        hipLaunchKernelGGL(zero_kernel, dim3((unsigned)zb), dim3(256), 0, stream, wsw, zero_words);
         err = hipGetLastError();
     }
     if (err == hipSuccess) {
         const bool largest = direction == SEGTOPK_MAX;
+        const uint32_t g = (uint32_t)grid;
         switch (type) {
-        case SEGTOPK_KEY_F32: err = launch<SEGTOPK_KEY_F32>(p, largest, (uint32_t)grid, lds, stream); break;
-        case SEGTOPK_KEY_BF16: err = launch<SEGTOPK_KEY_BF16>(p, largest, (uint32_t)grid, lds, stream); break;
-        case SEGTOPK_KEY_U32: err = launch<SEGTOPK_KEY_U32>(p, largest, (uint32_t)grid, lds, stream); break;
-        case SEGTOPK_KEY_I32: err = launch<SEGTOPK_KEY_I32>(p, largest, (uint32_t)grid, lds, stream); break;
-        default: err = launch<SEGTOPK_KEY_F16>(p, largest, (uint32_t)grid, lds, stream); break;
+        case SEGTOPK_KEY_F32: err = launch<SEGTOPK_KEY_F32>(p, largest, g, lds, stream); break;
+        case SEGTOPK_KEY_BF16: err = launch<SEGTOPK_KEY_BF16>(p, largest, g, lds, stream); break;
+        case SEGTOPK_KEY_U32: err = launch<SEGTOPK_KEY_U32>(p, largest, g, lds, stream); break;
+        case SEGTOPK_KEY_I32: err = launch<SEGTOPK_KEY_I32>(p, largest, g, lds, stream); break;
+        default: err = launch<SEGTOPK_KEY_F16>(p, largest, g, lds, stream); break;
         }
     }
     if (ws) {
@@ -1049,4 +1390,4 @@ extern "C" const char *segtopk_status_string(int status) {
     }
 }
 
-extern "C" int segtopk_version(void) { return 100; }
+extern "C" int segtopk_version(void) { return 200; }

@@ -118,9 +118,13 @@ def _row_sizes(offsets_np, k):
     return n, np.minimum(n, k)
 
 
-def compare(gk, gv, ok, ov, offsets_np, k, key_type, determinism, ordering, keys_bits):
+def compare(gk, gv, ok, ov, offsets_np, k, key_type, determinism, ordering, keys_bits,
+            values_are="index"):
     """Asserts that the GPU rows (gk, gv) agree with the oracle rows (ok, ov);
-    offsets_np / keys_bits describe exactly these rows."""
+    offsets_np / keys_bits describe exactly these rows.  ``values_are`` says
+    what the payload holds, for the not_guaranteed validity check: the source
+    index inside the segment ("index") or the key's position in the whole key
+    array ("position"; needed when segments overlap)."""
     n_all, ki = _row_sizes(offsets_np, k)
     rows = np.arange(gk.shape[0])
     col = np.arange(k)[None, :]
@@ -157,9 +161,14 @@ def compare(gk, gv, ok, ov, offsets_np, k, key_type, determinism, ordering, keys
     assert np.array_equal(np.sort(gnum, axis=1), np.sort(onum, axis=1)), "key multiset mismatch"
     if gv is not None:
         starts = offsets_np[:-1]
-        inb = (gv.astype(np.int64) < n_all[:, None]) | ~valid
+        if values_are == "index":
+            inb = (gv.astype(np.int64) < n_all[:, None]) | ~valid
+            src = np.where(valid, starts[:, None] + gv.astype(np.int64), 0)
+        else:
+            g = gv.astype(np.int64)
+            inb = ((g >= starts[:, None]) & (g < starts[:, None] + n_all[:, None])) | ~valid
+            src = np.where(valid, g, 0)
         assert inb.all(), "value (index) out of the segment"
-        src = np.where(valid, starts[:, None] + gv.astype(np.int64), 0)
         back = keys_bits[src] if keys_bits.size else np.zeros_like(gk)
         assert np.all((back == gk) | ~valid), "returned key is not the key at the returned index"
         sv = np.sort(np.where(valid, gv.astype(np.int64), -1 - col), axis=1)
@@ -167,7 +176,8 @@ def compare(gk, gv, ok, ov, offsets_np, k, key_type, determinism, ordering, keys
 
 
 def check(keys, values, offsets, k, key_type, largest=True, determinism="gpu_to_gpu",
-          tie_break="prefer_smaller_index", ordering="stable_sorted", rows=None):
+          tie_break="prefer_smaller_index", ordering="stable_sorted", rows=None,
+          values_are="index"):
     """GPU call on device tensors, oracle on host copies, row comparison.
     With ``rows`` only those rows are checked (the GPU still runs all)."""
     gk, gv = run_gpu(keys, values, offsets, k, key_type, largest, determinism, tie_break,
@@ -179,5 +189,5 @@ def check(keys, values, offsets, k, key_type, largest=True, determinism="gpu_to_
     if rows is not None:
         gk = gk[np.asarray(rows)]
         gv = gv[np.asarray(rows)] if gv is not None else None
-    compare(gk, gv, ok, ov, sub_off, k, key_type, determinism, ordering, kb)
+    compare(gk, gv, ok, ov, sub_off, k, key_type, determinism, ordering, kb, values_are)
     return gk, gv

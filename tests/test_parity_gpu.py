@@ -5,6 +5,7 @@ on host copies of the same input and compares rows as described in
 tests/parity.py: bitwise in the deterministic modes, key multiset plus validity
 in not_guaranteed, and untouched slots past min(k, n_i) everywhere.
 """
+import os
 import sys
 
 import numpy as np
@@ -77,18 +78,17 @@ def test_worked_example(key_type):
     keys = dev_keys([10, 8, 8, 8, 6, 5], key_type)
     off = torch.tensor([0, 6], dtype=torch.int64, device=DEV)
     vals = index_values(off)
-    for det, tb in MODES:
-        for ordering in ORDERINGS:
-            gk, gv = check(keys, vals, off, 3, key_type, True, det, tb, ordering)
-            got = sorted(int(v) for v in gv[0])
-            if tb == "prefer_larger_index":
-                assert got == [0, 2, 3]
-            elif det != "not_guaranteed":
-                assert got == [0, 1, 2]
-            else:
-                assert 0 in got and len(set(got)) == 3
-            if ordering == "stable_sorted" and det == "gpu_to_gpu" and tb != "unspecified":
-                assert list(gv[0]) == ([0, 2, 3] if tb == "prefer_larger_index" else [0, 1, 2])
+    for det, tb, ordering in [(d, t, o) for d, t in MODES for o in ORDERINGS]:
+        gk, gv = check(keys, vals, off, 3, key_type, True, det, tb, ordering)
+        got = sorted(int(v) for v in gv[0])
+        if tb == "prefer_larger_index":
+            assert got == [0, 2, 3]
+        elif det != "not_guaranteed":
+            assert got == [0, 1, 2]
+        else:
+            assert 0 in got and len(set(got)) == 3
+        if ordering == "stable_sorted" and det == "gpu_to_gpu" and tb != "unspecified":
+            assert list(gv[0]) == ([0, 2, 3] if tb == "prefer_larger_index" else [0, 1, 2])
 
 
 # ---------------------------------------------------------------------------
@@ -176,14 +176,16 @@ def test_edge_sizes_all_modes(key_type):
         off.append(off[-1] + s_)
     off_t = torch.tensor(off, dtype=torch.int64, device=DEV)
     total = max(off) + 7
+    # The negative-size segment makes later segments overlap earlier ones, so
+    # the payload is each key's global position (unique per key).
+    vals = torch.arange(total, dtype=torch.int32, device=DEV)
     for levels in (None, 6):
         keys = random_keys(total, key_type, g, levels)
-        vals = index_values(off_t)
-        vals = torch.cat([vals, torch.zeros(total - vals.numel(), dtype=torch.int32, device=DEV)])
         for largest in (True, False):
             for det, tb in MODES:
                 for ordering in ORDERINGS:
-                    check(keys, vals, off_t, k, key_type, largest, det, tb, ordering)
+                    check(keys, vals, off_t, k, key_type, largest, det, tb, ordering,
+                          values_are="position")
 
 
 @pytest.mark.parametrize("key_type", ["f32", "bf16"])
@@ -226,6 +228,22 @@ def test_heavy_ties(key_type):
             for det, tb in MODES:
                 for ordering in (["unsorted", "stable_sorted"] if k <= 4096 else ["unsorted"]):
                     check(keys, vals, off, k, key_type, largest, det, tb, ordering)
+
+
+def test_heavy_ties_long_segments():
+    """Few long segments (several workgroups each) whose slices overflow the
+    on-chip stash: the last workgroup re-reads those slices."""
+    n = 200000
+    rng = np.random.default_rng(4)
+    segs = [np.full(n, 2.0), rng.integers(0, 3, n) * 1.0,
+            np.where(rng.random(n) < 0.5, 0.0, -0.0)]
+    x = torch.tensor(np.concatenate(segs)).float().to(DEV)
+    off = torch.tensor(np.cumsum([0] + [len(v) for v in segs]), dtype=torch.int64, device=DEV)
+    vals = index_values(off)
+    for k in (100, 3000):
+        for largest in (True, False):
+            for det, tb in MODES:
+                check(x, vals, off, k, "f32", largest, det, tb, "unsorted")
 
 
 def test_negative_zero_comes_back_bitwise():
