@@ -130,6 +130,72 @@ def copy_probe(mib=256, reps=5):
     log(f"copy probe: {reps} copies of {mib} MiB")
 
 
+KERNEL_SRC = os.path.join(ROOT, "segmented_top_selection_amd", "csrc", "segtopk.hip")
+
+
+def kernel_hash():
+    import hashlib
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(name):
+    """HBM bytes per launch from the last rocprofv3 FETCH_SIZE / WRITE_SIZE
+    runs (profiles/traffic_<workload>.json), or None when the kernel source
+    has changed since they were taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
+    try:
+        with open(path) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256") != kernel_hash():
+        return None
+    return t.get("traffic_bytes_per_launch")
+
+
+def traffic_from(fetch_csv, write_csv, name):
+    """Turns two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, then
+    WRITE_SIZE; KiB per dispatch) of `--copy-probe` runs into HBM bytes per
+    topk_kernel launch, each counter scaled by what it reads for the 256 MiB
+    plain copy, and writes profiles/traffic_<workload>.json."""
+    import csv
+
+    def per_kernel(path, counter):
+        topk, copies = [], []
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if row["Counter_Name"] != counter:
+                    continue
+                v = float(row["Counter_Value"])
+                if "topk_kernel" in row["Kernel_Name"]:
+                    topk.append(v)
+                elif "copyBuffer" in row["Kernel_Name"]:
+                    copies.append(v)
+        if not topk or not copies:
+            raise SystemExit(f"{path}: no topk_kernel or copy dispatches with {counter}")
+        return sum(topk) / len(topk), max(copies), len(topk)
+
+    copy_bytes = 256 << 20
+    f_kib, f_copy, n_f = per_kernel(fetch_csv, "FETCH_SIZE")
+    w_kib, w_copy, n_w = per_kernel(write_csv, "WRITE_SIZE")
+    f_scale = copy_bytes / (f_copy * 1024)
+    w_scale = copy_bytes / (w_copy * 1024)
+    out = {
+        "workload": name,
+        "kernel_source_sha256": kernel_hash(),
+        "dispatches": [n_f, n_w],
+        "fetch_kib_per_launch": f_kib, "write_kib_per_launch": w_kib,
+        "copy_probe_fetch_kib": f_copy, "copy_probe_write_kib": w_copy,
+        "fetch_scale": f_scale, "write_scale": w_scale,
+        "traffic_bytes_per_launch": f_kib * 1024 * f_scale + w_kib * 1024 * w_scale,
+    }
+    path = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
+
+
 def cpu_baseline(name, budget_s=2.0):
     """The oracle, as it stands, on a bounded sample of the workload's segments
     (whole segments, taken from the start), on all host cores.  The sample
@@ -189,7 +255,13 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a 256 MiB device copy (counter calibration)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic_<workload>.json from two rocprofv3 --pmc "
+                         "runs of this script with --copy-probe, then exit")
     a = ap.parse_args()
+    if a.traffic_from:
+        traffic_from(a.traffic_from[0], a.traffic_from[1], a.workload)
+        return
     if a.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {a.gpus}); segments are "
               f"independent, so N GPUs would each run this call on their own shard.",
@@ -236,7 +308,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": head["bytes_alg"] / (kernel_ms / 1e3) / 1e9,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": head["bytes_alg"] / (kernel_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
-                     "traffic": None},
+                     "traffic": measured_traffic(a.workload)},
         "cpu_baseline": cpu,
         "workloads": {n: {kk: (round(v, 6) if isinstance(v, float) else v)
                           for kk, v in r.items()} for n, r in others.items()},

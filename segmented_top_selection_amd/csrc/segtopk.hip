@@ -370,6 +370,7 @@ template <int KT, int NT, int U> struct Range {
     static constexpr int kVec = 16 / kBytes;  // keys per 16-byte load
     static constexpr int kU = U;
     static constexpr int kKpt = kU * kVec;    // keys per thread per chunk
+    static constexpr int kDw = kU * 4;        // dwords per thread per chunk
     static constexpr uint32_t kChunkVecs = NT * kU;
 
     const unsigned char *ebase;  // element 0 of the segment
@@ -396,9 +397,10 @@ template <int KT, int NT, int U> struct Range {
         if (kBytes == 4) return reinterpret_cast<const uint32_t *>(ebase)[idx];
         return reinterpret_cast<const uint16_t *>(ebase)[idx];
     }
-    // Thread t's part of chunk c: raw[u * kVec + e] holds element vidx[u] + e
-    // (as a word of its key type); vidx[u] == kNone marks a load past the end.
-    __device__ __forceinline__ void load_chunk(uint32_t c, uint32_t t, uint32_t (&raw)[kKpt],
+    // Thread t's part of chunk c: the loaded dwords; key j = u * kVec + e is
+    // element vidx[u] + e (word_at extracts it as a word of its key type);
+    // vidx[u] == kNone marks a load past the end.
+    __device__ __forceinline__ void load_chunk(uint32_t c, uint32_t t, uint32_t (&raw)[kDw],
                                                uint32_t (&vidx)[kU]) const {
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
@@ -409,21 +411,16 @@ template <int KT, int NT, int U> struct Range {
                 v = vbase[vj];
                 vidx[u] = lo + head + vj * kVec;
             }
-            if (kBytes == 4) {
-                raw[u * 4 + 0] = v.x;
-                raw[u * 4 + 1] = v.y;
-                raw[u * 4 + 2] = v.z;
-                raw[u * 4 + 3] = v.w;
-            } else {
-                // Two 16-bit keys per dword, as words of their type.
-                const uint32_t d[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-                for (int h = 0; h < 4; ++h) {
-                    raw[u * 8 + 2 * h] = Key<KT>::word(d[h] & 0xFFFFu);
-                    raw[u * 8 + 2 * h + 1] = Key<KT>::word(d[h] >> 16);
-                }
-            }
+            raw[u * 4 + 0] = v.x;
+            raw[u * 4 + 1] = v.y;
+            raw[u * 4 + 2] = v.z;
+            raw[u * 4 + 3] = v.w;
         }
+    }
+    __device__ __forceinline__ static uint32_t word_at(const uint32_t (&raw)[kDw], int j) {
+        if (kBytes == 4) return raw[j];
+        const uint32_t d = raw[j >> 1];
+        return Key<KT>::word((j & 1) ? (d >> 16) : (d & 0xFFFFu));
     }
     // Calls f(raw, idx, active) for every element, chunk by chunk; every lane
     // of the thread group makes the same sequence of calls.
@@ -434,13 +431,13 @@ template <int KT, int NT, int U> struct Range {
             f(act ? load_scalar(idx) : 0u, idx, act);
         }
         for (uint32_t c = 0; c < nchunks; ++c) {
-            uint32_t raw[kKpt], vidx[kU];
+            uint32_t raw[kDw], vidx[kU];
             load_chunk(c, t, raw, vidx);
 #pragma unroll
             for (int u = 0; u < kU; ++u)
 #pragma unroll
                 for (int e = 0; e < kVec; ++e)
-                    f(Key<KT>::raw(raw[u * kVec + e]), vidx[u] + (uint32_t)e, vidx[u] != kNone);
+                    f(Key<KT>::raw(word_at(raw, u * kVec + e)), vidx[u] + (uint32_t)e, vidx[u] != kNone);
         }
     }
 };
@@ -455,17 +452,24 @@ template <int KT> using WaveRange = Range<KT, kWave, 4>;
 // workgroup adds an early snapshot of its histogram to a per-segment global
 // "early" histogram once, and its waves periodically turn that histogram
 // into a bound, published to the other waves through an LDS word.
+// Bound sharing between the workgroups of one segment (slice mode).  Wave 0
+// of each workgroup adds, every few chunks, what its histogram gained since
+// its last contribution (buckets within the bound only) to a per-segment
+// global histogram; it keeps what it has added so far in `glast`.  Every
+// count there is of a distinct key, so the histogram undercounts the
+// segment's and any bucket it yields is a valid bound.  The waves read a
+// bound from it in turn and publish it to the workgroup through an LDS word.
 struct Share {
     uint32_t *rg;        // LDS: best bound known to the workgroup
-    uint32_t *flag;      // LDS: the workgroup has contributed its snapshot
-    uint32_t *gearly;    // global: the segment's early histogram, or nullptr
+    uint32_t *gearly;    // global: the segment's shared histogram, or nullptr
+    uint32_t *glast;     // global: this workgroup's contributions so far
     uint32_t wave;       // this wave's index in the workgroup
 };
 
 struct Pass0 {
     uint32_t R;      // the wave's final bound (rank)
     uint32_t count;  // stash entries
-    bool bad;        // the stash lost candidates: re-read [lo, hi) instead
+    uint32_t defer;  // chunks [0, defer) were counted but not stashed
 };
 
 // Drops, in place, the stash entries whose pass-0 rank is beyond the bound.
@@ -487,12 +491,37 @@ __device__ __forceinline__ uint32_t wave_compact(uint2 *stash, uint32_t cnt, uin
     return out;
 }
 
+// Appends the lanes' entries with `ex` set to the stash; false when they do
+// not fit even after dropping the entries beyond bound R.
+template <int KT, bool LARGEST>
+__device__ __forceinline__ bool wave_push(uint2 *stash, uint32_t cap, uint32_t &count, uint32_t R,
+                                          bool ex, uint32_t x, uint32_t idx) {
+    const uint64_t m = __ballot(ex);
+    const uint32_t n = (uint32_t)__popcll(m);
+    if (n == 0) return true;
+    if (count + n > cap) {
+        wave_sync();
+        count = wave_compact<KT, LARGEST>(stash, count, rank_thr<KT, LARGEST>(R));
+        if (count + n > cap) return false;
+    }
+    if (ex) stash[count + lanes_below(m)] = make_uint2(x, idx);
+    count += n;
+    return true;
+}
+
+// Pass 0 of one wave over keys [lo, hi) of a segment.  Until the histogram
+// shared by the workgroup's waves yields a bound, every key is counted and
+// none is stashed.  From then on a key is counted and stashed only if its
+// bucket is within the running bound R, which only tightens.  Chunks that were
+// counted but not stashed (before the bound, or dropped when the stash
+// overflowed) are read again by wave_reread once the workgroup's bound is
+// final.
 template <int KT, bool LARGEST>
 __device__ __forceinline__ Pass0 wave_pass0(uint32_t *hist, uint2 *stash, uint32_t cap,
                                             const void *keys, int64_t begin, uint32_t lo,
                                             uint32_t hi, uint32_t target, const Share &sh) {
     using Rg = WaveRange<KT>;
-    constexpr int K = Rg::kKpt;
+    constexpr int K = Rg::kDw;
     const uint32_t ln = lane_id();
     Rg L;
     L.init(keys, begin, lo, hi);
@@ -500,11 +529,13 @@ __device__ __forceinline__ Pass0 wave_pass0(uint32_t *hist, uint2 *stash, uint32
     Pass0 r;
     r.R = kBuckets - 1;  // until `target` keys are counted any bucket may hold the k-th
     r.count = 0;
-    r.bad = false;
+    r.defer = 0;
     bool bounded = false;
+    bool contributed = false;
     FastBound fb;
     fb.mode = 0;
     fb.T = 0;
+
     uint32_t raw[K], vidx[Rg::kU];
     L.load_chunk(0, ln, raw, vidx);
     for (uint32_t c = 0; c < nch; ++c) {
@@ -520,25 +551,30 @@ __device__ __forceinline__ Pass0 wave_pass0(uint32_t *hist, uint2 *stash, uint32
         if (c + 1 < nch) L.load_chunk(c + 1, ln, raw, vidx);  // prefetch
 
         if (sh.gearly) {
-            // Adopt a tighter bound found by another wave of this workgroup.
-            const uint32_t rg = __hip_atomic_load(sh.rg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            // Adopt a tighter bound found by another wave of this workgroup
+            // (one lane reads it, so that the wave agrees on it).
+            const uint32_t rg = wave_bcast(
+                __hip_atomic_load(sh.rg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP), 0);
             if (rg < r.R) {
                 r.R = rg;
                 bounded = true;
                 fb = fast_bound<KT, LARGEST>(r.R);
             }
             if (bounded && c >= 1) {
-                // Once per workgroup: add the histogram so far to the segment's
-                // early histogram.  Every fourth chunk one wave reads it back.
-                uint32_t first = 0;
-                if (c == 1 && ln == 0) first = atomicCAS(sh.flag, 0u, 1u) == 0u ? 1u : 0u;
-                if (wave_bcast(first, 0)) {
+                if (sh.wave == 0 && ((c - 1) & 7u) == 0u) {
+                    // Add what the workgroup's histogram gained since the last
+                    // time.  Later bounds are never looser, so every bucket
+                    // read back from glast was written the first time.
+                    const bool first = !contributed;
+                    contributed = true;
                     for (uint32_t b = ln; b <= r.R; b += kWave) {
                         const uint32_t v = hist[b];
-                        if (v) atomicAdd(&sh.gearly[b], v);
+                        const uint32_t l = first ? 0u : sh.glast[b];
+                        if (v > l) atomicAdd(&sh.gearly[b], v - l);
+                        if (first || v != l) sh.glast[b] = v;
                     }
                 }
-                if ((c & 3u) == 3u && ((c >> 2) & 3u) == (sh.wave & 3u)) {
+                if (((c - 2u - 2u * sh.wave) & 7u) == 0u && c >= 2u) {
                     const Kth g = wave_find_global(sh.gearly, r.R + 1, target);
                     if (g.found && g.b < r.R) {
                         r.R = g.b;
@@ -550,15 +586,14 @@ __device__ __forceinline__ Pass0 wave_pass0(uint32_t *hist, uint2 *stash, uint32
         }
 
         if (!bounded) {
-            // No bound yet: count every key, find the bound, then stash the
-            // keys within it.
+            // No bound yet: count every key, then look for the bound.
             bool any = false;
 #pragma unroll
             for (int u = 0; u < Rg::kU; ++u)
 #pragma unroll
                 for (int e = 0; e < Rg::kVec; ++e) {
                     if (cv[u] != kNone) {
-                        atomicAdd(&hist[rank0<KT, LARGEST>(Key<KT>::ord(Key<KT>::raw(cur[u * Rg::kVec + e])))], 1u);
+                        atomicAdd(&hist[rank0<KT, LARGEST>(Key<KT>::ord(Key<KT>::raw(Rg::word_at(cur, u * Rg::kVec + e))))], 1u);
                         any = true;
                     }
                 }
@@ -566,15 +601,16 @@ __device__ __forceinline__ Pass0 wave_pass0(uint32_t *hist, uint2 *stash, uint32
                 atomicAdd(&hist[rank0<KT, LARGEST>(Key<KT>::ord(Key<KT>::raw(sw)))], 1u);
                 any = true;
             }
+            r.defer = c + 1;
             if (!__any(any)) continue;
             wave_sync();
             const Kth f = wave_find(hist, kBuckets, target);
-            if (f.found) {
-                r.R = f.b;
-                bounded = true;
-                fb = fast_bound<KT, LARGEST>(r.R);
-            }
-            if (r.bad) continue;
+            if (!f.found) continue;
+            r.R = f.b;
+            bounded = true;
+            fb = fast_bound<KT, LARGEST>(r.R);
+            // Stash this chunk's keys within the bound from the registers,
+            // if they fit; earlier chunks stay deferred.
             const uint32_t thr2 = rank_thr<KT, LARGEST>(r.R);
             uint32_t cnt = (sv && within<LARGEST>(Key<KT>::ord(Key<KT>::raw(sw)), thr2)) ? 1u : 0u;
 #pragma unroll
@@ -582,18 +618,11 @@ __device__ __forceinline__ Pass0 wave_pass0(uint32_t *hist, uint2 *stash, uint32
 #pragma unroll
                 for (int e = 0; e < Rg::kVec; ++e)
                     cnt += (cv[u] != kNone &&
-                            within<LARGEST>(Key<KT>::ord(Key<KT>::raw(cur[u * Rg::kVec + e])), thr2))
+                            within<LARGEST>(Key<KT>::ord(Key<KT>::raw(Rg::word_at(cur, u * Rg::kVec + e))), thr2))
                                ? 1u : 0u;
             const uint32_t incl = wave_incl_sum(cnt);
             const uint32_t total = wave_bcast(incl, kWave - 1);
-            if (r.count + total > cap) {
-                wave_sync();
-                r.count = wave_compact<KT, LARGEST>(stash, r.count, thr2);
-                if (r.count + total > cap) {
-                    r.bad = true;
-                    continue;
-                }
-            }
+            if (r.count + total > cap) continue;  // the stash is empty: defer the chunk
             uint32_t pos = r.count + incl - cnt;
             if (sv && within<LARGEST>(Key<KT>::ord(Key<KT>::raw(sw)), thr2))
                 stash[pos++] = make_uint2(Key<KT>::raw(sw), si);
@@ -601,11 +630,12 @@ __device__ __forceinline__ Pass0 wave_pass0(uint32_t *hist, uint2 *stash, uint32
             for (int u = 0; u < Rg::kU; ++u)
 #pragma unroll
                 for (int e = 0; e < Rg::kVec; ++e) {
-                    const uint32_t x = Key<KT>::raw(cur[u * Rg::kVec + e]);
+                    const uint32_t x = Key<KT>::raw(Rg::word_at(cur, u * Rg::kVec + e));
                     if (cv[u] != kNone && within<LARGEST>(Key<KT>::ord(x), thr2))
                         stash[pos++] = make_uint2(x, cv[u] + (uint32_t)e);
                 }
             r.count += total;
+            r.defer = c;
             continue;
         }
 
@@ -616,9 +646,10 @@ __device__ __forceinline__ Pass0 wave_pass0(uint32_t *hist, uint2 *stash, uint32
         for (int u = 0; u < Rg::kU; ++u)
 #pragma unroll
             for (int e = 0; e < Rg::kVec; ++e)
-                anyp = anyp || (cv[u] != kNone && fast_pass<KT, LARGEST>(cur[u * Rg::kVec + e], fb));
+                anyp = anyp || (cv[u] != kNone && fast_pass<KT, LARGEST>(Rg::word_at(cur, u * Rg::kVec + e), fb));
         if (!__any(anyp)) continue;
         uint32_t counted = 0;
+        bool ok = true;
         auto take = [&](uint32_t w, uint32_t idx, bool valid) {
             const bool pv = valid && fast_pass<KT, LARGEST>(w, fb);
             if (!__any(pv)) return;
@@ -626,27 +657,21 @@ __device__ __forceinline__ Pass0 wave_pass0(uint32_t *hist, uint2 *stash, uint32
             const uint32_t rk = rank0<KT, LARGEST>(Key<KT>::ord(x));
             const bool ex = pv && rk <= r.R;
             if (ex) atomicAdd(&hist[rk], 1u);
-            const uint64_t m = __ballot(ex);
-            const uint32_t n = (uint32_t)__popcll(m);
-            counted += n;
-            if (r.bad || n == 0) return;
-            if (r.count + n > cap) {
-                wave_sync();
-                r.count = wave_compact<KT, LARGEST>(stash, r.count, rank_thr<KT, LARGEST>(r.R));
-                if (r.count + n > cap) {
-                    r.bad = true;
-                    return;
-                }
-            }
-            if (ex) stash[r.count + lanes_below(m)] = make_uint2(x, idx);
-            r.count += n;
+            counted += (uint32_t)__popcll(__ballot(ex));
+            if (ok) ok = wave_push<KT, LARGEST>(stash, cap, r.count, r.R, ex, x, idx);
         };
         take(sw, si, sv);
 #pragma unroll
         for (int u = 0; u < Rg::kU; ++u)
 #pragma unroll
             for (int e = 0; e < Rg::kVec; ++e)
-                take(cur[u * Rg::kVec + e], cv[u] + (uint32_t)e, cv[u] != kNone);
+                take(Rg::word_at(cur, u * Rg::kVec + e), cv[u] + (uint32_t)e, cv[u] != kNone);
+        if (!ok) {
+            // The stash is full even within the bound: drop it and read this
+            // and every earlier chunk again later.
+            r.count = 0;
+            r.defer = c + 1;
+        }
         if (counted) {
             // Tighten the bound from everything counted so far.
             wave_sync();
@@ -658,6 +683,58 @@ __device__ __forceinline__ Pass0 wave_pass0(uint32_t *hist, uint2 *stash, uint32
         }
     }
     return r;
+}
+
+// Stashes, under the workgroup's final bound R, the keys of the chunks [0,
+// defer) of [lo, hi) (and the unaligned head and tail).  They were counted in
+// pass 0 already.  Returns false when they do not fit.
+template <int KT, bool LARGEST>
+__device__ __forceinline__ bool wave_reread(uint2 *stash, uint32_t cap, uint32_t &count,
+                                            const void *keys, int64_t begin, uint32_t lo,
+                                            uint32_t hi, uint32_t defer, uint32_t R) {
+    using Rg = WaveRange<KT>;
+    constexpr int K = Rg::kDw;
+    const uint32_t ln = lane_id();
+    Rg L;
+    L.init(keys, begin, lo, hi);
+    const uint32_t thr = rank_thr<KT, LARGEST>(R);
+    bool ok;
+    {
+        const bool sv = ln < L.nscalar;
+        const uint32_t si = sv ? L.scalar_idx(ln) : 0u;
+        const uint32_t x = sv ? Key<KT>::raw(Key<KT>::word(L.load_scalar(si))) : 0u;
+        ok = wave_push<KT, LARGEST>(stash, cap, count, R,
+                                    sv && within<LARGEST>(Key<KT>::ord(x), thr), x, si);
+    }
+    const uint32_t nre = defer < L.nchunks ? defer : L.nchunks;
+    uint32_t raw[K], vidx[Rg::kU];
+    if (nre > 0) L.load_chunk(0, ln, raw, vidx);
+    for (uint32_t c = 0; c < nre && ok; ++c) {
+        uint32_t cur[K], cv[Rg::kU];
+#pragma unroll
+        for (int j = 0; j < K; ++j) cur[j] = raw[j];
+#pragma unroll
+        for (int u = 0; u < Rg::kU; ++u) cv[u] = vidx[u];
+        if (c + 1 < nre) L.load_chunk(c + 1, ln, raw, vidx);
+        // A slot in which no lane is within the bound costs one ballot.
+        bool anyp = false;
+#pragma unroll
+        for (int j = 0; j < Rg::kKpt; ++j)
+            anyp = anyp || (cv[j / Rg::kVec] != kNone &&
+                            within<LARGEST>(Key<KT>::ord(Key<KT>::raw(Rg::word_at(cur, j))), thr));
+        if (!__any(anyp)) continue;
+#pragma unroll
+        for (int u = 0; u < Rg::kU; ++u)
+#pragma unroll
+            for (int e = 0; e < Rg::kVec; ++e) {
+                const uint32_t x = Key<KT>::raw(Rg::word_at(cur, u * Rg::kVec + e));
+                if (ok)
+                    ok = wave_push<KT, LARGEST>(stash, cap, count, R,
+                                                cv[u] != kNone && within<LARGEST>(Key<KT>::ord(x), thr),
+                                                x, cv[u] + (uint32_t)e);
+            }
+    }
+    return ok;
 }
 
 // ---------------------------------------------------------------------------
@@ -725,6 +802,27 @@ __device__ __forceinline__ void write_out(const Params &p, const Seg &sg, uint32
     else
         static_cast<uint16_t *>(p.keys_out)[o] = (uint16_t)raw;
     if (p.vals_in) p.vals_out[o] = idx < sg.n ? p.vals_in[sg.begin + idx] : kNone;
+}
+
+// write_out for B entries per lane: every value load is issued before the
+// first store, so that the loads' latencies overlap.
+template <int KT, int B>
+__device__ __forceinline__ void write_batch(const Params &p, const Seg &sg, const uint32_t (&pos)[B],
+                                            const uint2 (&e)[B]) {
+    uint32_t v[B];
+#pragma unroll
+    for (int u = 0; u < B; ++u)
+        v[u] = (p.vals_in && pos[u] < sg.k_i && e[u].y < sg.n) ? p.vals_in[sg.begin + e[u].y] : kNone;
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+        if (pos[u] >= sg.k_i) continue;
+        const size_t o = (size_t)sg.row * p.k + pos[u];
+        if (Key<KT>::kBytes == 4)
+            static_cast<uint32_t *>(p.keys_out)[o] = e[u].x;
+        else
+            static_cast<uint16_t *>(p.keys_out)[o] = (uint16_t)e[u].x;
+        if (p.vals_in) p.vals_out[o] = v[u];
+    }
 }
 
 // a before b in the output: better key first, then smaller index; entries
@@ -854,8 +952,17 @@ __device__ __forceinline__ void write_staged(uint2 *outbuf, const Params &p, con
         out_regs<KT, LARGEST, 4>(outbuf, p, sg);
     } else {
         if (p.sorted) wave_bitonic<KT, LARGEST>(outbuf, sg.k_i);
-        for (uint32_t j = lane_id(); j < sg.k_i; j += kWave)
-            write_out<KT>(p, sg, j, outbuf[j].x, outbuf[j].y);
+        constexpr int kB = 8;
+        for (uint32_t base = 0; base < sg.k_i; base += kB * kWave) {
+            uint32_t pos[kB];
+            uint2 e[kB];
+#pragma unroll
+            for (int u = 0; u < kB; ++u) {
+                pos[u] = base + (uint32_t)u * kWave + lane_id();
+                e[u] = pos[u] < sg.k_i ? outbuf[pos[u]] : make_uint2(0u, kNone);
+            }
+            write_batch<KT, kB>(p, sg, pos, e);
+        }
     }
 }
 
@@ -885,7 +992,8 @@ __device__ __forceinline__ void wave_select_all(uint2 *outbuf, const Params &p, 
 // ---------------------------------------------------------------------------
 template <int KT, bool LARGEST>
 __device__ __forceinline__ void wave_finish(uint32_t *hist, uint2 *outbuf, const Params &p,
-                                            const Seg &sg, const Cands<KT> &cand, Kth k0) {
+                                            const Seg &sg, const Cands<KT> &cand, Kth k0,
+                                            uint32_t placed = 0) {
     constexpr int KB = Key<KT>::kBits;
     const uint32_t ln = lane_id();
     const bool pl = p.prefer_larger != 0;
@@ -953,9 +1061,43 @@ __device__ __forceinline__ void wave_finish(uint32_t *hist, uint2 *outbuf, const
         }
     }
 
-    // Final filter: keys better than the splitter to [0, front), the chosen
-    // ties to [front, k_i).
-    uint32_t nf = 0, nt = 0;
+    // Final filter: keys better than the splitter to [placed, front) (the
+    // caller has written [0, placed) already), the chosen ties to
+    // [front, k_i).
+    uint32_t nf = placed, nt = 0;
+    if (!outbuf && cand.lds) {
+        // Written straight to the output: classify 8 entries per lane, then
+        // write them with their value loads in flight together.
+        constexpr int kB = 8;
+        for (uint32_t base = 0; base < cand.count; base += kB * kWave) {
+            uint32_t pos[kB];
+            uint2 e[kB];
+#pragma unroll
+            for (int u = 0; u < kB; ++u) {
+                const uint32_t i = base + (uint32_t)u * kWave + ln;
+                const bool act = i < cand.count;
+                e[u] = act ? cand.list[i] : make_uint2(0u, kNone);
+                const uint32_t km = Key<KT>::ord(e[u].x) & kmask;
+                const bool better = act && (LARGEST ? km > kpref : km < kpref);
+                bool tie = act && km == kpref;
+                if (by_index) {
+                    const uint32_t im = e[u].y & imask;
+                    tie = tie && (pl ? im >= ipref : im <= ipref);
+                }
+                const uint64_t mb = __ballot(better);
+                const uint64_t mt = __ballot(tie);
+                const uint32_t pb = nf + lanes_below(mb);
+                const uint32_t pt = nt + lanes_below(mt);
+                nf += (uint32_t)__popcll(mb);
+                nt += (uint32_t)__popcll(mt);
+                pos[u] = kNone;
+                if (better && pb < front) pos[u] = pb;
+                if (tie && pt < ties) pos[u] = front + pt;
+            }
+            write_batch<KT, kB>(p, sg, pos, e);
+        }
+        return;
+    }
     cand.visit([&](uint32_t r, uint32_t idx, bool act) {
         const uint32_t km = Key<KT>::ord(r) & kmask;
         const bool better = act && (LARGEST ? km > kpref : km < kpref);
@@ -996,7 +1138,7 @@ struct alignas(16) Shared {
     uint32_t hist[kBuckets];
     uint32_t wcount[kWaves];
     uint32_t wbad[kWaves];
-    uint32_t flag;
+    uint32_t wdefer[kWaves];
     uint32_t rg;
 };
 
@@ -1053,27 +1195,47 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(Params p) {
     for (uint32_t i = t * 4; i < (uint32_t)kBuckets; i += 4 * kThreads)
         *reinterpret_cast<uint4 *>(&sh.hist[i]) = make_uint4(0u, 0u, 0u, 0u);
     if (t == 0) {
-        sh.flag = 0;
         sh.rg = kBuckets - 1;
     }
     __syncthreads();
     Share share;
     share.rg = &sh.rg;
-    share.flag = &sh.flag;
     share.gearly = ps > 1 ? p.ws_early + (size_t)s * kBuckets : nullptr;
+    share.glast = ps > 1 ? p.ws_slot_cum + ((size_t)s * P + q) * kBuckets : nullptr;
     share.wave = w;
     const Pass0 r0 = wave_pass0<KT, LARGEST>(sh.hist, stash + w * capw, capw, p.keys_in,
                                              sg.begin, wlo, whi, sg.k_i, share);
     if (ln == 0) {
         sh.wcount[w] = r0.count;
-        sh.wbad[w] = r0.bad ? 1u : 0u;
+        sh.wbad[w] = 0;
+        sh.wdefer[w] = r0.defer;
     }
     __syncthreads();
+    bool anydefer = false;
+    for (uint32_t v = 0; v < (uint32_t)kWaves; ++v) anydefer = anydefer || sh.wdefer[v] != 0;
+    if (anydefer) {
+        // Every key of the workgroup is counted now: stash the deferred
+        // chunks under the workgroup's bound (computed alike by every wave).
+        uint32_t Rf = wave_find(sh.hist, kBuckets, sg.k_i).b;
+        if (ps > 1 && sh.rg < Rf) Rf = sh.rg;
+        if (r0.defer != 0) {
+            uint32_t cnt = r0.count;
+            const bool ok = wave_reread<KT, LARGEST>(stash + w * capw, capw, cnt, p.keys_in,
+                                                     sg.begin, wlo, whi, r0.defer, Rf);
+            if (ln == 0) {
+                sh.wcount[w] = cnt;
+                sh.wbad[w] = ok ? 0u : 1u;
+            }
+        }
+        __syncthreads();
+    }
     if (w != 0) return;  // wave 0 finishes the workgroup's work alone
 
     // ---- wave 0: this workgroup's k-th bucket, then its candidates ----
     const Kth kw = wave_find(sh.hist, kBuckets, sg.k_i);
-    const uint32_t R = kw.b;  // the last bucket when the range holds fewer keys
+    uint32_t R = kw.b;  // the last bucket when the range holds fewer keys
+    // A bound shared by the segment's workgroups is valid for this slice too.
+    if (ps > 1 && sh.rg < R) R = sh.rg;
     bool bad = false;
     for (uint32_t v = 0; v < (uint32_t)kWaves; ++v) bad = bad || sh.wbad[v] != 0;
     // Gather, in place, every stash entry with rank <= R (wave regions are
@@ -1156,12 +1318,14 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(Params p) {
         info[4 * q + 1] = bad ? 1u : 0u;
         info[4 * q + 2] = R;
     }
-    __threadfence();
+    // Release this slice's slot, histogram and info before taking a ticket;
+    // the last arriver acquires all of them.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     uint32_t last = 0;
     if (ln == 0) last = (atomicAdd(&p.ws_ticket[s], 1u) == ps - 1) ? 1u : 0u;
     last = wave_bcast(last, 0);
     if (!last) return;
-    __threadfence();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 
     // ---- last arriver: the segment's k-th bucket, then only the slot
     // prefixes that can still win ----
@@ -1176,8 +1340,77 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(Params p) {
     cand.slot_cum = p.ws_slot_cum + (size_t)s * P * kBuckets;
     cand.slot_data = p.ws_slot_data + (size_t)s * P * p.stash_cap;
     cand.bstar = ks.b;
-    // Pull the candidates into LDS when they fit.
-    {
+
+    // Per slot, the entries that can still win are the prefix up to bucket
+    // b*; lay the slots' prefixes end to end (exclusive prefix in LDS).
+    uint32_t *pre = sh.hist;  // the histogram is no longer needed
+    uint32_t total = 0;
+    bool any_bad = false;
+    for (uint32_t base = 0; base < ps; base += kWave) {
+        const uint32_t qi = base + ln;
+        uint32_t c = 0;
+        bool bd = false;
+        if (qi < ps) {
+            bd = info[4 * qi + 1] != 0;
+            if (!bd) {
+                c = cand.slot_cum[(size_t)qi * kBuckets + ks.b];
+                c = c < p.stash_cap ? c : p.stash_cap;
+            }
+        }
+        any_bad = any_bad || __any(bd);
+        const uint32_t incl = wave_incl_sum(c);
+        if (qi < ps) pre[qi] = total + incl - c;
+        total += wave_bcast(incl, kWave - 1);
+    }
+    if (ln == 0) pre[ps] = total;
+    wave_sync();
+    uint32_t placed = 0;
+    if (!any_bad && ks.count <= p.stash_cap) {
+        // Entries of better buckets are winners: write them now.  Entries of
+        // bucket b* go to the LDS list for the remaining passes.
+        constexpr int kB = 8;  // loads in flight per lane
+        uint32_t nb = 0, ntie = 0;
+        for (uint32_t base = 0; base < total; base += kB * kWave) {
+            uint2 e[kB];
+            uint32_t fpos[kB];
+#pragma unroll
+            for (int u = 0; u < kB; ++u) {
+                const uint32_t j = base + (uint32_t)u * kWave + ln;
+                e[u] = make_uint2(0u, kNone);
+                if (j < total) {
+                    // the slot holding entry j: the last q with pre[q] <= j
+                    uint32_t a = 0, z = ps;  // pre[a] <= j < pre[z]
+                    while (z - a > 1) {
+                        const uint32_t m = (a + z) >> 1;
+                        if (pre[m] <= j) a = m; else z = m;
+                    }
+                    e[u] = cand.slot_data[(size_t)a * p.stash_cap + (j - pre[a])];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < kB; ++u) {
+                const uint32_t rk = e[u].y != kNone ? rank0<KT, LARGEST>(Key<KT>::ord(e[u].x)) : kNone;
+                const bool better = rk < ks.b;
+                const bool tie = rk == ks.b;
+                const uint64_t mb = __ballot(better);
+                const uint64_t mt = __ballot(tie);
+                const uint32_t pb = nb + lanes_below(mb);
+                const uint32_t pt = ntie + lanes_below(mt);
+                nb += (uint32_t)__popcll(mb);
+                ntie += (uint32_t)__popcll(mt);
+                fpos[u] = (better && pb < ks.before) ? pb : kNone;
+                if (outbuf && fpos[u] != kNone) outbuf[pb] = e[u];
+                if (tie && pt < p.stash_cap) stash[pt] = e[u];
+            }
+            if (!outbuf) write_batch<KT, kB>(p, sg, fpos, e);
+        }
+        wave_sync();
+        cand.lds = true;
+        cand.count = ntie < p.stash_cap ? ntie : p.stash_cap;
+        placed = ks.before;
+    } else {
+        // Rare: a slice lost candidates or bucket b* does not fit in LDS.
+        // Pull what fits into LDS, else leave the candidates in place.
         const uint32_t thr = rank_thr<KT, LARGEST>(ks.b);
         const uint32_t cap = p.stash_cap;
         uint32_t got = 0;
@@ -1194,7 +1427,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(Params p) {
             cand.count = got;
         }
     }
-    wave_finish<KT, LARGEST>(sh.hist, outbuf, p, sg, cand, ks);
+    wave_finish<KT, LARGEST>(sh.hist, outbuf, p, sg, cand, ks, placed);
 }
 
 __global__ void zero_kernel(uint32_t *p, size_t n) {
@@ -1239,6 +1472,52 @@ template <typename K> hipError_t allow_lds(K kernel, size_t lds) {
     if (lds <= 64 * 1024) return hipSuccess;
     return hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxDynLds);
+}
+
+// Workgroups of topk_kernel<KT, largest> that fit on one CU with `lds` bytes
+// of dynamic LDS, times the device's CU count; cached per combination.
+struct OccKey {
+    int dev, kt, largest;
+    size_t lds;
+    uint32_t wgs;
+};
+std::mutex g_occ_mu;
+OccKey g_occ[64];
+int g_occ_n = 0;
+
+template <int KT> uint32_t resident_wgs(int dev, bool largest, size_t lds) {
+    {
+        std::lock_guard<std::mutex> lk(g_occ_mu);
+        for (int i = 0; i < g_occ_n; ++i)
+            if (g_occ[i].dev == dev && g_occ[i].kt == KT && g_occ[i].largest == (int)largest &&
+                g_occ[i].lds == lds)
+                return g_occ[i].wgs;
+    }
+    int per_cu = 0, cus = 0;
+    const void *fn = largest ? reinterpret_cast<const void *>(topk_kernel<KT, true>)
+                             : reinterpret_cast<const void *>(topk_kernel<KT, false>);
+    if (lds > 64 * 1024)
+        (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxDynLds);
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, lds) != hipSuccess ||
+        per_cu < 1)
+        per_cu = 1;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus < 1)
+        cus = 256;
+    const uint32_t wgs = (uint32_t)per_cu * (uint32_t)cus;
+    std::lock_guard<std::mutex> lk(g_occ_mu);
+    if (g_occ_n < 64) g_occ[g_occ_n++] = OccKey{dev, KT, (int)largest, lds, wgs};
+    return wgs;
+}
+
+uint32_t resident_wgs_for(int type, int dev, bool largest, size_t lds) {
+    switch (type) {
+    case SEGTOPK_KEY_F32: return resident_wgs<SEGTOPK_KEY_F32>(dev, largest, lds);
+    case SEGTOPK_KEY_BF16: return resident_wgs<SEGTOPK_KEY_BF16>(dev, largest, lds);
+    case SEGTOPK_KEY_U32: return resident_wgs<SEGTOPK_KEY_U32>(dev, largest, lds);
+    case SEGTOPK_KEY_I32: return resident_wgs<SEGTOPK_KEY_I32>(dev, largest, lds);
+    default: return resident_wgs<SEGTOPK_KEY_F16>(dev, largest, lds);
+    }
 }
 
 template <int KT>
@@ -1309,10 +1588,14 @@ extern "C" int batched_topk(const segtopk_keys *keys, const segtopk_values *valu
     // output only for small k (coalesced row writes), else written in place.
     uint32_t out_cap = next_pow2(k32 < 2 ? 2 : k32);
     if (!sorted && out_cap > 256) out_cap = 0;
-    // Stash: room for about eight times k candidates in four wave regions, so
-    // a wave's first chunk fits even before the bound has settled.
-    uint32_t stash_cap = next_pow2(8 * k32);
-    if (stash_cap < 1024) stash_cap = 1024;
+    // Several workgroups per segment when the segments alone cannot fill the
+    // device.  Stash: with one workgroup per segment, room for about eight
+    // times k candidates in four wave regions; with several, the
+    // segment-wide bound keeps each slice's candidates few, and the stash
+    // only has to hold bucket b* of the last arriver (about 2k at most).
+    const bool split = (uint64_t)num_segments < kTargetWorkgroups;
+    uint32_t stash_cap = next_pow2((split ? 2 : 8) * k32);
+    if (stash_cap < (split ? 2048u : 1024u)) stash_cap = split ? 2048u : 1024u;
     if (stash_cap > 8192) stash_cap = 8192;
     while (stash_cap > 1024 && 8 * (size_t)(stash_cap + out_cap) > kMaxDynLds) stash_cap >>= 1;
     if (8 * (size_t)(stash_cap + out_cap) > kMaxDynLds) return SEGTOPK_NOT_SUPPORTED;
@@ -1320,10 +1603,16 @@ extern "C" int batched_topk(const segtopk_keys *keys, const segtopk_values *valu
     p.out_cap = out_cap;
     const size_t lds = 8 * (size_t)(stash_cap + out_cap);
 
+    int dev = 0;
     uint32_t P = 1;
-    if ((uint64_t)num_segments < kTargetWorkgroups) {
-        P = (uint32_t)((kTargetWorkgroups + num_segments - 1) / num_segments);
+    if (split) {
+        // As many workgroups as the device holds at once, so that all the
+        // slices of a segment run together and share their bound.
+        if (hipGetDevice(&dev) != hipSuccess) return SEGTOPK_HIP_ERROR;
+        const uint32_t target = resident_wgs_for(type, dev, direction == SEGTOPK_MAX, lds);
+        P = (uint32_t)((target + num_segments - 1) / num_segments);
         if (P > kMaxWgPerSeg) P = kMaxWgPerSeg;
+        if (P < 1) P = 1;
     }
     uint32_t min_slice = kMinSlice;
     if ((uint64_t)8 * k32 > min_slice) min_slice = 8 * k32 > (1u << 30) ? (1u << 30) : 8 * k32;
@@ -1338,8 +1627,6 @@ extern "C" int batched_topk(const segtopk_keys *keys, const segtopk_values *valu
     void *ws = nullptr;
     hipError_t err = hipSuccess;
     if (P > 1) {
-        int dev = 0;
-        if (hipGetDevice(&dev) != hipSuccess) return SEGTOPK_HIP_ERROR;
         prepare_pool(dev);
         const size_t S = (size_t)num_segments;
         const size_t n_hist = S * kBuckets, n_ticket = S;
