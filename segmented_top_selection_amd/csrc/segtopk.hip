@@ -442,7 +442,9 @@ template <int KT, int NT, int U> struct Range {
     }
 };
 
-template <int KT> using WaveRange = Range<KT, kWave, 4>;
+// U 16-byte loads per lane per chunk: 4 where many workgroups each stream a
+// short range, 8 (more bytes in flight per wave) where a few long slices do.
+template <int KT, int U = 4> using WaveRange = Range<KT, kWave, U>;
 
 // ---------------------------------------------------------------------------
 // Pass 0 of one wave over keys [lo, hi) of a segment into a histogram shared
@@ -516,11 +518,11 @@ __device__ __forceinline__ bool wave_push(uint2 *stash, uint32_t cap, uint32_t &
 // counted but not stashed (before the bound, or dropped when the stash
 // overflowed) are read again by wave_reread once the workgroup's bound is
 // final.
-template <int KT, bool LARGEST>
+template <int KT, bool LARGEST, int U>
 __device__ __forceinline__ Pass0 wave_pass0(uint32_t *hist, uint2 *stash, uint32_t cap,
                                             const void *keys, int64_t begin, uint32_t lo,
                                             uint32_t hi, uint32_t target, const Share &sh) {
-    using Rg = WaveRange<KT>;
+    using Rg = WaveRange<KT, U>;
     constexpr int K = Rg::kDw;
     const uint32_t ln = lane_id();
     Rg L;
@@ -688,11 +690,11 @@ __device__ __forceinline__ Pass0 wave_pass0(uint32_t *hist, uint2 *stash, uint32
 // Stashes, under the workgroup's final bound R, the keys of the chunks [0,
 // defer) of [lo, hi) (and the unaligned head and tail).  They were counted in
 // pass 0 already.  Returns false when they do not fit.
-template <int KT, bool LARGEST>
+template <int KT, bool LARGEST, int U>
 __device__ __forceinline__ bool wave_reread(uint2 *stash, uint32_t cap, uint32_t &count,
                                             const void *keys, int64_t begin, uint32_t lo,
                                             uint32_t hi, uint32_t defer, uint32_t R) {
-    using Rg = WaveRange<KT>;
+    using Rg = WaveRange<KT, U>;
     constexpr int K = Rg::kDw;
     const uint32_t ln = lane_id();
     Rg L;
@@ -866,8 +868,15 @@ __device__ __forceinline__ void wave_bitonic(uint2 *buf, uint32_t cnt) {
 // latency overlaps the sort; sorted output is a bitonic network on
 // (key best-first, index ascending) using lane shuffles for strides of E and
 // more and register swaps below that.
+// Sorts list[0, m) (m <= 64 * E, E entries per lane, in registers) best
+// first, ties by ascending index, and writes the first k_i to the row: the
+// sort is both the selection and the output order.  With prefer_larger_index
+// the entries equal to the k_i-th key keep their largest-index members
+// instead, still written in index order.  Values are loaded before the sort
+// so that their latency overlaps it.
 template <int KT, bool LARGEST, int E>
-__device__ __forceinline__ void out_regs(const uint2 *outbuf, const Params &p, const Seg &sg) {
+__device__ __forceinline__ void sort_select(const uint2 *list, uint32_t m, const Params &p,
+                                            const Seg &sg) {
     const uint32_t ln = lane_id();
     uint32_t sk[E], id[E], rw[E], vv[E];
 #pragma unroll
@@ -877,8 +886,8 @@ __device__ __forceinline__ void out_regs(const uint2 *outbuf, const Params &p, c
         id[e] = kNone;
         rw[e] = 0;
         vv[e] = 0;
-        if (j < sg.k_i) {
-            const uint2 x = outbuf[j];
+        if (j < m) {
+            const uint2 x = list[j];
             const uint32_t o = Key<KT>::ord(x.x);
             sk[e] = LARGEST ? ~o : o;
             id[e] = x.y;
@@ -886,7 +895,7 @@ __device__ __forceinline__ void out_regs(const uint2 *outbuf, const Params &p, c
             if (p.vals_in) vv[e] = x.y < sg.n ? p.vals_in[sg.begin + x.y] : kNone;
         }
     }
-    if (p.sorted) {
+    if (p.sorted || m > sg.k_i) {
         for (uint32_t size = 2; size <= (uint32_t)(kWave * E); size <<= 1) {
             for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
                 if (stride >= (uint32_t)E) {
@@ -927,11 +936,34 @@ __device__ __forceinline__ void out_regs(const uint2 *outbuf, const Params &p, c
             }
         }
     }
+    // Output position of sorted position j: j itself, except that with
+    // prefer_larger_index the group [a, b) of entries equal to the k_i-th
+    // keeps its last k_i - a members, moved down to [a, k_i).
+    uint32_t shift = 0, a = sg.k_i;
+    if (p.prefer_larger && m > sg.k_i) {
+        const uint32_t kj = sg.k_i - 1;
+        uint32_t mine = 0;
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            if ((uint32_t)e == kj % E) mine = sk[e];
+        const uint32_t ks = wave_bcast(mine, kj / E);
+        uint32_t lt = 0, le = 0;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const bool real = ln * E + (uint32_t)e < m;  // padding sorts last
+            lt += (uint32_t)__popcll(__ballot(real && sk[e] < ks));
+            le += (uint32_t)__popcll(__ballot(real && sk[e] <= ks));
+        }
+        a = lt;
+        shift = le - sg.k_i;  // b - (k_i - a) - a
+    }
 #pragma unroll
     for (int e = 0; e < E; ++e) {
         const uint32_t j = ln * E + e;
-        if (j < sg.k_i) {
-            const size_t o = (size_t)sg.row * p.k + j;
+        uint32_t pos = j;
+        if (j >= a) pos = (j >= a + shift) ? j - shift : kNone;
+        if (j < m && pos < sg.k_i) {
+            const size_t o = (size_t)sg.row * p.k + pos;
             if (Key<KT>::kBytes == 4)
                 static_cast<uint32_t *>(p.keys_out)[o] = rw[e];
             else
@@ -945,11 +977,11 @@ __device__ __forceinline__ void out_regs(const uint2 *outbuf, const Params &p, c
 template <int KT, bool LARGEST>
 __device__ __forceinline__ void write_staged(uint2 *outbuf, const Params &p, const Seg &sg) {
     if (sg.k_i <= 64) {
-        out_regs<KT, LARGEST, 1>(outbuf, p, sg);
+        sort_select<KT, LARGEST, 1>(outbuf, sg.k_i, p, sg);
     } else if (sg.k_i <= 128) {
-        out_regs<KT, LARGEST, 2>(outbuf, p, sg);
+        sort_select<KT, LARGEST, 2>(outbuf, sg.k_i, p, sg);
     } else if (sg.k_i <= 256) {
-        out_regs<KT, LARGEST, 4>(outbuf, p, sg);
+        sort_select<KT, LARGEST, 4>(outbuf, sg.k_i, p, sg);
     } else {
         if (p.sorted) wave_bitonic<KT, LARGEST>(outbuf, sg.k_i);
         constexpr int kB = 8;
@@ -1140,9 +1172,164 @@ struct alignas(16) Shared {
     uint32_t wbad[kWaves];
     uint32_t wdefer[kWaves];
     uint32_t rg;
+    uint32_t last, total, any_bad, nfront, ntie;  // the last arriver's state
 };
 
+// The last workgroup of a segment to finish pass 0, all four waves: the
+// segment's exact k-th bucket b* from the merged histogram, then every slot's
+// entries up to b* (a prefix, as the slots are sorted by bucket): those of
+// better buckets are winners and are written at once, those of b* go to the
+// LDS list for the remaining passes (wave 0).
 template <int KT, bool LARGEST>
+__device__ __forceinline__ void slice_last(Shared &sh, uint2 *stash, uint2 *outbuf,
+                                           const Params &p, const Seg &sg, int64_t s, uint32_t P,
+                                           uint32_t ps, uint32_t slice) {
+    const uint32_t w = threadIdx.x / kWave;
+    const uint32_t ln = lane_id();
+    const uint32_t *gh = p.ws_hist + (size_t)s * kBuckets;
+    const uint32_t *info = p.ws_slot_info + (size_t)s * P * 4;
+    const uint32_t *slot_cum = p.ws_slot_cum + (size_t)s * P * kBuckets;
+    const uint2 *slot_data = p.ws_slot_data + (size_t)s * P * p.stash_cap;
+
+    // Merged histogram into LDS (plain loads: the ticket's acquire fence
+    // made every slice's additions visible).
+    {
+        const uint4 *g4 = reinterpret_cast<const uint4 *>(gh);
+        uint4 *h4 = reinterpret_cast<uint4 *>(sh.hist);
+        for (uint32_t i = threadIdx.x; i < (uint32_t)kBuckets / 4; i += kThreads) h4[i] = g4[i];
+    }
+    __syncthreads();
+    const Kth ks = wave_find(sh.hist, kBuckets, sg.k_i);  // alike in every wave
+    __syncthreads();
+
+    // Per slot, the prefix up to b*, laid end to end (exclusive prefix).
+    uint32_t *pre = sh.hist;
+    if (w == 0) {
+        uint32_t total = 0;
+        bool any_bad = false;
+        for (uint32_t base = 0; base < ps; base += kWave) {
+            const uint32_t qi = base + ln;
+            uint32_t c = 0;
+            bool bd = false;
+            if (qi < ps) {
+                bd = info[4 * qi + 1] != 0;
+                if (!bd) {
+                    c = slot_cum[(size_t)qi * kBuckets + ks.b];
+                    c = c < p.stash_cap ? c : p.stash_cap;
+                }
+            }
+            any_bad = any_bad || __any(bd);
+            const uint32_t incl = wave_incl_sum(c);
+            if (qi < ps) pre[qi] = total + incl - c;
+            total += wave_bcast(incl, kWave - 1);
+        }
+        if (ln == 0) {
+            pre[ps] = total;
+            sh.total = total;
+            sh.any_bad = any_bad ? 1u : 0u;
+            sh.nfront = 0;
+            sh.ntie = 0;
+        }
+    }
+    __syncthreads();
+    const uint32_t total = sh.total;
+    const bool fast = sh.any_bad == 0 && ks.count <= p.stash_cap;
+    if (fast) {
+        // Batches of 8 entries per lane, spread over the waves; positions
+        // come from LDS counters, one reservation per batch and kind.
+        constexpr int kB = 8;
+        for (uint32_t base = w * kB * kWave; base < total; base += kWaves * kB * kWave) {
+            uint2 e[kB];
+#pragma unroll
+            for (int u = 0; u < kB; ++u) {
+                const uint32_t j = base + (uint32_t)u * kWave + ln;
+                e[u] = make_uint2(0u, kNone);
+                if (j < total) {
+                    uint32_t a = 0, z = ps;  // pre[a] <= j < pre[z]
+                    while (z - a > 1) {
+                        const uint32_t m = (a + z) >> 1;
+                        if (pre[m] <= j) a = m; else z = m;
+                    }
+                    e[u] = slot_data[(size_t)a * p.stash_cap + (j - pre[a])];
+                }
+            }
+            uint32_t rk[kB], nb = 0, nt = 0;
+#pragma unroll
+            for (int u = 0; u < kB; ++u) {
+                rk[u] = e[u].y != kNone ? rank0<KT, LARGEST>(Key<KT>::ord(e[u].x)) : kNone;
+                nb += (uint32_t)__popcll(__ballot(rk[u] < ks.b));
+                nt += (uint32_t)__popcll(__ballot(rk[u] == ks.b));
+            }
+            uint32_t fb = 0, tb = 0;
+            if (ln == 0) {
+                fb = nb ? atomicAdd(&sh.nfront, nb) : 0u;
+                tb = nt ? atomicAdd(&sh.ntie, nt) : 0u;
+            }
+            fb = wave_bcast(fb, 0);
+            tb = wave_bcast(tb, 0);
+            uint32_t fpos[kB];
+#pragma unroll
+            for (int u = 0; u < kB; ++u) {
+                const bool better = rk[u] < ks.b;
+                const bool tie = rk[u] == ks.b;
+                const uint64_t mb = __ballot(better);
+                const uint64_t mt = __ballot(tie);
+                const uint32_t pb = fb + lanes_below(mb);
+                const uint32_t pt = tb + lanes_below(mt);
+                fb += (uint32_t)__popcll(mb);
+                tb += (uint32_t)__popcll(mt);
+                fpos[u] = (better && pb < ks.before) ? pb : kNone;
+                if (outbuf && fpos[u] != kNone) outbuf[pb] = e[u];
+                if (tie && pt < p.stash_cap) stash[pt] = e[u];
+            }
+            if (!outbuf) write_batch<KT, kB>(p, sg, fpos, e);
+        }
+    }
+    __syncthreads();
+    if (w != 0) return;
+
+    Cands<KT> cand;
+    cand.list = stash;
+    cand.keys_in = p.keys_in;
+    cand.begin = sg.begin;
+    cand.n = sg.n;
+    cand.nslices = ps;
+    cand.slice = slice;
+    cand.slot_info = info;
+    cand.slot_cum = slot_cum;
+    cand.slot_data = slot_data;
+    cand.slot_cap = p.stash_cap;
+    cand.bstar = ks.b;
+    cand.lds = false;
+    cand.count = 0;
+    uint32_t placed = 0;
+    if (fast) {
+        cand.lds = true;
+        cand.count = sh.ntie < p.stash_cap ? sh.ntie : p.stash_cap;
+        placed = ks.before;
+    } else {
+        // Rare: a slice lost candidates or bucket b* does not fit in LDS.
+        // Pull what fits into LDS, else leave the candidates in place.
+        const uint32_t thr = rank_thr<KT, LARGEST>(ks.b);
+        const uint32_t cap = p.stash_cap;
+        uint32_t got = 0;
+        cand.visit([&](uint32_t r, uint32_t idx, bool act) {
+            const bool keep = act && within<LARGEST>(Key<KT>::ord(r), thr);
+            const uint64_t m = __ballot(keep);
+            const uint32_t pos = got + lanes_below(m);
+            if (keep && pos < cap) stash[pos] = make_uint2(r, idx);
+            got += (uint32_t)__popcll(m);
+        });
+        wave_sync();
+        if (got <= cap) {
+            cand.lds = true;
+            cand.count = got;
+        }
+    }
+    wave_finish<KT, LARGEST>(sh.hist, outbuf, p, sg, cand, ks, placed);
+}
+
+template <int KT, bool LARGEST, int U>
 __global__ __launch_bounds__(kThreads) void topk_kernel(Params p) {
     __shared__ Shared sh;
     extern __shared__ uint4 dyn[];
@@ -1203,7 +1390,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(Params p) {
     share.gearly = ps > 1 ? p.ws_early + (size_t)s * kBuckets : nullptr;
     share.glast = ps > 1 ? p.ws_slot_cum + ((size_t)s * P + q) * kBuckets : nullptr;
     share.wave = w;
-    const Pass0 r0 = wave_pass0<KT, LARGEST>(sh.hist, stash + w * capw, capw, p.keys_in,
+    const Pass0 r0 = wave_pass0<KT, LARGEST, U>(sh.hist, stash + w * capw, capw, p.keys_in,
                                              sg.begin, wlo, whi, sg.k_i, share);
     if (ln == 0) {
         sh.wcount[w] = r0.count;
@@ -1220,7 +1407,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(Params p) {
         if (ps > 1 && sh.rg < Rf) Rf = sh.rg;
         if (r0.defer != 0) {
             uint32_t cnt = r0.count;
-            const bool ok = wave_reread<KT, LARGEST>(stash + w * capw, capw, cnt, p.keys_in,
+            const bool ok = wave_reread<KT, LARGEST, U>(stash + w * capw, capw, cnt, p.keys_in,
                                                      sg.begin, wlo, whi, r0.defer, Rf);
             if (ln == 0) {
                 sh.wcount[w] = cnt;
@@ -1229,7 +1416,16 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(Params p) {
         }
         __syncthreads();
     }
-    if (w != 0) return;  // wave 0 finishes the workgroup's work alone
+    if (w != 0) {
+        // Wave 0 finishes the workgroup's work alone; with several workgroups
+        // per segment the others wait for the ticket and help the last one.
+        if (ps == 1) return;
+        __syncthreads();
+        if (!sh.last) return;
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        slice_last<KT, LARGEST>(sh, stash, outbuf, p, sg, s, P, ps, slice);
+        return;
+    }
 
     // ---- wave 0: this workgroup's k-th bucket, then its candidates ----
     const Kth kw = wave_find(sh.hist, kBuckets, sg.k_i);
@@ -1324,110 +1520,12 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(Params p) {
     uint32_t last = 0;
     if (ln == 0) last = (atomicAdd(&p.ws_ticket[s], 1u) == ps - 1) ? 1u : 0u;
     last = wave_bcast(last, 0);
+
+    if (ln == 0) sh.last = last;
+    __syncthreads();  // pairs with the one the other waves wait in
     if (!last) return;
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-
-    // ---- last arriver: the segment's k-th bucket, then only the slot
-    // prefixes that can still win ----
-    for (uint32_t i = ln; i < (uint32_t)kBuckets; i += kWave)
-        sh.hist[i] = __hip_atomic_load(&gh[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    wave_sync();
-    const Kth ks = wave_find(sh.hist, kBuckets, sg.k_i);
-    cand.lds = false;
-    cand.nslices = ps;
-    cand.slice = slice;
-    cand.slot_info = info;
-    cand.slot_cum = p.ws_slot_cum + (size_t)s * P * kBuckets;
-    cand.slot_data = p.ws_slot_data + (size_t)s * P * p.stash_cap;
-    cand.bstar = ks.b;
-
-    // Per slot, the entries that can still win are the prefix up to bucket
-    // b*; lay the slots' prefixes end to end (exclusive prefix in LDS).
-    uint32_t *pre = sh.hist;  // the histogram is no longer needed
-    uint32_t total = 0;
-    bool any_bad = false;
-    for (uint32_t base = 0; base < ps; base += kWave) {
-        const uint32_t qi = base + ln;
-        uint32_t c = 0;
-        bool bd = false;
-        if (qi < ps) {
-            bd = info[4 * qi + 1] != 0;
-            if (!bd) {
-                c = cand.slot_cum[(size_t)qi * kBuckets + ks.b];
-                c = c < p.stash_cap ? c : p.stash_cap;
-            }
-        }
-        any_bad = any_bad || __any(bd);
-        const uint32_t incl = wave_incl_sum(c);
-        if (qi < ps) pre[qi] = total + incl - c;
-        total += wave_bcast(incl, kWave - 1);
-    }
-    if (ln == 0) pre[ps] = total;
-    wave_sync();
-    uint32_t placed = 0;
-    if (!any_bad && ks.count <= p.stash_cap) {
-        // Entries of better buckets are winners: write them now.  Entries of
-        // bucket b* go to the LDS list for the remaining passes.
-        constexpr int kB = 8;  // loads in flight per lane
-        uint32_t nb = 0, ntie = 0;
-        for (uint32_t base = 0; base < total; base += kB * kWave) {
-            uint2 e[kB];
-            uint32_t fpos[kB];
-#pragma unroll
-            for (int u = 0; u < kB; ++u) {
-                const uint32_t j = base + (uint32_t)u * kWave + ln;
-                e[u] = make_uint2(0u, kNone);
-                if (j < total) {
-                    // the slot holding entry j: the last q with pre[q] <= j
-                    uint32_t a = 0, z = ps;  // pre[a] <= j < pre[z]
-                    while (z - a > 1) {
-                        const uint32_t m = (a + z) >> 1;
-                        if (pre[m] <= j) a = m; else z = m;
-                    }
-                    e[u] = cand.slot_data[(size_t)a * p.stash_cap + (j - pre[a])];
-                }
-            }
-#pragma unroll
-            for (int u = 0; u < kB; ++u) {
-                const uint32_t rk = e[u].y != kNone ? rank0<KT, LARGEST>(Key<KT>::ord(e[u].x)) : kNone;
-                const bool better = rk < ks.b;
-                const bool tie = rk == ks.b;
-                const uint64_t mb = __ballot(better);
-                const uint64_t mt = __ballot(tie);
-                const uint32_t pb = nb + lanes_below(mb);
-                const uint32_t pt = ntie + lanes_below(mt);
-                nb += (uint32_t)__popcll(mb);
-                ntie += (uint32_t)__popcll(mt);
-                fpos[u] = (better && pb < ks.before) ? pb : kNone;
-                if (outbuf && fpos[u] != kNone) outbuf[pb] = e[u];
-                if (tie && pt < p.stash_cap) stash[pt] = e[u];
-            }
-            if (!outbuf) write_batch<KT, kB>(p, sg, fpos, e);
-        }
-        wave_sync();
-        cand.lds = true;
-        cand.count = ntie < p.stash_cap ? ntie : p.stash_cap;
-        placed = ks.before;
-    } else {
-        // Rare: a slice lost candidates or bucket b* does not fit in LDS.
-        // Pull what fits into LDS, else leave the candidates in place.
-        const uint32_t thr = rank_thr<KT, LARGEST>(ks.b);
-        const uint32_t cap = p.stash_cap;
-        uint32_t got = 0;
-        cand.visit([&](uint32_t r, uint32_t idx, bool act) {
-            const bool keep = act && within<LARGEST>(Key<KT>::ord(r), thr);
-            const uint64_t m = __ballot(keep);
-            const uint32_t pos = got + lanes_below(m);
-            if (keep && pos < cap) stash[pos] = make_uint2(r, idx);
-            got += (uint32_t)__popcll(m);
-        });
-        wave_sync();
-        if (got <= cap) {
-            cand.lds = true;
-            cand.count = got;
-        }
-    }
-    wave_finish<KT, LARGEST>(sh.hist, outbuf, p, sg, cand, ks, placed);
+    slice_last<KT, LARGEST>(sh, stash, outbuf, p, sg, s, P, ps, slice);
 }
 
 __global__ void zero_kernel(uint32_t *p, size_t n) {
@@ -1441,6 +1539,7 @@ __global__ void zero_kernel(uint32_t *p, size_t n) {
 // ---------------------------------------------------------------------------
 constexpr uint32_t kTargetWorkgroups = 2048;  // enough to fill 256 CUs several times
 constexpr uint32_t kMaxWgPerSeg = 256;
+constexpr int kSplitU = 8;  // loads per lane per chunk when segments are split
 constexpr uint32_t kMinSlice = 16384;
 constexpr size_t kMaxDynLds = 120 * 1024;
 
@@ -1494,8 +1593,8 @@ template <int KT> uint32_t resident_wgs(int dev, bool largest, size_t lds) {
                 return g_occ[i].wgs;
     }
     int per_cu = 0, cus = 0;
-    const void *fn = largest ? reinterpret_cast<const void *>(topk_kernel<KT, true>)
-                             : reinterpret_cast<const void *>(topk_kernel<KT, false>);
+    const void *fn = largest ? reinterpret_cast<const void *>(topk_kernel<KT, true, kSplitU>)
+                             : reinterpret_cast<const void *>(topk_kernel<KT, false, kSplitU>);
     if (lds > 64 * 1024)
         (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxDynLds);
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, lds) != hipSuccess ||
@@ -1520,17 +1619,22 @@ uint32_t resident_wgs_for(int type, int dev, bool largest, size_t lds) {
     }
 }
 
-template <int KT>
-hipError_t launch(const Params &p, bool largest, uint32_t grid, size_t lds, hipStream_t st) {
+template <int KT, bool LARGEST, int U>
+hipError_t launch_u(const Params &p, uint32_t grid, size_t lds, hipStream_t st) {
     hipError_t e;
-    if (largest) {
-        if ((e = allow_lds(topk_kernel<KT, true>, lds)) != hipSuccess) return e;
-        hipLaunchKernelGGL((topk_kernel<KT, true>), dim3(grid), dim3(kThreads), lds, st, p);
-    } else {
-        if ((e = allow_lds(topk_kernel<KT, false>, lds)) != hipSuccess) return e;
-        hipLaunchKernelGGL((topk_kernel<KT, false>), dim3(grid), dim3(kThreads), lds, st, p);
-    }
+    if ((e = allow_lds(topk_kernel<KT, LARGEST, U>, lds)) != hipSuccess) return e;
+    hipLaunchKernelGGL((topk_kernel<KT, LARGEST, U>), dim3(grid), dim3(kThreads), lds, st, p);
     return hipGetLastError();
+}
+
+template <int KT>
+hipError_t launch(const Params &p, bool largest, bool split, uint32_t grid, size_t lds,
+                  hipStream_t st) {
+    if (largest)
+        return split ? launch_u<KT, true, kSplitU>(p, grid, lds, st)
+                     : launch_u<KT, true, 4>(p, grid, lds, st);
+    return split ? launch_u<KT, false, kSplitU>(p, grid, lds, st)
+                 : launch_u<KT, false, 4>(p, grid, lds, st);
 }
 
 }  // namespace
@@ -1654,11 +1758,11 @@ extern "C" int batched_topk(const segtopk_keys *keys, const segtopk_values *valu
         const bool largest = direction == SEGTOPK_MAX;
         const uint32_t g = (uint32_t)grid;
         switch (type) {
-        case SEGTOPK_KEY_F32: err = launch<SEGTOPK_KEY_F32>(p, largest, g, lds, stream); break;
-        case SEGTOPK_KEY_BF16: err = launch<SEGTOPK_KEY_BF16>(p, largest, g, lds, stream); break;
-        case SEGTOPK_KEY_U32: err = launch<SEGTOPK_KEY_U32>(p, largest, g, lds, stream); break;
-        case SEGTOPK_KEY_I32: err = launch<SEGTOPK_KEY_I32>(p, largest, g, lds, stream); break;
-        default: err = launch<SEGTOPK_KEY_F16>(p, largest, g, lds, stream); break;
+        case SEGTOPK_KEY_F32: err = launch<SEGTOPK_KEY_F32>(p, largest, split, g, lds, stream); break;
+        case SEGTOPK_KEY_BF16: err = launch<SEGTOPK_KEY_BF16>(p, largest, split, g, lds, stream); break;
+        case SEGTOPK_KEY_U32: err = launch<SEGTOPK_KEY_U32>(p, largest, split, g, lds, stream); break;
+        case SEGTOPK_KEY_I32: err = launch<SEGTOPK_KEY_I32>(p, largest, split, g, lds, stream); break;
+        default: err = launch<SEGTOPK_KEY_F16>(p, largest, split, g, lds, stream); break;
         }
     }
     if (ws) {
