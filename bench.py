@@ -130,13 +130,17 @@ def copy_probe(mib=256, reps=5):
     log(f"copy probe: {reps} copies of {mib} MiB")
 
 
-KERNEL_SRC = os.path.join(ROOT, "segmented_top_selection_amd", "csrc", "segtopk.hip")
+KERNEL_SRC_DIR = os.path.join(ROOT, "segmented_top_selection_amd", "csrc")
 
 
 def kernel_hash():
+    """SHA-256 over every library source (names and contents, sorted)."""
     import hashlib
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(KERNEL_SRC_DIR)):
+        with open(os.path.join(KERNEL_SRC_DIR, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
 
 
 def measured_traffic(name):

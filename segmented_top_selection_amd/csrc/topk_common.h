@@ -1,0 +1,61 @@
+// topk_common.h -- what the host code of libsegtopk and its per-key-type
+// kernel translation units share: launch constants, the kernel argument block
+// and the two entry points every key type provides.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "segtopk.h"
+
+namespace segtopk_impl {
+
+constexpr int kWave = 64;               // wave64
+constexpr int kWaves = 4;               // waves per workgroup
+constexpr int kThreads = kWave * kWaves;
+constexpr int kDigit = 11;              // digit width of every radix pass
+constexpr int kBuckets = 1 << kDigit;   // 2048 histogram buckets
+constexpr uint32_t kNone = 0xFFFFFFFFu; // "no element" / sort padding
+constexpr int kSplitU = 8;               // loads per lane per chunk when segments are split
+constexpr size_t kMaxDynLds = 120 * 1024;
+
+// ---------------------------------------------------------------------------
+// Kernel arguments.
+// ---------------------------------------------------------------------------
+struct Params {
+    const void *keys_in;
+    void *keys_out;
+    const uint32_t *vals_in;  // nullptr: keys only
+    uint32_t *vals_out;
+    const int64_t *offsets;
+    int64_t num_segments;
+    uint32_t k;              // output row stride
+    uint32_t det;            // deterministic tie-break requested
+    uint32_t prefer_larger;  // ties toward larger source indices
+    uint32_t sorted;         // sorted or stable_sorted output
+    uint32_t stash_cap;      // LDS stash entries per workgroup (four equal wave regions)
+    uint32_t out_cap;        // LDS output staging entries (power of two), 0 = none
+    uint32_t wg_per_seg;     // workgroups per segment (1: one workgroup each)
+    uint32_t min_slice;      // smallest slice a segment is split into
+    uint32_t *ws_hist;       // [segments][kBuckets]    merged pass-0 histograms
+    uint32_t *ws_early;      // [segments][kBuckets]    early snapshots (bound sharing)
+    uint32_t *ws_ticket;     // [segments]              arrival tickets
+    uint32_t *ws_slot_info;  // [segments][P][4]        (count, overflowed, bound, -)
+    uint32_t *ws_slot_cum;   // [segments][P][kBuckets] entries with rank <= r
+    uint2 *ws_slot_data;     // [segments][P][stash_cap] candidates sorted by rank
+};
+
+// Launches the top-k kernel for key type KT on `st`: grid workgroups of
+// kThreads threads with `lds` bytes of dynamic LDS.  `split` selects the
+// variant for segments spread over several workgroups.
+template <int KT>
+hipError_t launch_topk(const Params &p, bool largest, bool split, uint32_t grid, size_t lds,
+                       hipStream_t st);
+
+// Workgroups of the split variant of that kernel that fit on one CU of the
+// current device with `lds` bytes of dynamic LDS (at least 1).
+template <int KT> int topk_per_cu(bool largest, size_t lds);
+
+}  // namespace segtopk_impl

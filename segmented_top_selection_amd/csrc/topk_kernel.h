@@ -1,0 +1,1602 @@
+// segtopk.hip -- segmented (batched) top-k for gfx950 (AMD Instinct MI355X).
+//
+// Method: most-significant-digit radix selection.  Each pass builds a histogram
+// of one digit over the surviving candidates, scans it best-first to find the
+// bucket that holds the k-th key, narrows k and the candidate set to that bucket
+// and folds the digit into the splitter.  When the chosen bucket holds exactly
+// the remaining k candidates the passes stop early.  A final filter writes every
+// key beyond the splitter plus exactly enough splitter-equal keys.
+//   [PR "Implement Segmented TopK using Thread-Block-Clusters", §1.2 Radix
+//    (digit) top-k, §1.4 Early stop, §1.5 Final filter and output placement]
+//
+// How it maps onto gfx950 (where it departs from the pages' cluster design):
+//
+//  * One workgroup of four wave64 serves a segment (or a slice of one).  The
+//    four waves stream disjoint quarters of the keys from HBM once each, with
+//    no workgroup barrier inside the streaming loop.
+//  * Pass 0 counts a key in the workgroup's LDS histogram, and copies it with
+//    its index into its wave's LDS stash, only if its bucket can still hold the
+//    k-th key.  The bound each wave uses is the k-th best bucket of what the
+//    shared histogram held when the wave last looked: counts only grow, so a
+//    bound read from a histogram other waves are still filling is merely loose,
+//    never wrong.  Hence every key the answer needs is counted and stashed, and
+//    the counts of every bucket up to the final k-th bucket are exact.  Later
+//    passes, the tie selection and the output read only the stashes; a wave
+//    whose stash overflows (heavy ties, large k) has its quarter re-read.
+//  * After one barrier, wave 0 finishes the segment alone, synchronising its
+//    lanes with wave fences only.
+//  * Buckets are reversed for MAX (bucket = B-1-digit) instead of inverting the
+//    key bits, after -0.0 has been folded onto +0.0 in the order-preserving bit
+//    transform.   [PR "Fix BlockTopK +/-0.0 handling", Fix]
+//  * Deterministic tie-break: the splitter-equal keys are narrowed by further
+//    radix passes over their source index (digits ascending for
+//    prefer_smaller_index, reversed for prefer_larger_index), which picks
+//    exactly the required ties without an index-ordered scan; not_guaranteed
+//    takes ties in arrival order behind an `out < k` guard.
+//    [PR "Implement Segmented TopK ...", §1.6 Determinism / tie-breaking]
+//  * A batch of few, long segments spreads each segment over several
+//    workgroups (CDNA4 has no thread-block clusters).  Each finishes pass 0 on
+//    its slice, adds its histogram to a per-segment global histogram with
+//    atomics, and writes its candidates to a global slot sorted by bucket
+//    together with their cumulative bucket counts; the last workgroup to take
+//    the segment's ticket scans the merged histogram and reads from every slot
+//    only the prefix that can still win.
+//  * sorted / stable_sorted output is a bitonic sort in LDS of the k results on
+//    (ordered key best-first, source index ascending).
+//    [docs "Top-K: Determinism, Tie-Breaking, and Output Ordering", Output
+//     ordering]
+#pragma once
+
+#include "topk_common.h"
+
+namespace segtopk_impl {
+namespace {
+
+// ---------------------------------------------------------------------------
+// Order-preserving bit transform: ord(a) < ord(b) exactly when a < b, and
+// ord(-0.0) == ord(+0.0).  The original bits are kept for output.  Keys are
+// held as their raw bits, zero-extended to 32 bits.
+// ---------------------------------------------------------------------------
+template <int KT> struct Key;
+
+// kSignMag: the raw bits are sign and magnitude (IEEE floats), so the raw
+// bits read as signed integers order the non-negative keys and read as
+// unsigned integers order the non-positive keys in reverse.
+template <> struct Key<SEGTOPK_KEY_F32> {
+    static constexpr int kBits = 32, kBytes = 4;
+    static constexpr bool kSignMag = true;
+    __device__ __forceinline__ static uint32_t ord(uint32_t r) {
+        r = (r == 0x80000000u) ? 0u : r;  // -0.0 joins +0.0
+        return r ^ ((uint32_t)((int32_t)r >> 31) | 0x80000000u);
+    }
+};
+template <> struct Key<SEGTOPK_KEY_BF16> {
+    static constexpr int kBits = 16, kBytes = 2;
+    static constexpr bool kSignMag = true;
+    __device__ __forceinline__ static uint32_t ord(uint32_t r) {
+        r = (r == 0x8000u) ? 0u : r;
+        return r ^ ((r & 0x8000u) ? 0xFFFFu : 0x8000u);
+    }
+};
+template <> struct Key<SEGTOPK_KEY_F16> {
+    static constexpr int kBits = 16, kBytes = 2;
+    static constexpr bool kSignMag = true;
+    __device__ __forceinline__ static uint32_t ord(uint32_t r) {
+        r = (r == 0x8000u) ? 0u : r;
+        return r ^ ((r & 0x8000u) ? 0xFFFFu : 0x8000u);
+    }
+};
+template <> struct Key<SEGTOPK_KEY_U32> {
+    static constexpr int kBits = 32, kBytes = 4;
+    static constexpr bool kSignMag = false;
+    __device__ __forceinline__ static uint32_t ord(uint32_t r) { return r; }
+};
+template <> struct Key<SEGTOPK_KEY_I32> {
+    static constexpr int kBits = 32, kBytes = 4;
+    static constexpr bool kSignMag = false;
+    __device__ __forceinline__ static uint32_t ord(uint32_t r) { return r ^ 0x80000000u; }
+};
+
+// Pass-0 bucket rank of an ordered key: 0 is the best bucket.
+template <int KT, bool LARGEST> __device__ __forceinline__ uint32_t rank0(uint32_t o) {
+    constexpr int sh = Key<KT>::kBits - kDigit;
+    const uint32_t d = o >> sh;
+    return LARGEST ? (uint32_t)(kBuckets - 1) - d : d;
+}
+// Ordered-key threshold of "rank0 <= R": for MAX o >= thr, for MIN o <= thr.
+template <int KT, bool LARGEST> __device__ __forceinline__ uint32_t rank_thr(uint32_t R) {
+    constexpr int sh = Key<KT>::kBits - kDigit;
+    return LARGEST ? ((uint32_t)(kBuckets - 1) - R) << sh : (R << sh) | ((1u << sh) - 1u);
+}
+template <bool LARGEST> __device__ __forceinline__ bool within(uint32_t o, uint32_t thr) {
+    return LARGEST ? o >= thr : o <= thr;
+}
+
+// ---------------------------------------------------------------------------
+// Pre-filter of raw keys against a bucket bound "rank0 <= R", without the
+// ordered-bits transform.  Which keys pass is the same test as the exact one,
+// except that -0.0 may pass where +0.0 would not (a superset, never fewer
+// keys); the exact test follows for the keys that pass.
+//
+//  * Per chunk, each lane reduces its keys with one min or max per key
+//    (packed pairs of 16-bit keys count as one operation) in the domain in
+//    which the bound is a plain threshold, and compares the result once:
+//      kPfMaxS  signed max   >= T      kPfMinU  unsigned min <= T
+//      kPfMinS  signed min   <= T      kPfMaxU  unsigned max >= T
+//    (for sign-magnitude keys a bound above zero is a signed threshold on the
+//    non-negative keys, a bound below zero an unsigned one on the negative
+//    keys, which every non-negative key passes for MAX or fails for MIN).
+//  * A single key passes when (x ^ X) >= T2, the same test folded into one
+//    unsigned comparison.
+// All fields are wave-uniform (scalar registers).
+// ---------------------------------------------------------------------------
+enum : uint32_t { kPfMaxS = 0, kPfMinU = 1, kPfMinS = 2, kPfMaxU = 3 };
+
+struct Prefilter {
+    uint32_t mode, T;  // chunk reduction and its threshold
+    uint32_t X, T2;    // single key: (x ^ X) >= T2
+};
+
+template <int KT, bool LARGEST> __device__ __forceinline__ Prefilter prefilter(uint32_t R) {
+    constexpr int B = Key<KT>::kBits;
+    constexpr uint32_t H = 1u << (B - 1);
+    constexpr uint32_t M = B == 32 ? 0xFFFFFFFFu : 0xFFFFu;
+    const uint32_t thr = rank_thr<KT, LARGEST>(R);
+    uint32_t mode, T;
+    if constexpr (KT == SEGTOPK_KEY_U32) {
+        mode = LARGEST ? kPfMaxU : kPfMinU;
+        T = thr;
+    } else if constexpr (KT == SEGTOPK_KEY_I32) {
+        mode = LARGEST ? kPfMaxS : kPfMinS;
+        T = thr ^ H;
+    } else if (LARGEST) {
+        // ord >= thr.  thr > H: positive keys with bits >= thr - H.  Else
+        // every positive key and the negative keys with bits <= ~thr; a
+        // bound of exactly +0.0 is widened by one step so that -0.0 (which
+        // ord puts at H) passes with it.
+        if (thr > H) {
+            mode = kPfMaxS;
+            T = thr - H;
+        } else {
+            mode = kPfMinU;
+            T = ~(thr < H ? thr : H - 1u) & M;
+        }
+    } else {
+        // ord <= thr.  thr >= H: every negative key (and -0.0) and the
+        // positive keys with bits <= thr - H.  Else the negative keys with
+        // bits >= ~thr.
+        if (thr >= H) {
+            mode = kPfMinS;
+            T = thr - H;
+        } else {
+            mode = kPfMaxU;
+            T = ~thr & M;
+        }
+    }
+    Prefilter f;
+    f.mode = __builtin_amdgcn_readfirstlane(mode);
+    f.T = __builtin_amdgcn_readfirstlane(T & M);
+    // Signed tests become unsigned ones by flipping the sign bit; "<=" tests
+    // become ">=" ones by complementing both sides.
+    const uint32_t flip = (mode == kPfMaxS || mode == kPfMinS) ? H : 0u;
+    const uint32_t neg = (mode == kPfMinU || mode == kPfMinS) ? M : 0u;
+    f.X = __builtin_amdgcn_readfirstlane(flip ^ neg);
+    f.T2 = __builtin_amdgcn_readfirstlane(((T & M) ^ flip) ^ neg);
+    return f;
+}
+
+__device__ __forceinline__ bool pf_key(const Prefilter &f, uint32_t x) { return (x ^ f.X) >= f.T2; }
+
+typedef short pf_s16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned short pf_u16x2 __attribute__((ext_vector_type(2)));
+
+// Reduction of N dwords by op with four interleaved accumulators (enough
+// independent operations in flight, few extra registers).
+template <class T, int N, class Op>
+__device__ __forceinline__ T pf_tree(const uint32_t (&d)[N], Op op) {
+    constexpr int A = N < 4 ? N : 4;
+    T acc[A];
+#pragma unroll
+    for (int j = 0; j < A; ++j) acc[j] = __builtin_bit_cast(T, d[j]);
+#pragma unroll
+    for (int j = A; j < N; ++j) acc[j % A] = op(acc[j % A], __builtin_bit_cast(T, d[j]));
+#pragma unroll
+    for (int w = 1; w < A; w *= 2)
+#pragma unroll
+        for (int j = 0; j + w < A; j += 2 * w) acc[j] = op(acc[j], acc[j + w]);
+    return acc[0];
+}
+
+// Whether any of a lane's keys (N dwords, every key slot valid or zero) can
+// be within the bound.  Zero slots past the end of a range may pass.
+template <int KT, int N>
+__device__ __forceinline__ bool pf_chunk(const Prefilter &f, const uint32_t (&d)[N]) {
+    if constexpr (Key<KT>::kBytes == 4) {
+        switch (f.mode) {
+        case kPfMaxS:
+            return pf_tree<int32_t>(d, [](int32_t a, int32_t b) { return a > b ? a : b; }) >=
+                   (int32_t)f.T;
+        case kPfMinS:
+            return pf_tree<int32_t>(d, [](int32_t a, int32_t b) { return a < b ? a : b; }) <=
+                   (int32_t)f.T;
+        case kPfMinU:
+            return pf_tree<uint32_t>(d, [](uint32_t a, uint32_t b) { return a < b ? a : b; }) <= f.T;
+        default:
+            return pf_tree<uint32_t>(d, [](uint32_t a, uint32_t b) { return a > b ? a : b; }) >= f.T;
+        }
+    } else {
+        switch (f.mode) {
+        case kPfMaxS: {
+            const pf_s16x2 m = pf_tree<pf_s16x2>(
+                d, [](pf_s16x2 a, pf_s16x2 b) { return __builtin_elementwise_max(a, b); });
+            return (int32_t)(m.x > m.y ? m.x : m.y) >= (int32_t)(int16_t)f.T;
+        }
+        case kPfMinS: {
+            const pf_s16x2 m = pf_tree<pf_s16x2>(
+                d, [](pf_s16x2 a, pf_s16x2 b) { return __builtin_elementwise_min(a, b); });
+            return (int32_t)(m.x < m.y ? m.x : m.y) <= (int32_t)(int16_t)f.T;
+        }
+        case kPfMinU: {
+            const pf_u16x2 m = pf_tree<pf_u16x2>(
+                d, [](pf_u16x2 a, pf_u16x2 b) { return __builtin_elementwise_min(a, b); });
+            return (uint32_t)(m.x < m.y ? m.x : m.y) <= f.T;
+        }
+        default: {
+            const pf_u16x2 m = pf_tree<pf_u16x2>(
+                d, [](pf_u16x2 a, pf_u16x2 b) { return __builtin_elementwise_max(a, b); });
+            return (uint32_t)(m.x > m.y ? m.x : m.y) >= f.T;
+        }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Wave helpers (wave64).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t lane_id() { return __lane_id(); }
+
+__device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                     __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// Inclusive prefix sum over the wave with DPP row shifts (within each row of
+// 16 lanes), then row broadcasts of lane 15 and lane 31 across rows.  Lanes
+// with no source lane add 0.
+__device__ __forceinline__ uint32_t wave_incl_sum(uint32_t x) {
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, false);  // row_shr:1
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, false);  // row_shr:2
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, false);  // row_shr:4
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, false);  // row_shr:8
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);  // row_bcast:31
+    return x;
+}
+
+// Value of x in lane `src` (a wave-uniform lane index), in a scalar register.
+__device__ __forceinline__ uint32_t wave_bcast(uint32_t x, uint32_t src) {
+    return (uint32_t)__builtin_amdgcn_readlane((int)x, (int)src);
+}
+
+// Orders this wave's LDS accesses across lanes (lanes run in lockstep; this
+// keeps the compiler from moving LDS traffic across the point).
+__device__ __forceinline__ void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+struct Kth {
+    uint32_t found;   // 0: the buckets hold fewer than `target` keys
+    uint32_t b;       // the bucket holding the target-th key
+    uint32_t before;  // keys in buckets before b
+    uint32_t count;   // keys in bucket b
+};
+
+// Smallest bucket b < nb with hist[0] + ... + hist[b] >= target, by one wave:
+// every lane sums a run of buckets, a wave scan finds the lane whose run
+// crosses the target, then the lanes take one bucket each of that run.
+// hist may be filled concurrently by other waves: every count read is at most
+// the final count, so the bucket found is at or after the final one.
+__device__ __forceinline__ Kth wave_find(const uint32_t *hist, uint32_t nb, uint32_t target) {
+    const uint32_t ln = lane_id();
+    uint32_t per = (nb + 63u) >> 6;
+    per = (per + 3u) & ~3u;  // 4 .. 32 buckets per lane
+    const uint32_t b0 = ln * per;
+    uint32_t s = 0;
+#pragma unroll
+    for (uint32_t q = 0; q < 32; q += 4) {
+        const uint32_t b = b0 + q;
+        if (q < per && b < nb) {
+            const uint4 h = *reinterpret_cast<const uint4 *>(&hist[b]);
+            s += h.x + (b + 1 < nb ? h.y : 0u) + (b + 2 < nb ? h.z : 0u) + (b + 3 < nb ? h.w : 0u);
+        }
+    }
+    const uint32_t incl = wave_incl_sum(s);
+    const uint32_t excl = incl - s;
+    const uint64_t hit = __ballot(excl < target && incl >= target);
+    Kth r;
+    if (hit == 0) {
+        r.found = 0;
+        r.b = nb - 1;
+        r.before = 0;
+        r.count = 0;
+        return r;
+    }
+    const uint32_t L = (uint32_t)__ffsll((unsigned long long)hit) - 1u;
+    const uint32_t baseL = wave_bcast(excl, L);
+    const uint32_t bl = L * per + ln;
+    const uint32_t v = (ln < per && bl < nb) ? hist[bl] : 0u;
+    const uint32_t vi = wave_incl_sum(v);
+    const uint64_t hit2 = __ballot(ln < per && baseL + vi >= target);
+    const uint32_t j = (uint32_t)__ffsll((unsigned long long)hit2) - 1u;
+    r.found = 1;
+    r.b = L * per + j;
+    r.count = wave_bcast(v, j);
+    r.before = baseL + wave_bcast(vi, j) - r.count;
+    return r;
+}
+
+// wave_find over a histogram in global memory that other workgroups are still
+// adding to (relaxed agent-scope loads; any count read is at most the final
+// count, so the bucket found is at or after the final one).
+__device__ __forceinline__ Kth wave_find_global(const uint32_t *g, uint32_t nb, uint32_t target) {
+    const uint32_t ln = lane_id();
+    const uint32_t per = (nb + 63u) >> 6;  // 1 .. 32 buckets per lane
+    const uint32_t b0 = ln * per;
+    uint32_t s = 0;
+    for (uint32_t q = 0; q < per; ++q) {
+        const uint32_t b = b0 + q;
+        if (b < nb) s += __hip_atomic_load(&g[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    const uint32_t incl = wave_incl_sum(s);
+    const uint32_t excl = incl - s;
+    const uint64_t hit = __ballot(excl < target && incl >= target);
+    Kth r;
+    r.found = 0;
+    r.b = nb - 1;
+    r.before = 0;
+    r.count = 0;
+    if (hit == 0) return r;
+    const uint32_t L = (uint32_t)__ffsll((unsigned long long)hit) - 1u;
+    const uint32_t baseL = wave_bcast(excl, L);
+    const uint32_t bl = L * per + ln;
+    const uint32_t v = (ln < per && bl < nb)
+                           ? __hip_atomic_load(&g[bl], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                           : 0u;
+    const uint32_t vi = wave_incl_sum(v);
+    const uint64_t hit2 = __ballot(ln < per && baseL + vi >= target);
+    if (hit2 == 0) return r;  // the counts grew between the two reads: no tighter bound now
+    const uint32_t j = (uint32_t)__ffsll((unsigned long long)hit2) - 1u;
+    r.found = 1;
+    r.b = L * per + j;
+    return r;
+}
+
+__device__ __forceinline__ void wave_clear(uint32_t *hist, uint32_t nb) {
+    const uint32_t ln = lane_id();
+    if (nb >= 256) {
+        for (uint32_t i = ln * 4; i < nb; i += 4 * kWave)
+            *reinterpret_cast<uint4 *>(&hist[i]) = make_uint4(0u, 0u, 0u, 0u);
+    } else {
+        for (uint32_t i = ln; i < nb; i += kWave) hist[i] = 0u;
+    }
+}
+
+
+struct Seg {
+    int64_t begin;  // first element of the segment in keys_in / vals_in
+    uint32_t n;     // segment size
+    uint32_t k_i;   // min(k, n)
+    int64_t row;    // output row
+};
+
+// ---------------------------------------------------------------------------
+// Coalesced reader of the keys [lo, hi) of one segment by NT threads: an
+// unaligned head and tail (under 16 bytes each) element by element, the
+// aligned body with 16-byte loads, U loads per thread per chunk.
+// ---------------------------------------------------------------------------
+template <int KT, int NT, int U> struct Range {
+    static constexpr int kBytes = Key<KT>::kBytes;
+    static constexpr int kVec = 16 / kBytes;  // keys per 16-byte load
+    static constexpr int kU = U;
+    static constexpr int kKpt = kU * kVec;    // keys per thread per chunk
+    static constexpr int kDw = kU * 4;        // dwords per thread per chunk
+    static constexpr uint32_t kChunkVecs = NT * kU;
+
+    const unsigned char *ebase;  // element 0 of the segment
+    const uint4 *vbase;          // first aligned vector of the range
+    uint32_t lo, head, nvec, tail_lo, nscalar, nchunks;
+
+    __device__ __forceinline__ void init(const void *keys, int64_t begin, uint32_t lo_, uint32_t hi_) {
+        ebase = static_cast<const unsigned char *>(keys) + begin * kBytes;
+        lo = lo_;
+        const uint32_t len = hi_ - lo_;
+        const uintptr_t a = reinterpret_cast<uintptr_t>(ebase + (size_t)lo_ * kBytes);
+        const uint32_t h = (uint32_t)(((16u - (a & 15u)) & 15u) / kBytes);
+        head = h < len ? h : len;
+        nvec = (len - head) / kVec;
+        tail_lo = lo + head + nvec * kVec;
+        nscalar = head + (hi_ - tail_lo);
+        vbase = reinterpret_cast<const uint4 *>(ebase + (size_t)(lo + head) * kBytes);
+        nchunks = (nvec + kChunkVecs - 1) / kChunkVecs;
+    }
+    __device__ __forceinline__ uint32_t scalar_idx(uint32_t s) const {
+        return s < head ? lo + s : tail_lo + (s - head);
+    }
+    __device__ __forceinline__ uint32_t load_scalar(uint32_t idx) const {
+        if (kBytes == 4) return reinterpret_cast<const uint32_t *>(ebase)[idx];
+        return reinterpret_cast<const uint16_t *>(ebase)[idx];
+    }
+    // Thread t's part of chunk c: the loaded dwords; key j = u * kVec + e is
+    // element vidx[u] + e (key_at extracts it); vidx[u] == kNone marks a load
+    // past the end, whose dwords are zero.  STREAM: non-temporal loads, for a
+    // single pass over keys that are not read again soon.
+    template <bool STREAM = false>
+    __device__ __forceinline__ void load_chunk(uint32_t c, uint32_t t, uint32_t (&raw)[kDw],
+                                               uint32_t (&vidx)[kU]) const {
+        typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const uint32_t vj = c * kChunkVecs + (uint32_t)u * NT + t;
+            v4u v = {0u, 0u, 0u, 0u};
+            vidx[u] = kNone;
+            if (vj < nvec) {
+                const v4u *src = reinterpret_cast<const v4u *>(vbase) + vj;
+                v = STREAM ? __builtin_nontemporal_load(src) : *src;
+                vidx[u] = lo + head + vj * kVec;
+            }
+            raw[u * 4 + 0] = v.x;
+            raw[u * 4 + 1] = v.y;
+            raw[u * 4 + 2] = v.z;
+            raw[u * 4 + 3] = v.w;
+        }
+    }
+    // Key j of a thread's chunk as raw bits, zero-extended.
+    __device__ __forceinline__ static uint32_t key_at(const uint32_t (&raw)[kDw], int j) {
+        if (kBytes == 4) return raw[j];
+        const uint32_t d = raw[j >> 1];
+        return (j & 1) ? (d >> 16) : (d & 0xFFFFu);
+    }
+    // Calls f(raw, idx, active) for every element, chunk by chunk; every lane
+    // of the thread group makes the same sequence of calls.
+    template <class F> __device__ __forceinline__ void for_each(uint32_t t, F &&f) const {
+        {
+            const bool act = t < nscalar;
+            const uint32_t idx = act ? scalar_idx(t) : 0u;
+            f(act ? load_scalar(idx) : 0u, idx, act);
+        }
+        for (uint32_t c = 0; c < nchunks; ++c) {
+            uint32_t raw[kDw], vidx[kU];
+            load_chunk(c, t, raw, vidx);
+#pragma unroll
+            for (int u = 0; u < kU; ++u)
+#pragma unroll
+                for (int e = 0; e < kVec; ++e)
+                    f(key_at(raw, u * kVec + e), vidx[u] + (uint32_t)e, vidx[u] != kNone);
+        }
+    }
+};
+
+// U 16-byte loads per lane per chunk: 4 where many workgroups each stream a
+// short range, 8 (more bytes in flight per wave) where a few long slices do.
+template <int KT, int U = 4> using WaveRange = Range<KT, kWave, U>;
+
+// ---------------------------------------------------------------------------
+// Pass 0 of one wave over keys [lo, hi) of a segment into a histogram shared
+// with the other waves of the workgroup and into the wave's own stash.
+// ---------------------------------------------------------------------------
+// Bound sharing between the workgroups of one segment (slice mode): the
+// workgroup adds an early snapshot of its histogram to a per-segment global
+// "early" histogram once, and its waves periodically turn that histogram
+// into a bound, published to the other waves through an LDS word.
+// Bound sharing between the workgroups of one segment (slice mode).  Wave 0
+// of each workgroup adds, every few chunks, what its histogram gained since
+// its last contribution (buckets within the bound only) to a per-segment
+// global histogram; it keeps what it has added so far in `glast`.  Every
+// count there is of a distinct key, so the histogram undercounts the
+// segment's and any bucket it yields is a valid bound.  The waves read a
+// bound from it in turn and publish it to the workgroup through an LDS word.
+struct Share {
+    uint32_t *rg;        // LDS: best bound known to the workgroup
+    uint32_t *gearly;    // global: the segment's shared histogram, or nullptr
+    uint32_t *glast;     // global: this workgroup's contributions so far
+    uint32_t wave;       // this wave's index in the workgroup
+};
+
+struct Pass0 {
+    uint32_t R;      // the wave's final bound (rank)
+    uint32_t count;  // stash entries
+    uint32_t defer;  // chunks [0, defer) were counted but not stashed
+};
+
+// Drops, in place, the stash entries whose pass-0 rank is beyond the bound.
+template <int KT, bool LARGEST>
+__device__ __forceinline__ uint32_t wave_compact(uint2 *stash, uint32_t cnt, uint32_t thr) {
+    const uint32_t ln = lane_id();
+    uint32_t out = 0;
+    for (uint32_t base = 0; base < cnt; base += kWave) {
+        const uint32_t i = base + ln;
+        const bool act = i < cnt;
+        const uint2 e = act ? stash[i] : make_uint2(0u, 0u);
+        const bool keep = act && within<LARGEST>(Key<KT>::ord(e.x), thr);
+        const uint64_t m = __ballot(keep);
+        wave_sync();  // this round's reads come before its writes
+        if (keep) stash[out + lanes_below(m)] = e;
+        out += (uint32_t)__popcll(m);
+        wave_sync();
+    }
+    return out;
+}
+
+// Appends the lanes' entries with `ex` set to the stash; false when they do
+// not fit even after dropping the entries beyond bound R.
+template <int KT, bool LARGEST>
+__device__ __forceinline__ bool wave_push(uint2 *stash, uint32_t cap, uint32_t &count, uint32_t R,
+                                          bool ex, uint32_t x, uint32_t idx) {
+    const uint64_t m = __ballot(ex);
+    const uint32_t n = (uint32_t)__popcll(m);
+    if (n == 0) return true;
+    if (count + n > cap) {
+        wave_sync();
+        count = wave_compact<KT, LARGEST>(stash, count, rank_thr<KT, LARGEST>(R));
+        if (count + n > cap) return false;
+    }
+    if (ex) stash[count + lanes_below(m)] = make_uint2(x, idx);
+    count += n;
+    return true;
+}
+
+// Pass 0 of one wave over keys [lo, hi) of a segment.  Until the histogram
+// shared by the workgroup's waves yields a bound, every key is counted and
+// none is stashed.  From then on a key is counted and stashed only if its
+// bucket is within the running bound R, which only tightens.  Chunks that were
+// counted but not stashed (before the bound, or dropped when the stash
+// overflowed) are read again by wave_reread once the workgroup's bound is
+// final.
+template <int KT, bool LARGEST, int U>
+__device__ __forceinline__ Pass0 wave_pass0(uint32_t *hist, uint2 *stash, uint32_t cap,
+                                            const void *keys, int64_t begin, uint32_t lo,
+                                            uint32_t hi, uint32_t target, const Share &sh) {
+    using Rg = WaveRange<KT, U>;
+    constexpr int K = Rg::kDw;
+    constexpr int V = Rg::kVec;
+    const uint32_t ln = lane_id();
+    Rg L;
+    L.init(keys, begin, lo, hi);
+    const uint32_t nch = L.nchunks > 0 ? L.nchunks : 1u;
+    Pass0 r;
+    r.R = kBuckets - 1;  // until `target` keys are counted any bucket may hold the k-th
+    r.count = 0;
+    r.defer = 0;
+    bool bounded = false;
+    bool contributed = false;
+    Prefilter pf = prefilter<KT, LARGEST>(kBuckets - 1);
+
+    // The unaligned head and tail ride along with chunk 0.
+    const bool sv = ln < L.nscalar;
+    const uint32_t si = sv ? L.scalar_idx(ln) : 0u;
+    const uint32_t sx = sv ? L.load_scalar(si) : 0u;
+
+    uint32_t raw[K], vidx[Rg::kU];
+    L.template load_chunk<true>(0, ln, raw, vidx);
+    for (uint32_t c = 0; c < nch; ++c) {
+        uint32_t cur[K], cv[Rg::kU];
+#pragma unroll
+        for (int j = 0; j < K; ++j) cur[j] = raw[j];
+#pragma unroll
+        for (int u = 0; u < Rg::kU; ++u) cv[u] = vidx[u];
+        const bool s0 = sv && c == 0;  // this lane carries a head/tail key now
+        if (c + 1 < nch) L.template load_chunk<true>(c + 1, ln, raw, vidx);  // prefetch
+
+        if (sh.gearly) {
+            // Adopt a tighter bound found by another wave of this workgroup
+            // (one lane reads it, so that the wave agrees on it).
+            const uint32_t rg = __builtin_amdgcn_readfirstlane(
+                __hip_atomic_load(sh.rg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+            if (rg < r.R) {
+                r.R = rg;
+                bounded = true;
+                pf = prefilter<KT, LARGEST>(r.R);
+            }
+            if (bounded && c >= 1) {
+                if (sh.wave == 0 && ((c - 1) & 7u) == 0u) {
+                    // Add what the workgroup's histogram gained since the last
+                    // time.  Later bounds are never looser, so every bucket
+                    // read back from glast was written the first time.
+                    const bool first = !contributed;
+                    contributed = true;
+                    for (uint32_t b = ln; b <= r.R; b += kWave) {
+                        const uint32_t v = hist[b];
+                        const uint32_t l = first ? 0u : sh.glast[b];
+                        if (v > l) atomicAdd(&sh.gearly[b], v - l);
+                        if (first || v != l) sh.glast[b] = v;
+                    }
+                }
+                if (((c - 2u - 2u * sh.wave) & 7u) == 0u && c >= 2u) {
+                    const Kth g = wave_find_global(sh.gearly, r.R + 1, target);
+                    if (g.found && g.b < r.R) {
+                        r.R = g.b;
+                        pf = prefilter<KT, LARGEST>(r.R);
+                        if (ln == 0) atomicMin(sh.rg, g.b);
+                    }
+                }
+            }
+        }
+
+        if (!bounded) {
+            // No bound yet: count every key, then look for the bound.
+            bool any = false;
+#pragma unroll
+            for (int u = 0; u < Rg::kU; ++u)
+#pragma unroll
+                for (int e = 0; e < V; ++e) {
+                    if (cv[u] != kNone) {
+                        atomicAdd(&hist[rank0<KT, LARGEST>(Key<KT>::ord(Rg::key_at(cur, u * V + e)))], 1u);
+                        any = true;
+                    }
+                }
+            if (s0) {
+                atomicAdd(&hist[rank0<KT, LARGEST>(Key<KT>::ord(sx))], 1u);
+                any = true;
+            }
+            r.defer = c + 1;
+            if (!__any(any)) continue;
+            wave_sync();
+            const Kth f = wave_find(hist, kBuckets, target);
+            if (!f.found) continue;
+            r.R = f.b;
+            bounded = true;
+            pf = prefilter<KT, LARGEST>(r.R);
+            // Stash this chunk's keys within the bound from the registers,
+            // if they fit; earlier chunks stay deferred.
+            const uint32_t thr2 = rank_thr<KT, LARGEST>(r.R);
+            const bool sin = s0 && within<LARGEST>(Key<KT>::ord(sx), thr2);
+            uint32_t cnt = sin ? 1u : 0u;
+#pragma unroll
+            for (int u = 0; u < Rg::kU; ++u)
+#pragma unroll
+                for (int e = 0; e < V; ++e)
+                    cnt += (cv[u] != kNone &&
+                            within<LARGEST>(Key<KT>::ord(Rg::key_at(cur, u * V + e)), thr2))
+                               ? 1u : 0u;
+            const uint32_t incl = wave_incl_sum(cnt);
+            const uint32_t total = wave_bcast(incl, kWave - 1);
+            if (r.count + total > cap) continue;  // the stash is empty: defer the chunk
+            uint32_t pos = r.count + incl - cnt;
+            if (sin) stash[pos++] = make_uint2(sx, si);
+#pragma unroll
+            for (int u = 0; u < Rg::kU; ++u)
+#pragma unroll
+                for (int e = 0; e < V; ++e) {
+                    const uint32_t x = Rg::key_at(cur, u * V + e);
+                    if (cv[u] != kNone && within<LARGEST>(Key<KT>::ord(x), thr2))
+                        stash[pos++] = make_uint2(x, cv[u] + (uint32_t)e);
+                }
+            r.count += total;
+            r.defer = c;
+            continue;
+        }
+
+        // Bounded: one min or max per key decides whether any key of the
+        // chunk can be within the bound; only then are the keys tested one
+        // by one, and only a key position in which some lane passes takes
+        // the exact rank test, the count and the stash push.
+        const bool cp = pf_chunk<KT>(pf, cur);
+        const bool sp = s0 && pf_key(pf, sx);
+        if (!__any(cp || sp)) continue;
+        uint32_t counted = 0;
+        bool ok = true;
+        auto take = [&](uint32_t x, uint32_t idx, bool valid) {
+            const bool pv = valid && pf_key(pf, x);
+            if (!__any(pv)) return;
+            const uint32_t rk = rank0<KT, LARGEST>(Key<KT>::ord(x));
+            const bool ex = pv && rk <= r.R;
+            if (ex) atomicAdd(&hist[rk], 1u);
+            counted += (uint32_t)__popcll(__ballot(ex));
+            if (ok) ok = wave_push<KT, LARGEST>(stash, cap, r.count, r.R, ex, x, idx);
+        };
+        take(sx, si, s0);
+#pragma unroll
+        for (int u = 0; u < Rg::kU; ++u)
+#pragma unroll
+            for (int e = 0; e < V; ++e)
+                take(Rg::key_at(cur, u * V + e), cv[u] + (uint32_t)e, cv[u] != kNone);
+        if (!ok) {
+            // The stash is full even within the bound: drop it and read this
+            // and every earlier chunk again later.
+            r.count = 0;
+            r.defer = c + 1;
+        }
+        if (counted) {
+            // Tighten the bound from everything counted so far.
+            wave_sync();
+            const Kth f = wave_find(hist, r.R + 1, target);
+            if (f.found && f.b < r.R) {
+                r.R = f.b;
+                pf = prefilter<KT, LARGEST>(r.R);
+            }
+        }
+    }
+    return r;
+}
+
+// Stashes, under the workgroup's final bound R, the keys of the chunks [0,
+// defer) of [lo, hi) (and the unaligned head and tail).  They were counted in
+// pass 0 already.  Returns false when they do not fit.
+template <int KT, bool LARGEST, int U>
+__device__ __forceinline__ bool wave_reread(uint2 *stash, uint32_t cap, uint32_t &count,
+                                            const void *keys, int64_t begin, uint32_t lo,
+                                            uint32_t hi, uint32_t defer, uint32_t R) {
+    using Rg = WaveRange<KT, U>;
+    constexpr int K = Rg::kDw;
+    constexpr int V = Rg::kVec;
+    const uint32_t ln = lane_id();
+    Rg L;
+    L.init(keys, begin, lo, hi);
+    const uint32_t thr = rank_thr<KT, LARGEST>(R);
+    const Prefilter pf = prefilter<KT, LARGEST>(R);
+    bool ok;
+    {
+        const bool sv = ln < L.nscalar;
+        const uint32_t si = sv ? L.scalar_idx(ln) : 0u;
+        const uint32_t x = sv ? L.load_scalar(si) : 0u;
+        ok = wave_push<KT, LARGEST>(stash, cap, count, R,
+                                    sv && within<LARGEST>(Key<KT>::ord(x), thr), x, si);
+    }
+    const uint32_t nre = defer < L.nchunks ? defer : L.nchunks;
+    uint32_t raw[K], vidx[Rg::kU];
+    if (nre > 0) L.load_chunk(0, ln, raw, vidx);
+    for (uint32_t c = 0; c < nre && ok; ++c) {
+        uint32_t cur[K], cv[Rg::kU];
+#pragma unroll
+        for (int j = 0; j < K; ++j) cur[j] = raw[j];
+#pragma unroll
+        for (int u = 0; u < Rg::kU; ++u) cv[u] = vidx[u];
+        if (c + 1 < nre) L.load_chunk(c + 1, ln, raw, vidx);
+        // A chunk in which no lane can be within the bound costs one
+        // reduction and one ballot.
+        if (!__any(pf_chunk<KT>(pf, cur))) continue;
+#pragma unroll
+        for (int u = 0; u < Rg::kU; ++u)
+#pragma unroll
+            for (int e = 0; e < V; ++e) {
+                const uint32_t x = Rg::key_at(cur, u * V + e);
+                if (ok)
+                    ok = wave_push<KT, LARGEST>(stash, cap, count, R,
+                                                cv[u] != kNone && within<LARGEST>(Key<KT>::ord(x), thr),
+                                                x, cv[u] + (uint32_t)e);
+            }
+    }
+    return ok;
+}
+
+// ---------------------------------------------------------------------------
+// Candidates after pass 0, visited by wave 0: an LDS list, or (when a stash
+// overflowed) global sources -- per slice either the first `cnt` entries of a
+// global slot or, for an overflowed slot, the slice's keys again.
+// ---------------------------------------------------------------------------
+template <int KT> struct Cands {
+    const uint2 *list;      // LDS list ...
+    uint32_t count;
+    bool lds;
+    const void *keys_in;    // ... or global sources
+    int64_t begin;
+    uint32_t n, nslices, slice;
+    const uint32_t *slot_info;  // nullptr: every slice is re-read from the keys
+    const uint32_t *slot_cum;
+    const uint2 *slot_data;
+    uint32_t slot_cap, bstar;
+
+    template <class F> __device__ __forceinline__ void visit(F &&f) const {
+        const uint32_t ln = lane_id();
+        if (lds) {
+            for (uint32_t base = 0; base < count; base += kWave) {
+                const uint32_t i = base + ln;
+                const bool act = i < count;
+                const uint2 e = act ? list[i] : make_uint2(0u, 0u);
+                f(e.x, e.y, act);
+            }
+            return;
+        }
+        for (uint32_t q = 0; q < nslices; ++q) {
+            const uint32_t lo = q * slice;
+            const uint32_t hi = (n - lo) > slice ? lo + slice : n;
+            if (slot_info == nullptr || slot_info[4 * q + 1] != 0) {
+                WaveRange<KT> L;
+                L.init(keys_in, begin, lo, hi);
+                L.for_each(ln, f);
+            } else {
+                uint32_t cnt = slot_cum[(size_t)q * kBuckets + bstar];
+                cnt = cnt < slot_cap ? cnt : slot_cap;
+                const uint2 *d = slot_data + (size_t)q * slot_cap;
+                for (uint32_t base = 0; base < cnt; base += kWave) {
+                    const uint32_t i = base + ln;
+                    const bool act = i < cnt;
+                    const uint2 e = act ? d[i] : make_uint2(0u, 0u);
+                    f(e.x, e.y, act);
+                }
+            }
+        }
+    }
+};
+
+// ---------------------------------------------------------------------------
+// Output.
+// ---------------------------------------------------------------------------
+template <int KT>
+__device__ __forceinline__ void write_out(const Params &p, const Seg &sg, uint32_t pos,
+                                          uint32_t raw, uint32_t idx) {
+    // Both indices are in range by construction; the checks keep any slip
+    // inside the segment's own row and input.
+    if (pos >= sg.k_i) return;
+    const size_t o = (size_t)sg.row * p.k + pos;
+    if (Key<KT>::kBytes == 4)
+        static_cast<uint32_t *>(p.keys_out)[o] = raw;
+    else
+        static_cast<uint16_t *>(p.keys_out)[o] = (uint16_t)raw;
+    if (p.vals_in) p.vals_out[o] = idx < sg.n ? p.vals_in[sg.begin + idx] : kNone;
+}
+
+// write_out for B entries per lane: every value load is issued before the
+// first store, so that the loads' latencies overlap.
+template <int KT, int B>
+__device__ __forceinline__ void write_batch(const Params &p, const Seg &sg, const uint32_t (&pos)[B],
+                                            const uint2 (&e)[B]) {
+    uint32_t v[B];
+#pragma unroll
+    for (int u = 0; u < B; ++u)
+        v[u] = (p.vals_in && pos[u] < sg.k_i && e[u].y < sg.n) ? p.vals_in[sg.begin + e[u].y] : kNone;
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+        if (pos[u] >= sg.k_i) continue;
+        const size_t o = (size_t)sg.row * p.k + pos[u];
+        if (Key<KT>::kBytes == 4)
+            static_cast<uint32_t *>(p.keys_out)[o] = e[u].x;
+        else
+            static_cast<uint16_t *>(p.keys_out)[o] = (uint16_t)e[u].x;
+        if (p.vals_in) p.vals_out[o] = v[u];
+    }
+}
+
+// a before b in the output: better key first, then smaller index; entries
+// with idx == kNone are padding and go last.
+template <int KT, bool LARGEST>
+__device__ __forceinline__ bool out_before(uint2 a, uint2 b) {
+    if (a.y == kNone) return false;
+    if (b.y == kNone) return true;
+    const uint32_t oa = Key<KT>::ord(a.x), ob = Key<KT>::ord(b.x);
+    if (oa != ob) return LARGEST ? oa > ob : oa < ob;
+    return a.y < b.y;
+}
+
+// Bitonic sort of buf[0, cnt) in LDS by one wave.
+template <int KT, bool LARGEST>
+__device__ __forceinline__ void wave_bitonic(uint2 *buf, uint32_t cnt) {
+    const uint32_t ln = lane_id();
+    uint32_t P = 1;
+    while (P < cnt) P <<= 1;
+    for (uint32_t i = cnt + ln; i < P; i += kWave) buf[i] = make_uint2(0u, kNone);
+    wave_sync();
+    for (uint32_t size = 2; size <= P; size <<= 1) {
+        for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
+            for (uint32_t i = ln; i < (P >> 1); i += kWave) {
+                const uint32_t lo = 2 * i - (i & (stride - 1));
+                const uint32_t hi = lo + stride;
+                const bool asc = (lo & size) == 0;
+                const uint2 a = buf[lo], b = buf[hi];
+                if (out_before<KT, LARGEST>(b, a) == asc) {
+                    buf[lo] = b;
+                    buf[hi] = a;
+                }
+            }
+            wave_sync();
+        }
+    }
+}
+
+// Output of up to 64*E staged results held in registers, E per lane (lane l
+// holds results l*E .. l*E+E-1).  The values are gathered first so their
+// latency overlaps the sort; sorted output is a bitonic network on
+// (key best-first, index ascending) using lane shuffles for strides of E and
+// more and register swaps below that.
+// Sorts list[0, m) (m <= 64 * E, E entries per lane, in registers) best
+// first, ties by ascending index, and writes the first k_i to the row: the
+// sort is both the selection and the output order.  With prefer_larger_index
+// the entries equal to the k_i-th key keep their largest-index members
+// instead, still written in index order.  Values are loaded before the sort
+// so that their latency overlaps it.
+template <int KT, bool LARGEST, int E>
+__device__ __forceinline__ void sort_select(const uint2 *list, uint32_t m, const Params &p,
+                                            const Seg &sg) {
+    const uint32_t ln = lane_id();
+    uint32_t sk[E], id[E], rw[E], vv[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const uint32_t j = ln * E + e;
+        sk[e] = kNone;
+        id[e] = kNone;
+        rw[e] = 0;
+        vv[e] = 0;
+        if (j < m) {
+            const uint2 x = list[j];
+            const uint32_t o = Key<KT>::ord(x.x);
+            sk[e] = LARGEST ? ~o : o;
+            id[e] = x.y;
+            rw[e] = x.x;
+            if (p.vals_in) vv[e] = x.y < sg.n ? p.vals_in[sg.begin + x.y] : kNone;
+        }
+    }
+    if (p.sorted || m > sg.k_i) {
+        for (uint32_t size = 2; size <= (uint32_t)(kWave * E); size <<= 1) {
+            for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
+                if (stride >= (uint32_t)E) {
+                    const int lm = (int)(stride / E);
+#pragma unroll
+                    for (int e = 0; e < E; ++e) {
+                        const uint32_t j = ln * E + e;
+                        const uint32_t psk = __shfl_xor(sk[e], lm, kWave);
+                        const uint32_t pid = __shfl_xor(id[e], lm, kWave);
+                        const uint32_t prw = __shfl_xor(rw[e], lm, kWave);
+                        const uint32_t pvv = __shfl_xor(vv[e], lm, kWave);
+                        const bool asc = (j & size) == 0;
+                        const bool lower = (j & stride) == 0;
+                        const bool pfirst = psk < sk[e] || (psk == sk[e] && pid < id[e]);
+                        if ((lower == asc) ? pfirst : !pfirst) {
+                            sk[e] = psk;
+                            id[e] = pid;
+                            rw[e] = prw;
+                            vv[e] = pvv;
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < E; ++e) {
+                        if (e & stride) continue;
+                        const int f = e | (int)stride;
+                        const uint32_t j = ln * E + e;
+                        const bool asc = (j & size) == 0;
+                        const bool ffirst = sk[f] < sk[e] || (sk[f] == sk[e] && id[f] < id[e]);
+                        if (ffirst == asc) {
+                            uint32_t t0 = sk[e]; sk[e] = sk[f]; sk[f] = t0;
+                            t0 = id[e]; id[e] = id[f]; id[f] = t0;
+                            t0 = rw[e]; rw[e] = rw[f]; rw[f] = t0;
+                            t0 = vv[e]; vv[e] = vv[f]; vv[f] = t0;
+                        }
+                    }
+                }
+            }
+        }
+    }
+    // Output position of sorted position j: j itself, except that with
+    // prefer_larger_index the group [a, b) of entries equal to the k_i-th
+    // keeps its last k_i - a members, moved down to [a, k_i).
+    uint32_t shift = 0, a = sg.k_i;
+    if (p.prefer_larger && m > sg.k_i) {
+        const uint32_t kj = sg.k_i - 1;
+        uint32_t mine = 0;
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            if ((uint32_t)e == kj % E) mine = sk[e];
+        const uint32_t ks = wave_bcast(mine, kj / E);
+        uint32_t lt = 0, le = 0;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const bool real = ln * E + (uint32_t)e < m;  // padding sorts last
+            lt += (uint32_t)__popcll(__ballot(real && sk[e] < ks));
+            le += (uint32_t)__popcll(__ballot(real && sk[e] <= ks));
+        }
+        a = lt;
+        shift = le - sg.k_i;  // b - (k_i - a) - a
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const uint32_t j = ln * E + e;
+        uint32_t pos = j;
+        if (j >= a) pos = (j >= a + shift) ? j - shift : kNone;
+        if (j < m && pos < sg.k_i) {
+            const size_t o = (size_t)sg.row * p.k + pos;
+            if (Key<KT>::kBytes == 4)
+                static_cast<uint32_t *>(p.keys_out)[o] = rw[e];
+            else
+                static_cast<uint16_t *>(p.keys_out)[o] = (uint16_t)rw[e];
+            if (p.vals_in) p.vals_out[o] = vv[e];
+        }
+    }
+}
+
+// The staged results outbuf[0, k_i): registers for small k, else an LDS sort.
+template <int KT, bool LARGEST>
+__device__ __forceinline__ void write_staged(uint2 *outbuf, const Params &p, const Seg &sg) {
+    if (sg.k_i <= 64) {
+        sort_select<KT, LARGEST, 1>(outbuf, sg.k_i, p, sg);
+    } else if (sg.k_i <= 128) {
+        sort_select<KT, LARGEST, 2>(outbuf, sg.k_i, p, sg);
+    } else if (sg.k_i <= 256) {
+        sort_select<KT, LARGEST, 4>(outbuf, sg.k_i, p, sg);
+    } else {
+        if (p.sorted) wave_bitonic<KT, LARGEST>(outbuf, sg.k_i);
+        constexpr int kB = 8;
+        for (uint32_t base = 0; base < sg.k_i; base += kB * kWave) {
+            uint32_t pos[kB];
+            uint2 e[kB];
+#pragma unroll
+            for (int u = 0; u < kB; ++u) {
+                pos[u] = base + (uint32_t)u * kWave + lane_id();
+                e[u] = pos[u] < sg.k_i ? outbuf[pos[u]] : make_uint2(0u, kNone);
+            }
+            write_batch<KT, kB>(p, sg, pos, e);
+        }
+    }
+}
+
+// k >= n: every key of the segment is selected (one wave).
+template <int KT, bool LARGEST>
+__device__ __forceinline__ void wave_select_all(uint2 *outbuf, const Params &p, const Seg &sg) {
+    const uint32_t ln = lane_id();
+    WaveRange<KT> L;
+    L.init(p.keys_in, sg.begin, 0u, sg.n);
+    if (p.sorted) {  // n <= k <= out_cap
+        L.for_each(ln, [&](uint32_t raw, uint32_t idx, bool act) {
+            if (act) outbuf[idx] = make_uint2(raw, idx);
+        });
+        wave_sync();
+        write_staged<KT, LARGEST>(outbuf, p, sg);
+    } else {
+        L.for_each(ln, [&](uint32_t raw, uint32_t idx, bool act) {
+            if (act) write_out<KT>(p, sg, idx, raw, idx);
+        });
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Passes 1.., the tie selection and the output, by one wave, given the
+// pass-0 result (bucket k0.b holds the k-th key, k0.before keys precede it,
+// k0.count keys are in it).  hist is scratch.
+// ---------------------------------------------------------------------------
+template <int KT, bool LARGEST>
+__device__ __forceinline__ void wave_finish(uint32_t *hist, uint2 *outbuf, const Params &p,
+                                            const Seg &sg, const Cands<KT> &cand, Kth k0,
+                                            uint32_t placed = 0) {
+    constexpr int KB = Key<KT>::kBits;
+    const uint32_t ln = lane_id();
+    const bool pl = p.prefer_larger != 0;
+
+    int hi = KB - kDigit;
+    uint32_t kmask = (uint32_t)(kBuckets - 1) << hi;
+    uint32_t kpref = (LARGEST ? (uint32_t)(kBuckets - 1) - k0.b : k0.b) << hi;
+    uint32_t krem = sg.k_i - k0.before;
+    uint32_t front = k0.before;
+    bool done = (k0.count == krem);
+
+    // Key digits.
+    while (!done && hi > 0) {
+        const int w = hi < kDigit ? hi : kDigit;
+        const int sh = hi - w;
+        const uint32_t nb = 1u << w;
+        wave_clear(hist, nb);
+        wave_sync();
+        cand.visit([&](uint32_t r, uint32_t idx, bool act) {
+            const uint32_t o = Key<KT>::ord(r);
+            if (act && (o & kmask) == kpref) {
+                const uint32_t d = (o >> sh) & (nb - 1);
+                atomicAdd(&hist[LARGEST ? nb - 1 - d : d], 1u);
+            }
+        });
+        wave_sync();
+        const Kth f = wave_find(hist, nb, krem);
+        krem -= f.before;
+        front += f.before;
+        kpref |= (LARGEST ? nb - 1 - f.b : f.b) << sh;
+        kmask |= (nb - 1) << sh;
+        done = (f.count == krem);
+        hi = sh;
+        wave_sync();
+    }
+
+    // Deterministic modes: narrow the splitter-equal keys by source index.
+    // The `ties` winners are the best of them by index; `front` stays.
+    const uint32_t ties = krem;
+    bool by_index = false;
+    uint32_t imask = 0, ipref = 0;
+    if (!done && p.det) {
+        by_index = true;
+        hi = 32 - __clz((int)(sg.n - 1u));
+        while (!done && hi > 0) {
+            const int w = hi < kDigit ? hi : kDigit;
+            const int sh = hi - w;
+            const uint32_t nb = 1u << w;
+            wave_clear(hist, nb);
+            wave_sync();
+            cand.visit([&](uint32_t r, uint32_t idx, bool act) {
+                if (act && (Key<KT>::ord(r) & kmask) == kpref && (idx & imask) == ipref) {
+                    const uint32_t d = (idx >> sh) & (nb - 1);
+                    atomicAdd(&hist[pl ? nb - 1 - d : d], 1u);
+                }
+            });
+            wave_sync();
+            const Kth f = wave_find(hist, nb, krem);
+            krem -= f.before;
+            ipref |= (pl ? nb - 1 - f.b : f.b) << sh;
+            imask |= (nb - 1) << sh;
+            done = (f.count == krem);
+            hi = sh;
+            wave_sync();
+        }
+    }
+
+    // Final filter: keys better than the splitter to [placed, front) (the
+    // caller has written [0, placed) already), the chosen ties to
+    // [front, k_i).
+    uint32_t nf = placed, nt = 0;
+    if (!outbuf && cand.lds) {
+        // Written straight to the output: classify 8 entries per lane, then
+        // write them with their value loads in flight together.
+        constexpr int kB = 8;
+        for (uint32_t base = 0; base < cand.count; base += kB * kWave) {
+            uint32_t pos[kB];
+            uint2 e[kB];
+#pragma unroll
+            for (int u = 0; u < kB; ++u) {
+                const uint32_t i = base + (uint32_t)u * kWave + ln;
+                const bool act = i < cand.count;
+                e[u] = act ? cand.list[i] : make_uint2(0u, kNone);
+                const uint32_t km = Key<KT>::ord(e[u].x) & kmask;
+                const bool better = act && (LARGEST ? km > kpref : km < kpref);
+                bool tie = act && km == kpref;
+                if (by_index) {
+                    const uint32_t im = e[u].y & imask;
+                    tie = tie && (pl ? im >= ipref : im <= ipref);
+                }
+                const uint64_t mb = __ballot(better);
+                const uint64_t mt = __ballot(tie);
+                const uint32_t pb = nf + lanes_below(mb);
+                const uint32_t pt = nt + lanes_below(mt);
+                nf += (uint32_t)__popcll(mb);
+                nt += (uint32_t)__popcll(mt);
+                pos[u] = kNone;
+                if (better && pb < front) pos[u] = pb;
+                if (tie && pt < ties) pos[u] = front + pt;
+            }
+            write_batch<KT, kB>(p, sg, pos, e);
+        }
+        return;
+    }
+    cand.visit([&](uint32_t r, uint32_t idx, bool act) {
+        const uint32_t km = Key<KT>::ord(r) & kmask;
+        const bool better = act && (LARGEST ? km > kpref : km < kpref);
+        bool tie = act && km == kpref;
+        if (by_index) {
+            const uint32_t im = idx & imask;
+            tie = tie && (pl ? im >= ipref : im <= ipref);
+        }
+        const uint64_t mb = __ballot(better);
+        const uint64_t mt = __ballot(tie);
+        const uint32_t pb = nf + lanes_below(mb);
+        const uint32_t pt = nt + lanes_below(mt);
+        nf += (uint32_t)__popcll(mb);
+        nt += (uint32_t)__popcll(mt);
+        uint32_t pos = kNone;
+        if (better && pb < front) pos = pb;
+        if (tie && pt < ties) pos = front + pt;
+        if (pos != kNone) {
+            if (outbuf)
+                outbuf[pos] = make_uint2(r, idx);
+            else
+                write_out<KT>(p, sg, pos, r, idx);
+        }
+    });
+    if (outbuf) {
+        wave_sync();
+        write_staged<KT, LARGEST>(outbuf, p, sg);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// The kernel.  Grid: ceil(S / 8) * 8 * P workgroups of four waves.
+// Workgroup b serves segment (b / 8 / P) * 8 + b % 8, slice (b / 8) % P, so all
+// workgroups of one segment share b % 8 -- the XCD they are dispatched to --
+// and their atomics and slots stay in one L2.
+// ---------------------------------------------------------------------------
+struct alignas(16) Shared {
+    uint32_t hist[kBuckets];
+    uint32_t wcount[kWaves];
+    uint32_t wbad[kWaves];
+    uint32_t wdefer[kWaves];
+    uint32_t rg;
+    uint32_t last, total, any_bad, nfront, ntie;  // the last arriver's state
+};
+
+// The last workgroup of a segment to finish pass 0, all four waves: the
+// segment's exact k-th bucket b* from the merged histogram, then every slot's
+// entries up to b* (a prefix, as the slots are sorted by bucket): those of
+// better buckets are winners and are written at once, those of b* go to the
+// LDS list for the remaining passes (wave 0).
+template <int KT, bool LARGEST>
+__device__ __forceinline__ void slice_last(Shared &sh, uint2 *stash, uint2 *outbuf,
+                                           const Params &p, const Seg &sg, int64_t s, uint32_t P,
+                                           uint32_t ps, uint32_t slice) {
+    const uint32_t w = threadIdx.x / kWave;
+    const uint32_t ln = lane_id();
+    const uint32_t *gh = p.ws_hist + (size_t)s * kBuckets;
+    const uint32_t *info = p.ws_slot_info + (size_t)s * P * 4;
+    const uint32_t *slot_cum = p.ws_slot_cum + (size_t)s * P * kBuckets;
+    const uint2 *slot_data = p.ws_slot_data + (size_t)s * P * p.stash_cap;
+
+    // Merged histogram into LDS (plain loads: the ticket's acquire fence
+    // made every slice's additions visible).
+    {
+        const uint4 *g4 = reinterpret_cast<const uint4 *>(gh);
+        uint4 *h4 = reinterpret_cast<uint4 *>(sh.hist);
+        for (uint32_t i = threadIdx.x; i < (uint32_t)kBuckets / 4; i += kThreads) h4[i] = g4[i];
+    }
+    __syncthreads();
+    const Kth ks = wave_find(sh.hist, kBuckets, sg.k_i);  // alike in every wave
+    __syncthreads();
+
+    // Per slot, the prefix up to b*, laid end to end (exclusive prefix).
+    uint32_t *pre = sh.hist;
+    if (w == 0) {
+        uint32_t total = 0;
+        bool any_bad = false;
+        for (uint32_t base = 0; base < ps; base += kWave) {
+            const uint32_t qi = base + ln;
+            uint32_t c = 0;
+            bool bd = false;
+            if (qi < ps) {
+                bd = info[4 * qi + 1] != 0;
+                if (!bd) {
+                    c = slot_cum[(size_t)qi * kBuckets + ks.b];
+                    c = c < p.stash_cap ? c : p.stash_cap;
+                }
+            }
+            any_bad = any_bad || __any(bd);
+            const uint32_t incl = wave_incl_sum(c);
+            if (qi < ps) pre[qi] = total + incl - c;
+            total += wave_bcast(incl, kWave - 1);
+        }
+        if (ln == 0) {
+            pre[ps] = total;
+            sh.total = total;
+            sh.any_bad = any_bad ? 1u : 0u;
+            sh.nfront = 0;
+            sh.ntie = 0;
+        }
+    }
+    __syncthreads();
+    const uint32_t total = sh.total;
+    const bool fast = sh.any_bad == 0 && ks.count <= p.stash_cap;
+    if (fast) {
+        // Batches of 8 entries per lane, spread over the waves; positions
+        // come from LDS counters, one reservation per batch and kind.
+        constexpr int kB = 8;
+        for (uint32_t base = w * kB * kWave; base < total; base += kWaves * kB * kWave) {
+            uint2 e[kB];
+#pragma unroll
+            for (int u = 0; u < kB; ++u) {
+                const uint32_t j = base + (uint32_t)u * kWave + ln;
+                e[u] = make_uint2(0u, kNone);
+                if (j < total) {
+                    uint32_t a = 0, z = ps;  // pre[a] <= j < pre[z]
+                    while (z - a > 1) {
+                        const uint32_t m = (a + z) >> 1;
+                        if (pre[m] <= j) a = m; else z = m;
+                    }
+                    e[u] = slot_data[(size_t)a * p.stash_cap + (j - pre[a])];
+                }
+            }
+            uint32_t rk[kB], nb = 0, nt = 0;
+#pragma unroll
+            for (int u = 0; u < kB; ++u) {
+                rk[u] = e[u].y != kNone ? rank0<KT, LARGEST>(Key<KT>::ord(e[u].x)) : kNone;
+                nb += (uint32_t)__popcll(__ballot(rk[u] < ks.b));
+                nt += (uint32_t)__popcll(__ballot(rk[u] == ks.b));
+            }
+            uint32_t fb = 0, tb = 0;
+            if (ln == 0) {
+                fb = nb ? atomicAdd(&sh.nfront, nb) : 0u;
+                tb = nt ? atomicAdd(&sh.ntie, nt) : 0u;
+            }
+            fb = wave_bcast(fb, 0);
+            tb = wave_bcast(tb, 0);
+            uint32_t fpos[kB];
+#pragma unroll
+            for (int u = 0; u < kB; ++u) {
+                const bool better = rk[u] < ks.b;
+                const bool tie = rk[u] == ks.b;
+                const uint64_t mb = __ballot(better);
+                const uint64_t mt = __ballot(tie);
+                const uint32_t pb = fb + lanes_below(mb);
+                const uint32_t pt = tb + lanes_below(mt);
+                fb += (uint32_t)__popcll(mb);
+                tb += (uint32_t)__popcll(mt);
+                fpos[u] = (better && pb < ks.before) ? pb : kNone;
+                if (outbuf && fpos[u] != kNone) outbuf[pb] = e[u];
+                if (tie && pt < p.stash_cap) stash[pt] = e[u];
+            }
+            if (!outbuf) write_batch<KT, kB>(p, sg, fpos, e);
+        }
+    }
+    __syncthreads();
+    if (w != 0) return;
+
+    Cands<KT> cand;
+    cand.list = stash;
+    cand.keys_in = p.keys_in;
+    cand.begin = sg.begin;
+    cand.n = sg.n;
+    cand.nslices = ps;
+    cand.slice = slice;
+    cand.slot_info = info;
+    cand.slot_cum = slot_cum;
+    cand.slot_data = slot_data;
+    cand.slot_cap = p.stash_cap;
+    cand.bstar = ks.b;
+    cand.lds = false;
+    cand.count = 0;
+    uint32_t placed = 0;
+    if (fast) {
+        cand.lds = true;
+        cand.count = sh.ntie < p.stash_cap ? sh.ntie : p.stash_cap;
+        placed = ks.before;
+    } else {
+        // Rare: a slice lost candidates or bucket b* does not fit in LDS.
+        // Pull what fits into LDS, else leave the candidates in place.
+        const uint32_t thr = rank_thr<KT, LARGEST>(ks.b);
+        const uint32_t cap = p.stash_cap;
+        uint32_t got = 0;
+        cand.visit([&](uint32_t r, uint32_t idx, bool act) {
+            const bool keep = act && within<LARGEST>(Key<KT>::ord(r), thr);
+            const uint64_t m = __ballot(keep);
+            const uint32_t pos = got + lanes_below(m);
+            if (keep && pos < cap) stash[pos] = make_uint2(r, idx);
+            got += (uint32_t)__popcll(m);
+        });
+        wave_sync();
+        if (got <= cap) {
+            cand.lds = true;
+            cand.count = got;
+        }
+    }
+    wave_finish<KT, LARGEST>(sh.hist, outbuf, p, sg, cand, ks, placed);
+}
+
+template <int KT, bool LARGEST, int U>
+__global__ __launch_bounds__(kThreads) void topk_kernel(Params p) {
+    __shared__ Shared sh;
+    extern __shared__ uint4 dyn[];
+    uint2 *stash = reinterpret_cast<uint2 *>(dyn);  // kWaves regions of capw entries
+    uint2 *outbuf = p.out_cap ? stash + p.stash_cap : nullptr;
+    const uint32_t t = threadIdx.x;
+    const uint32_t w = t / kWave;
+    const uint32_t ln = lane_id();
+
+    const uint32_t P = p.wg_per_seg;
+    const uint32_t b = blockIdx.x;
+    const uint32_t qq = b >> 3;
+    const int64_t s = (int64_t)(qq / P) * 8 + (b & 7u);
+    const uint32_t q = qq % P;
+    if (s >= p.num_segments) return;
+
+    Seg sg;
+    sg.begin = p.offsets[s];
+    const int64_t end = p.offsets[s + 1];
+    sg.n = end > sg.begin ? (uint32_t)(end - sg.begin) : 0u;
+    sg.k_i = sg.n < p.k ? sg.n : p.k;
+    sg.row = s;
+    if (sg.k_i == 0) return;
+
+    // Workgroups that share this segment.
+    uint32_t ps = 1, slice = sg.n;
+    if (P > 1 && sg.n > p.k) {
+        uint32_t sl = (uint32_t)(((uint64_t)sg.n + P - 1) / P);
+        if (sl < p.min_slice) sl = p.min_slice;
+        sl = (sl + 255u) & ~255u;
+        ps = (uint32_t)(((uint64_t)sg.n + sl - 1) / sl);
+        slice = sl;
+    }
+    if (q >= ps) return;
+
+    if (sg.n <= p.k) {  // select-all: one wave does it
+        if (w == 0) wave_select_all<KT, LARGEST>(outbuf, p, sg);
+        return;
+    }
+
+    // ---- pass 0: each wave streams a quarter of this workgroup's keys ----
+    const uint32_t lo = q * slice;
+    const uint32_t hi = (sg.n - lo) > slice ? lo + slice : sg.n;
+    const uint32_t len = hi - lo;
+    uint32_t part = (len + kWaves - 1) / kWaves;
+    part = (part + 63u) & ~63u;
+    const uint32_t wlo = lo + (w * part < len ? w * part : len);
+    const uint32_t whi = lo + ((w + 1) * part < len ? (w + 1) * part : len);
+    const uint32_t capw = p.stash_cap / kWaves;
+    for (uint32_t i = t * 4; i < (uint32_t)kBuckets; i += 4 * kThreads)
+        *reinterpret_cast<uint4 *>(&sh.hist[i]) = make_uint4(0u, 0u, 0u, 0u);
+    if (t == 0) {
+        sh.rg = kBuckets - 1;
+    }
+    __syncthreads();
+    Share share;
+    share.rg = &sh.rg;
+    share.gearly = ps > 1 ? p.ws_early + (size_t)s * kBuckets : nullptr;
+    share.glast = ps > 1 ? p.ws_slot_cum + ((size_t)s * P + q) * kBuckets : nullptr;
+    share.wave = w;
+    const Pass0 r0 = wave_pass0<KT, LARGEST, U>(sh.hist, stash + w * capw, capw, p.keys_in,
+                                             sg.begin, wlo, whi, sg.k_i, share);
+    if (ln == 0) {
+        sh.wcount[w] = r0.count;
+        sh.wbad[w] = 0;
+        sh.wdefer[w] = r0.defer;
+    }
+    __syncthreads();
+    bool anydefer = false;
+    for (uint32_t v = 0; v < (uint32_t)kWaves; ++v) anydefer = anydefer || sh.wdefer[v] != 0;
+    if (anydefer) {
+        // Every key of the workgroup is counted now: stash the deferred
+        // chunks under the workgroup's bound (computed alike by every wave).
+        uint32_t Rf = wave_find(sh.hist, kBuckets, sg.k_i).b;
+        if (ps > 1 && sh.rg < Rf) Rf = sh.rg;
+        if (r0.defer != 0) {
+            uint32_t cnt = r0.count;
+            const bool ok = wave_reread<KT, LARGEST, U>(stash + w * capw, capw, cnt, p.keys_in,
+                                                     sg.begin, wlo, whi, r0.defer, Rf);
+            if (ln == 0) {
+                sh.wcount[w] = cnt;
+                sh.wbad[w] = ok ? 0u : 1u;
+            }
+        }
+        __syncthreads();
+    }
+    if (w != 0) {
+        // Wave 0 finishes the workgroup's work alone; with several workgroups
+        // per segment the others wait for the ticket and help the last one.
+        if (ps == 1) return;
+        __syncthreads();
+        if (!sh.last) return;
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        slice_last<KT, LARGEST>(sh, stash, outbuf, p, sg, s, P, ps, slice);
+        return;
+    }
+
+    // ---- wave 0: this workgroup's k-th bucket, then its candidates ----
+    const Kth kw = wave_find(sh.hist, kBuckets, sg.k_i);
+    uint32_t R = kw.b;  // the last bucket when the range holds fewer keys
+    // A bound shared by the segment's workgroups is valid for this slice too.
+    if (ps > 1 && sh.rg < R) R = sh.rg;
+    bool bad = false;
+    for (uint32_t v = 0; v < (uint32_t)kWaves; ++v) bad = bad || sh.wbad[v] != 0;
+    // Gather, in place, every stash entry with rank <= R (wave regions are
+    // visited in order, so writes never pass reads).
+    uint32_t ncand = 0;
+    if (!bad) {
+        const uint32_t thr = rank_thr<KT, LARGEST>(R);
+        for (uint32_t v = 0; v < (uint32_t)kWaves; ++v) {
+            const uint32_t cnt = sh.wcount[v];
+            const uint2 *src = stash + v * capw;
+            for (uint32_t base = 0; base < cnt; base += kWave) {
+                const uint32_t i = base + ln;
+                const bool act = i < cnt;
+                const uint2 e = act ? src[i] : make_uint2(0u, 0u);
+                const bool keep = act && within<LARGEST>(Key<KT>::ord(e.x), thr);
+                const uint64_t m = __ballot(keep);
+                wave_sync();
+                if (keep) stash[ncand + lanes_below(m)] = e;
+                ncand += (uint32_t)__popcll(m);
+                wave_sync();
+            }
+        }
+    }
+
+    Cands<KT> cand;
+    cand.list = stash;
+    cand.count = ncand;
+    cand.lds = !bad;
+    cand.keys_in = p.keys_in;
+    cand.begin = sg.begin;
+    cand.n = sg.n;
+    cand.nslices = 1;
+    cand.slice = sg.n;
+    cand.slot_info = nullptr;
+    cand.slot_cum = nullptr;
+    cand.slot_data = nullptr;
+    cand.slot_cap = p.stash_cap;
+    cand.bstar = 0;
+
+    if (ps == 1) {
+        wave_finish<KT, LARGEST>(sh.hist, outbuf, p, sg, cand, kw);
+        return;
+    }
+
+    // ---- several workgroups per segment: publish this slice ----
+    uint32_t *gh = p.ws_hist + (size_t)s * kBuckets;
+    uint32_t *info = p.ws_slot_info + (size_t)s * P * 4;
+    uint32_t *cum = p.ws_slot_cum + ((size_t)s * P + q) * kBuckets;
+    uint2 *slot = p.ws_slot_data + ((size_t)s * P + q) * p.stash_cap;
+    for (uint32_t i = ln; i <= R; i += kWave) {
+        const uint32_t h = sh.hist[i];
+        if (h) atomicAdd(&gh[i], h);
+    }
+    if (!bad) {
+        // Counting sort of the candidates by rank into the slot: hist becomes
+        // the exclusive prefix (a cursor per rank); after the scatter each
+        // cursor holds the number of entries with rank <= r.
+        uint32_t carry = 0;
+        for (uint32_t base = 0; base <= R; base += kWave) {
+            const uint32_t i = base + ln;
+            const uint32_t h = i <= R ? sh.hist[i] : 0u;
+            const uint32_t incl = wave_incl_sum(h);
+            if (i <= R) sh.hist[i] = carry + incl - h;
+            carry += wave_bcast(incl, kWave - 1);
+        }
+        wave_sync();
+        for (uint32_t base = 0; base < ncand; base += kWave) {
+            const uint32_t i = base + ln;
+            if (i < ncand) {
+                const uint2 e = stash[i];
+                const uint32_t pos = atomicAdd(&sh.hist[rank0<KT, LARGEST>(Key<KT>::ord(e.x))], 1u);
+                if (pos < p.stash_cap) slot[pos] = e;
+            }
+        }
+        wave_sync();
+        for (uint32_t i = ln; i <= R; i += kWave) cum[i] = sh.hist[i];
+    }
+    if (ln == 0) {
+        info[4 * q + 0] = bad ? 0u : ncand;
+        info[4 * q + 1] = bad ? 1u : 0u;
+        info[4 * q + 2] = R;
+    }
+    // Release this slice's slot, histogram and info before taking a ticket;
+    // the last arriver acquires all of them.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    uint32_t last = 0;
+    if (ln == 0) last = (atomicAdd(&p.ws_ticket[s], 1u) == ps - 1) ? 1u : 0u;
+    last = wave_bcast(last, 0);
+
+    if (ln == 0) sh.last = last;
+    __syncthreads();  // pairs with the one the other waves wait in
+    if (!last) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    slice_last<KT, LARGEST>(sh, stash, outbuf, p, sg, s, P, ps, slice);
+}
+
+// Dynamic LDS above 64 KiB has to be allowed per kernel.
+template <typename K> hipError_t allow_lds(K kernel, size_t lds) {
+    if (lds <= 64 * 1024) return hipSuccess;
+    return hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxDynLds);
+}
+
+template <int KT, bool LARGEST, int U>
+hipError_t launch_u(const Params &p, uint32_t grid, size_t lds, hipStream_t st) {
+    hipError_t e;
+    if ((e = allow_lds(topk_kernel<KT, LARGEST, U>, lds)) != hipSuccess) return e;
+    hipLaunchKernelGGL((topk_kernel<KT, LARGEST, U>), dim3(grid), dim3(kThreads), lds, st, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+template <int KT>
+hipError_t launch_topk(const Params &p, bool largest, bool split, uint32_t grid, size_t lds,
+                       hipStream_t st) {
+    if (largest)
+        return split ? launch_u<KT, true, kSplitU>(p, grid, lds, st)
+                     : launch_u<KT, true, 4>(p, grid, lds, st);
+    return split ? launch_u<KT, false, kSplitU>(p, grid, lds, st)
+                 : launch_u<KT, false, 4>(p, grid, lds, st);
+}
+
+template <int KT> int topk_per_cu(bool largest, size_t lds) {
+    const void *fn = largest ? reinterpret_cast<const void *>(topk_kernel<KT, true, kSplitU>)
+                             : reinterpret_cast<const void *>(topk_kernel<KT, false, kSplitU>);
+    if (lds > 64 * 1024)
+        (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxDynLds);
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, lds) != hipSuccess ||
+        per_cu < 1)
+        per_cu = 1;
+    return per_cu;
+}
+
+}  // namespace segtopk_impl
