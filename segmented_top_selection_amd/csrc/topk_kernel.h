@@ -65,7 +65,7 @@ template <int KT> struct Key;
 template <> struct Key<SEGTOPK_KEY_F32> {
     static constexpr int kBits = 32, kBytes = 4;
     static constexpr bool kSignMag = true;
-    __device__ __forceinline__ static uint32_t ord(uint32_t r) {
+    __host__ __device__ __forceinline__ static uint32_t ord(uint32_t r) {
         r = (r == 0x80000000u) ? 0u : r;  // -0.0 joins +0.0
         return r ^ ((uint32_t)((int32_t)r >> 31) | 0x80000000u);
     }
@@ -73,7 +73,7 @@ template <> struct Key<SEGTOPK_KEY_F32> {
 template <> struct Key<SEGTOPK_KEY_BF16> {
     static constexpr int kBits = 16, kBytes = 2;
     static constexpr bool kSignMag = true;
-    __device__ __forceinline__ static uint32_t ord(uint32_t r) {
+    __host__ __device__ __forceinline__ static uint32_t ord(uint32_t r) {
         r = (r == 0x8000u) ? 0u : r;
         return r ^ ((r & 0x8000u) ? 0xFFFFu : 0x8000u);
     }
@@ -81,7 +81,7 @@ template <> struct Key<SEGTOPK_KEY_BF16> {
 template <> struct Key<SEGTOPK_KEY_F16> {
     static constexpr int kBits = 16, kBytes = 2;
     static constexpr bool kSignMag = true;
-    __device__ __forceinline__ static uint32_t ord(uint32_t r) {
+    __host__ __device__ __forceinline__ static uint32_t ord(uint32_t r) {
         r = (r == 0x8000u) ? 0u : r;
         return r ^ ((r & 0x8000u) ? 0xFFFFu : 0x8000u);
     }
@@ -89,34 +89,30 @@ template <> struct Key<SEGTOPK_KEY_F16> {
 template <> struct Key<SEGTOPK_KEY_U32> {
     static constexpr int kBits = 32, kBytes = 4;
     static constexpr bool kSignMag = false;
-    __device__ __forceinline__ static uint32_t ord(uint32_t r) { return r; }
+    __host__ __device__ __forceinline__ static uint32_t ord(uint32_t r) { return r; }
 };
 template <> struct Key<SEGTOPK_KEY_I32> {
     static constexpr int kBits = 32, kBytes = 4;
     static constexpr bool kSignMag = false;
-    __device__ __forceinline__ static uint32_t ord(uint32_t r) { return r ^ 0x80000000u; }
+    __host__ __device__ __forceinline__ static uint32_t ord(uint32_t r) { return r ^ 0x80000000u; }
 };
 
 // Pass-0 bucket rank of an ordered key: 0 is the best bucket.
-template <int KT, bool LARGEST> __device__ __forceinline__ uint32_t rank0(uint32_t o) {
+template <int KT, bool LARGEST> __host__ __device__ __forceinline__ uint32_t rank0(uint32_t o) {
     constexpr int sh = Key<KT>::kBits - kDigit;
     const uint32_t d = o >> sh;
     return LARGEST ? (uint32_t)(kBuckets - 1) - d : d;
 }
 // Ordered-key threshold of "rank0 <= R": for MAX o >= thr, for MIN o <= thr.
-template <int KT, bool LARGEST> __device__ __forceinline__ uint32_t rank_thr(uint32_t R) {
+template <int KT, bool LARGEST> __host__ __device__ __forceinline__ uint32_t rank_thr(uint32_t R) {
     constexpr int sh = Key<KT>::kBits - kDigit;
     return LARGEST ? ((uint32_t)(kBuckets - 1) - R) << sh : (R << sh) | ((1u << sh) - 1u);
 }
-template <bool LARGEST> __device__ __forceinline__ bool within(uint32_t o, uint32_t thr) {
-    return LARGEST ? o >= thr : o <= thr;
-}
 
 // ---------------------------------------------------------------------------
-// Pre-filter of raw keys against a bucket bound "rank0 <= R", without the
-// ordered-bits transform.  Which keys pass is the same test as the exact one,
-// except that -0.0 may pass where +0.0 would not (a superset, never fewer
-// keys); the exact test follows for the keys that pass.
+// Test of raw keys against a bucket bound "rank0 <= R", without the
+// ordered-bits transform; it passes exactly the keys that pass the test on
+// the ordered bits (-0.0 with +0.0).
 //
 //  * Per chunk, each lane reduces its keys with one min or max per key
 //    (packed pairs of 16-bit keys count as one operation) in the domain in
@@ -137,11 +133,13 @@ struct Prefilter {
     uint32_t X, T2;    // single key: (x ^ X) >= T2
 };
 
-template <int KT, bool LARGEST> __device__ __forceinline__ Prefilter prefilter(uint32_t R) {
+// The test for the ordered-key threshold thr (for MAX ord >= thr passes, for
+// MIN ord <= thr).
+template <int KT, bool LARGEST>
+__host__ __device__ __forceinline__ Prefilter prefilter_thr(uint32_t thr) {
     constexpr int B = Key<KT>::kBits;
     constexpr uint32_t H = 1u << (B - 1);
     constexpr uint32_t M = B == 32 ? 0xFFFFFFFFu : 0xFFFFu;
-    const uint32_t thr = rank_thr<KT, LARGEST>(R);
     uint32_t mode, T;
     if constexpr (KT == SEGTOPK_KEY_U32) {
         mode = LARGEST ? kPfMaxU : kPfMinU;
@@ -153,7 +151,7 @@ template <int KT, bool LARGEST> __device__ __forceinline__ Prefilter prefilter(u
         // ord >= thr.  thr > H: positive keys with bits >= thr - H.  Else
         // every positive key and the negative keys with bits <= ~thr; a
         // bound of exactly +0.0 is widened by one step so that -0.0 (which
-        // ord puts at H) passes with it.
+        // ord puts at H) passes with it, and nothing else.
         if (thr > H) {
             mode = kPfMaxS;
             T = thr - H;
@@ -164,28 +162,39 @@ template <int KT, bool LARGEST> __device__ __forceinline__ Prefilter prefilter(u
     } else {
         // ord <= thr.  thr >= H: every negative key (and -0.0) and the
         // positive keys with bits <= thr - H.  Else the negative keys with
-        // bits >= ~thr.
+        // bits >= ~thr, except -0.0 (bits H), which ord puts at H: no key has
+        // ord H - 1, so a bound there is taken as "bits >= H + 1".
         if (thr >= H) {
             mode = kPfMinS;
             T = thr - H;
         } else {
             mode = kPfMaxU;
-            T = ~thr & M;
+            T = thr == H - 1u ? H + 1u : ~thr & M;
         }
     }
     Prefilter f;
-    f.mode = __builtin_amdgcn_readfirstlane(mode);
-    f.T = __builtin_amdgcn_readfirstlane(T & M);
+    f.mode = mode;
+    f.T = T & M;
     // Signed tests become unsigned ones by flipping the sign bit; "<=" tests
     // become ">=" ones by complementing both sides.
     const uint32_t flip = (mode == kPfMaxS || mode == kPfMinS) ? H : 0u;
     const uint32_t neg = (mode == kPfMinU || mode == kPfMinS) ? M : 0u;
-    f.X = __builtin_amdgcn_readfirstlane(flip ^ neg);
-    f.T2 = __builtin_amdgcn_readfirstlane(((T & M) ^ flip) ^ neg);
+    f.X = flip ^ neg;
+    f.T2 = (f.T ^ flip) ^ neg;
     return f;
 }
 
-__device__ __forceinline__ bool pf_key(const Prefilter &f, uint32_t x) { return (x ^ f.X) >= f.T2; }
+// The test for "rank0 <= R", its fields in scalar registers.
+template <int KT, bool LARGEST> __device__ __forceinline__ Prefilter prefilter(uint32_t R) {
+    Prefilter f = prefilter_thr<KT, LARGEST>(rank_thr<KT, LARGEST>(R));
+    f.mode = __builtin_amdgcn_readfirstlane(f.mode);
+    f.T = __builtin_amdgcn_readfirstlane(f.T);
+    f.X = __builtin_amdgcn_readfirstlane(f.X);
+    f.T2 = __builtin_amdgcn_readfirstlane(f.T2);
+    return f;
+}
+
+__host__ __device__ __forceinline__ bool pf_key(const Prefilter &f, uint32_t x) { return (x ^ f.X) >= f.T2; }
 
 typedef short pf_s16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned short pf_u16x2 __attribute__((ext_vector_type(2)));
@@ -193,7 +202,7 @@ typedef unsigned short pf_u16x2 __attribute__((ext_vector_type(2)));
 // Reduction of N dwords by op with four interleaved accumulators (enough
 // independent operations in flight, few extra registers).
 template <class T, int N, class Op>
-__device__ __forceinline__ T pf_tree(const uint32_t (&d)[N], Op op) {
+__host__ __device__ __forceinline__ T pf_tree(const uint32_t (&d)[N], Op op) {
     constexpr int A = N < 4 ? N : 4;
     T acc[A];
 #pragma unroll
@@ -210,7 +219,7 @@ __device__ __forceinline__ T pf_tree(const uint32_t (&d)[N], Op op) {
 // Whether any of a lane's keys (N dwords, every key slot valid or zero) can
 // be within the bound.  Zero slots past the end of a range may pass.
 template <int KT, int N>
-__device__ __forceinline__ bool pf_chunk(const Prefilter &f, const uint32_t (&d)[N]) {
+__host__ __device__ __forceinline__ bool pf_chunk(const Prefilter &f, const uint32_t (&d)[N]) {
     if constexpr (Key<KT>::kBytes == 4) {
         switch (f.mode) {
         case kPfMaxS:
@@ -512,14 +521,14 @@ struct Pass0 {
 
 // Drops, in place, the stash entries whose pass-0 rank is beyond the bound.
 template <int KT, bool LARGEST>
-__device__ __forceinline__ uint32_t wave_compact(uint2 *stash, uint32_t cnt, uint32_t thr) {
+__device__ __forceinline__ uint32_t wave_compact(uint2 *stash, uint32_t cnt, const Prefilter &pf) {
     const uint32_t ln = lane_id();
     uint32_t out = 0;
     for (uint32_t base = 0; base < cnt; base += kWave) {
         const uint32_t i = base + ln;
         const bool act = i < cnt;
         const uint2 e = act ? stash[i] : make_uint2(0u, 0u);
-        const bool keep = act && within<LARGEST>(Key<KT>::ord(e.x), thr);
+        const bool keep = act && pf_key(pf, e.x);
         const uint64_t m = __ballot(keep);
         wave_sync();  // this round's reads come before its writes
         if (keep) stash[out + lanes_below(m)] = e;
@@ -539,7 +548,7 @@ __device__ __forceinline__ bool wave_push(uint2 *stash, uint32_t cap, uint32_t &
     if (n == 0) return true;
     if (count + n > cap) {
         wave_sync();
-        count = wave_compact<KT, LARGEST>(stash, count, rank_thr<KT, LARGEST>(R));
+        count = wave_compact<KT, LARGEST>(stash, count, prefilter<KT, LARGEST>(R));
         if (count + n > cap) return false;
     }
     if (ex) stash[count + lanes_below(m)] = make_uint2(x, idx);
@@ -650,16 +659,13 @@ __device__ __forceinline__ Pass0 wave_pass0(uint32_t *hist, uint2 *stash, uint32
             pf = prefilter<KT, LARGEST>(r.R);
             // Stash this chunk's keys within the bound from the registers,
             // if they fit; earlier chunks stay deferred.
-            const uint32_t thr2 = rank_thr<KT, LARGEST>(r.R);
-            const bool sin = s0 && within<LARGEST>(Key<KT>::ord(sx), thr2);
+            const bool sin = s0 && pf_key(pf, sx);
             uint32_t cnt = sin ? 1u : 0u;
 #pragma unroll
             for (int u = 0; u < Rg::kU; ++u)
 #pragma unroll
                 for (int e = 0; e < V; ++e)
-                    cnt += (cv[u] != kNone &&
-                            within<LARGEST>(Key<KT>::ord(Rg::key_at(cur, u * V + e)), thr2))
-                               ? 1u : 0u;
+                    cnt += (cv[u] != kNone && pf_key(pf, Rg::key_at(cur, u * V + e))) ? 1u : 0u;
             const uint32_t incl = wave_incl_sum(cnt);
             const uint32_t total = wave_bcast(incl, kWave - 1);
             if (r.count + total > cap) continue;  // the stash is empty: defer the chunk
@@ -670,7 +676,7 @@ __device__ __forceinline__ Pass0 wave_pass0(uint32_t *hist, uint2 *stash, uint32
 #pragma unroll
                 for (int e = 0; e < V; ++e) {
                     const uint32_t x = Rg::key_at(cur, u * V + e);
-                    if (cv[u] != kNone && within<LARGEST>(Key<KT>::ord(x), thr2))
+                    if (cv[u] != kNone && pf_key(pf, x))
                         stash[pos++] = make_uint2(x, cv[u] + (uint32_t)e);
                 }
             r.count += total;
@@ -734,15 +740,13 @@ __device__ __forceinline__ bool wave_reread(uint2 *stash, uint32_t cap, uint32_t
     const uint32_t ln = lane_id();
     Rg L;
     L.init(keys, begin, lo, hi);
-    const uint32_t thr = rank_thr<KT, LARGEST>(R);
     const Prefilter pf = prefilter<KT, LARGEST>(R);
     bool ok;
     {
         const bool sv = ln < L.nscalar;
         const uint32_t si = sv ? L.scalar_idx(ln) : 0u;
         const uint32_t x = sv ? L.load_scalar(si) : 0u;
-        ok = wave_push<KT, LARGEST>(stash, cap, count, R,
-                                    sv && within<LARGEST>(Key<KT>::ord(x), thr), x, si);
+        ok = wave_push<KT, LARGEST>(stash, cap, count, R, sv && pf_key(pf, x), x, si);
     }
     const uint32_t nre = defer < L.nchunks ? defer : L.nchunks;
     uint32_t raw[K], vidx[Rg::kU];
@@ -763,8 +767,7 @@ __device__ __forceinline__ bool wave_reread(uint2 *stash, uint32_t cap, uint32_t
             for (int e = 0; e < V; ++e) {
                 const uint32_t x = Rg::key_at(cur, u * V + e);
                 if (ok)
-                    ok = wave_push<KT, LARGEST>(stash, cap, count, R,
-                                                cv[u] != kNone && within<LARGEST>(Key<KT>::ord(x), thr),
+                    ok = wave_push<KT, LARGEST>(stash, cap, count, R, cv[u] != kNone && pf_key(pf, x),
                                                 x, cv[u] + (uint32_t)e);
             }
     }
@@ -895,11 +898,94 @@ __device__ __forceinline__ void wave_bitonic(uint2 *buf, uint32_t cnt) {
     }
 }
 
+// x of lane (l ^ M), for a constant M: DPP quad permutes for 1 and 2, DPP row
+// shifts limited to the receiving banks for 4 and 8, and the permlane swaps
+// of gfx950 for 16 and 32 -- no trip through the LDS crossbar.
+template <int M> __device__ __forceinline__ uint32_t lane_xor(uint32_t x) {
+    if constexpr (M == 1) {
+        return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
+    } else if constexpr (M == 2) {
+        return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
+    } else if constexpr (M == 4) {
+        const int t = __builtin_amdgcn_update_dpp((int)x, (int)x, 0x104, 0xF, 0x5, false);  // row_shl:4
+        return (uint32_t)__builtin_amdgcn_update_dpp(t, (int)x, 0x114, 0xF, 0xA, false);   // row_shr:4
+    } else if constexpr (M == 8) {
+        const int t = __builtin_amdgcn_update_dpp((int)x, (int)x, 0x108, 0xF, 0x3, false);  // row_shl:8
+        return (uint32_t)__builtin_amdgcn_update_dpp(t, (int)x, 0x118, 0xF, 0xC, false);   // row_shr:8
+    } else if constexpr (M == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+        return (lane_id() & 16u) ? r[0] : r[1];
+    } else {
+        static_assert(M == 32, "lane_xor: M must be a power of two below 64");
+        const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+        return (lane_id() & 32u) ? r[0] : r[1];
+    }
+}
+
+// One compare-exchange step (block SIZE, distance STRIDE) of a bitonic sort
+// of 64*E register entries, lane l holding entries l*E .. l*E+E-1, ascending
+// by (sk, id); rw and vv ride along.
+template <int E, int SIZE, int STRIDE>
+__device__ __forceinline__ void bitonic_step(uint32_t (&sk)[E], uint32_t (&id)[E], uint32_t (&rw)[E],
+                                             uint32_t (&vv)[E]) {
+    const uint32_t ln = lane_id();
+    if constexpr (STRIDE >= E) {
+        constexpr int LM = STRIDE / E;
+        const bool lower = ((ln * E) & STRIDE) == 0;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const uint32_t j = ln * E + e;
+            const uint32_t psk = lane_xor<LM>(sk[e]);
+            const uint32_t pid = lane_xor<LM>(id[e]);
+            const uint32_t prw = lane_xor<LM>(rw[e]);
+            const uint32_t pvv = lane_xor<LM>(vv[e]);
+            const bool asc = (j & SIZE) == 0;
+            const bool pfirst = psk < sk[e] || (psk == sk[e] && pid < id[e]);
+            if ((lower == asc) ? pfirst : !pfirst) {
+                sk[e] = psk;
+                id[e] = pid;
+                rw[e] = prw;
+                vv[e] = pvv;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            if (e & STRIDE) continue;
+            const int f = e | STRIDE;
+            const uint32_t j = ln * E + e;
+            const bool asc = (j & SIZE) == 0;
+            const bool ffirst = sk[f] < sk[e] || (sk[f] == sk[e] && id[f] < id[e]);
+            if (ffirst == asc) {
+                uint32_t t0 = sk[e]; sk[e] = sk[f]; sk[f] = t0;
+                t0 = id[e]; id[e] = id[f]; id[f] = t0;
+                t0 = rw[e]; rw[e] = rw[f]; rw[f] = t0;
+                t0 = vv[e]; vv[e] = vv[f]; vv[f] = t0;
+            }
+        }
+    }
+}
+
+template <int E, int SIZE, int STRIDE>
+__device__ __forceinline__ void bitonic_merge(uint32_t (&sk)[E], uint32_t (&id)[E], uint32_t (&rw)[E],
+                                              uint32_t (&vv)[E]) {
+    bitonic_step<E, SIZE, STRIDE>(sk, id, rw, vv);
+    if constexpr (STRIDE > 1) bitonic_merge<E, SIZE, STRIDE / 2>(sk, id, rw, vv);
+}
+
+// Bitonic sort of all 64*E entries, blocks of SIZE and up (call with SIZE 2).
+template <int E, int SIZE>
+__device__ __forceinline__ void bitonic_regs(uint32_t (&sk)[E], uint32_t (&id)[E], uint32_t (&rw)[E],
+                                             uint32_t (&vv)[E]) {
+    bitonic_merge<E, SIZE, SIZE / 2>(sk, id, rw, vv);
+    if constexpr (SIZE < kWave * E) bitonic_regs<E, SIZE * 2>(sk, id, rw, vv);
+}
+
 // Output of up to 64*E staged results held in registers, E per lane (lane l
 // holds results l*E .. l*E+E-1).  The values are gathered first so their
 // latency overlaps the sort; sorted output is a bitonic network on
-// (key best-first, index ascending) using lane shuffles for strides of E and
-// more and register swaps below that.
+// (key best-first, index ascending) using lane exchanges for strides of E
+// and more and register swaps below that.
 // Sorts list[0, m) (m <= 64 * E, E entries per lane, in registers) best
 // first, ties by ascending index, and writes the first k_i to the row: the
 // sort is both the selection and the output order.  With prefer_larger_index
@@ -927,47 +1013,7 @@ __device__ __forceinline__ void sort_select(const uint2 *list, uint32_t m, const
             if (p.vals_in) vv[e] = x.y < sg.n ? p.vals_in[sg.begin + x.y] : kNone;
         }
     }
-    if (p.sorted || m > sg.k_i) {
-        for (uint32_t size = 2; size <= (uint32_t)(kWave * E); size <<= 1) {
-            for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
-                if (stride >= (uint32_t)E) {
-                    const int lm = (int)(stride / E);
-#pragma unroll
-                    for (int e = 0; e < E; ++e) {
-                        const uint32_t j = ln * E + e;
-                        const uint32_t psk = __shfl_xor(sk[e], lm, kWave);
-                        const uint32_t pid = __shfl_xor(id[e], lm, kWave);
-                        const uint32_t prw = __shfl_xor(rw[e], lm, kWave);
-                        const uint32_t pvv = __shfl_xor(vv[e], lm, kWave);
-                        const bool asc = (j & size) == 0;
-                        const bool lower = (j & stride) == 0;
-                        const bool pfirst = psk < sk[e] || (psk == sk[e] && pid < id[e]);
-                        if ((lower == asc) ? pfirst : !pfirst) {
-                            sk[e] = psk;
-                            id[e] = pid;
-                            rw[e] = prw;
-                            vv[e] = pvv;
-                        }
-                    }
-                } else {
-#pragma unroll
-                    for (int e = 0; e < E; ++e) {
-                        if (e & stride) continue;
-                        const int f = e | (int)stride;
-                        const uint32_t j = ln * E + e;
-                        const bool asc = (j & size) == 0;
-                        const bool ffirst = sk[f] < sk[e] || (sk[f] == sk[e] && id[f] < id[e]);
-                        if (ffirst == asc) {
-                            uint32_t t0 = sk[e]; sk[e] = sk[f]; sk[f] = t0;
-                            t0 = id[e]; id[e] = id[f]; id[f] = t0;
-                            t0 = rw[e]; rw[e] = rw[f]; rw[f] = t0;
-                            t0 = vv[e]; vv[e] = vv[f]; vv[f] = t0;
-                        }
-                    }
-                }
-            }
-        }
-    }
+    if (p.sorted || m > sg.k_i) bitonic_regs<E, 2>(sk, id, rw, vv);
     // Output position of sorted position j: j itself, except that with
     // prefer_larger_index the group [a, b) of entries equal to the k_i-th
     // keeps its last k_i - a members, moved down to [a, k_i).
@@ -1342,11 +1388,11 @@ __device__ __forceinline__ void slice_last(Shared &sh, uint2 *stash, uint2 *outb
     } else {
         // Rare: a slice lost candidates or bucket b* does not fit in LDS.
         // Pull what fits into LDS, else leave the candidates in place.
-        const uint32_t thr = rank_thr<KT, LARGEST>(ks.b);
+        const Prefilter pf = prefilter<KT, LARGEST>(ks.b);
         const uint32_t cap = p.stash_cap;
         uint32_t got = 0;
         cand.visit([&](uint32_t r, uint32_t idx, bool act) {
-            const bool keep = act && within<LARGEST>(Key<KT>::ord(r), thr);
+            const bool keep = act && pf_key(pf, r);
             const uint64_t m = __ballot(keep);
             const uint32_t pos = got + lanes_below(m);
             if (keep && pos < cap) stash[pos] = make_uint2(r, idx);
@@ -1470,7 +1516,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(Params p) {
     // visited in order, so writes never pass reads).
     uint32_t ncand = 0;
     if (!bad) {
-        const uint32_t thr = rank_thr<KT, LARGEST>(R);
+        const Prefilter pf = prefilter<KT, LARGEST>(R);
         for (uint32_t v = 0; v < (uint32_t)kWaves; ++v) {
             const uint32_t cnt = sh.wcount[v];
             const uint2 *src = stash + v * capw;
@@ -1478,7 +1524,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(Params p) {
                 const uint32_t i = base + ln;
                 const bool act = i < cnt;
                 const uint2 e = act ? src[i] : make_uint2(0u, 0u);
-                const bool keep = act && within<LARGEST>(Key<KT>::ord(e.x), thr);
+                const bool keep = act && pf_key(pf, e.x);
                 const uint64_t m = __ballot(keep);
                 wave_sync();
                 if (keep) stash[ncand + lanes_below(m)] = e;

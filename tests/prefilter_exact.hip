@@ -1,0 +1,107 @@
+// Host check of the raw-bit bound test used by the top-k kernels: for every
+// key type and direction, the test built for a bucket bound passes exactly
+// the keys whose order-preserving bits are within the bound (-0.0 counted as
+// +0.0), and the per-lane chunk reduction passes exactly when one of the
+// chunk's keys does.  16-bit keys: every bit pattern against every pass-0
+// bound; 32-bit keys: boundary patterns plus seeded random ones.  Built
+// host-only; prints the number of mismatches and exits non-zero on any.
+#include "../segmented_top_selection_amd/csrc/topk_kernel.h"
+
+#include <cstdio>
+#include <random>
+#include <vector>
+
+using namespace segtopk_impl;
+
+static long g_bad = 0;
+
+template <int KT, bool LARGEST>
+static void check(const std::vector<uint32_t> &keys, const std::vector<uint32_t> &thrs,
+                  const char *name) {
+    long bad = 0, pass = 0;
+    for (uint32_t thr : thrs) {
+        const Prefilter f = prefilter_thr<KT, LARGEST>(thr);
+        for (uint32_t x : keys) {
+            const uint32_t o = Key<KT>::ord(x);
+            const bool want = LARGEST ? o >= thr : o <= thr;
+            const bool got = pf_key(f, x);
+            pass += want;
+            if (got != want) {
+                if (bad < 5)
+                    std::printf("  %s %s thr=%08x key=%08x want=%d got=%d\n", name,
+                                LARGEST ? "max" : "min", thr, x, want, got);
+                ++bad;
+            }
+        }
+    }
+    // Chunk reduction: 16 dwords (32 16-bit keys or 16 32-bit keys), random
+    // draws from the key set; it passes exactly when some key passes.
+    std::mt19937 rng(7);
+    std::uniform_int_distribution<size_t> pick(0, keys.size() - 1);
+    for (uint32_t thr : thrs) {
+        const Prefilter f = prefilter_thr<KT, LARGEST>(thr);
+        for (int rep = 0; rep < 8; ++rep) {
+            uint32_t d[16];
+            bool any = false;
+            for (int j = 0; j < 16; ++j) {
+                uint32_t a = keys[pick(rng)], b = keys[pick(rng)];
+                if (Key<KT>::kBytes == 2) {
+                    d[j] = (a & 0xFFFFu) | (b << 16);
+                    any = any || pf_key(f, a & 0xFFFFu) || pf_key(f, b & 0xFFFFu);
+                } else {
+                    d[j] = a;
+                    any = any || pf_key(f, a);
+                }
+            }
+            if (pf_chunk<KT>(f, d) != any) {
+                if (bad < 5)
+                    std::printf("  %s %s thr=%08x chunk reduction mismatch\n", name,
+                                LARGEST ? "max" : "min", thr);
+                ++bad;
+            }
+        }
+    }
+    std::printf("%-4s %s: %zu thresholds x %zu keys, %ld passing, %ld mismatches\n", name,
+                LARGEST ? "max" : "min", thrs.size(), keys.size(), pass, bad);
+    g_bad += bad;
+}
+
+template <int KT> static void run(const std::vector<uint32_t> &keys, const char *name) {
+    constexpr uint32_t H = 1u << (Key<KT>::kBits - 1);
+    std::vector<uint32_t> tmax, tmin;
+    for (uint32_t R = 0; R < (uint32_t)kBuckets; ++R) {
+        tmax.push_back(rank_thr<KT, true>(R));
+        tmin.push_back(rank_thr<KT, false>(R));
+    }
+    // Thresholds next to zero, whatever the digit width.
+    for (uint32_t t : {H - 2u, H - 1u, H, H + 1u, H + 2u, 0u, 1u, 2u * H - 1u}) {
+        tmax.push_back(t);
+        tmin.push_back(t);
+    }
+    check<KT, true>(keys, tmax, name);
+    check<KT, false>(keys, tmin, name);
+}
+
+int main() {
+    std::vector<uint32_t> k16;
+    for (uint32_t x = 0; x < 65536u; ++x) k16.push_back(x);
+    std::vector<uint32_t> k32 = {0x00000000u, 0x80000000u, 0x00000001u, 0x80000001u, 0x007FFFFFu,
+                                 0x807FFFFFu, 0x00800000u, 0x80800000u, 0x3F800000u, 0xBF800000u,
+                                 0x7F7FFFFFu, 0xFF7FFFFFu, 0x7F800000u, 0xFF800000u, 0x7FFFFFFFu,
+                                 0xFFFFFFFFu, 0x7FC00000u, 0xFFC00000u, 0x40000000u, 0xC0000000u};
+    std::mt19937 rng(1234);
+    for (int i = 0; i < 4000; ++i) k32.push_back((uint32_t)rng());
+    // Patterns on and next to every 11-bit bucket boundary.
+    for (uint32_t b = 0; b < 2048u; ++b) {
+        const uint32_t base = b << 21;
+        for (uint32_t d : {0u, 1u, (1u << 21) - 1u}) k32.push_back(base + d);
+        k32.push_back(base - 1u);
+    }
+    run<SEGTOPK_KEY_BF16>(k16, "bf16");
+    run<SEGTOPK_KEY_F16>(k16, "f16");
+    run<SEGTOPK_KEY_F32>(k32, "f32");
+    run<SEGTOPK_KEY_U32>(k32, "u32");
+    run<SEGTOPK_KEY_I32>(k32, "i32");
+    std::printf("total mismatches: %ld\n", g_bad);
+    return g_bad != 0;
+}

@@ -188,6 +188,64 @@ def test_edge_sizes_all_modes(key_type):
                           values_are="position")
 
 
+# ---------------------------------------------------------------------------
+# Batches of many segments (the plans with one wave per segment for small k
+# and one workgroup per segment for larger k): mixed sizes from empty to well
+# past the stash, negative sizes, unaligned starts, tied levels.
+# ---------------------------------------------------------------------------
+def _many_segments(seed, count=2048):
+    rng = np.random.default_rng(seed)
+    pool = [0, 1, 2, 31, 32, 33, 64, 65, 127, 128, 129, 300, 1000, 1023, 1025, 4096, 4097,
+            7777, 16384, -3]
+    sizes = rng.choice(pool, size=count)
+    off = [5]
+    for s_ in sizes:
+        off.append(off[-1] + int(s_))
+    return torch.tensor(off, dtype=torch.int64, device=DEV), max(off) + 3
+
+
+@pytest.mark.parametrize("key_type", KEY_TYPES)
+def test_many_segments_all_modes(key_type):
+    g = torch.Generator(device=DEV)
+    g.manual_seed(77)
+    off, total = _many_segments(11)
+    vals = torch.arange(total, dtype=torch.int32, device=DEV)
+    say(f"[many segments {key_type}] segments={off.numel() - 1} keys={total}")
+    for levels in (None, 5):
+        keys = random_keys(total, key_type, g, levels)
+        modes = MODES if levels else [MODES[0], MODES[4]]
+        orderings = ORDERINGS if levels else ["unsorted", "stable_sorted"]
+        for k in (33, 200):
+            for largest in (True, False):
+                for det, tb in modes:
+                    for ordering in orderings:
+                        check(keys, vals, off, k, key_type, largest, det, tb, ordering,
+                              values_are="position")
+        check(keys, vals, off, 1, key_type, True, "gpu_to_gpu", "prefer_smaller_index",
+              "stable_sorted", values_are="position")
+
+
+def test_many_segments_keys_only_and_ties():
+    g = torch.Generator(device=DEV)
+    g.manual_seed(78)
+    off, total = _many_segments(12, count=2500)
+    say(f"[many segments, ties, keys only] segments={off.numel() - 1} keys={total}")
+    x = np.zeros(total)
+    rng = np.random.default_rng(5)
+    r = rng.random(total)
+    x[r < 0.3] = -0.0
+    x[(r >= 0.3) & (r < 0.35)] = np.inf
+    x[(r >= 0.35) & (r < 0.4)] = -np.inf
+    lv = (r >= 0.4)
+    x[lv] = rng.integers(-4, 5, int(lv.sum())) * 0.25
+    keys = torch.tensor(x).float().to(DEV)
+    for k in (16, 100):
+        for largest in (True, False):
+            for det, tb in MODES:
+                for ordering in ("unsorted", "stable_sorted"):
+                    check(keys, None, off, k, "f32", largest, det, tb, ordering)
+
+
 @pytest.mark.parametrize("key_type", ["f32", "bf16"])
 def test_keys_only(key_type):
     g = torch.Generator(device=DEV)
