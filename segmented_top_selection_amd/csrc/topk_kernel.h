@@ -412,6 +412,7 @@ template <int KT, int NT, int U> struct Range {
     static constexpr int kKpt = kU * kVec;    // keys per thread per chunk
     static constexpr int kDw = kU * 4;        // dwords per thread per chunk
     static constexpr uint32_t kChunkVecs = NT * kU;
+    static constexpr uint32_t kChunkKeys = kChunkVecs * kVec;  // keys per chunk (all threads)
 
     const unsigned char *ebase;  // element 0 of the segment
     const uint4 *vbase;          // first aligned vector of the range
@@ -1251,6 +1252,7 @@ struct alignas(16) Shared {
     uint32_t wdefer[kWaves];
     uint32_t rg;
     uint32_t last, total, any_bad, nfront, ntie;  // the last arriver's state
+    uint32_t ncand;                               // candidates listed (one-chunk segments)
 };
 
 // The last workgroup of a segment to finish pass 0, all four waves: the
@@ -1407,8 +1409,91 @@ __device__ __forceinline__ void slice_last(Shared &sh, uint2 *stash, uint2 *outb
     wave_finish<KT, LARGEST>(sh.hist, outbuf, p, sg, cand, ks, placed);
 }
 
+// A segment of one chunk per wave (each wave's quarter [wlo, whi) fits one
+// chunk of U loads per lane): the keys stay in registers; every key is
+// counted, every wave finds the exact k-th bucket in the finished histogram,
+// and pushes its keys in or before that bucket straight into one candidate
+// list (their number is known from the histogram); wave 0 finishes.  Waves
+// 1..3 return after the last workgroup barrier.
 template <int KT, bool LARGEST, int U>
-__global__ __launch_bounds__(kThreads) void topk_kernel(Params p) {
+__device__ __forceinline__ void small_block(Shared &sh, uint2 *stash, uint2 *outbuf, const Params &p,
+                                            const Seg &sg, uint32_t wlo, uint32_t whi) {
+    using Rg = WaveRange<KT, U>;
+    constexpr int V = Rg::kVec;
+    const uint32_t t = threadIdx.x;
+    const uint32_t w = t / kWave;
+    const uint32_t ln = lane_id();
+    Rg L;
+    L.init(p.keys_in, sg.begin, wlo, whi);
+    uint32_t raw[Rg::kDw], vidx[Rg::kU];
+    L.template load_chunk<true>(0, ln, raw, vidx);  // in flight during the clear
+    const bool sv = ln < L.nscalar;
+    const uint32_t si = sv ? L.scalar_idx(ln) : 0u;
+    const uint32_t sx = sv ? L.load_scalar(si) : 0u;
+    for (uint32_t i = t * 4; i < (uint32_t)kBuckets; i += 4 * kThreads)
+        *reinterpret_cast<uint4 *>(&sh.hist[i]) = make_uint4(0u, 0u, 0u, 0u);
+    if (t == 0) sh.ncand = 0;
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < Rg::kU; ++u)
+#pragma unroll
+        for (int e = 0; e < V; ++e)
+            if (vidx[u] != kNone)
+                atomicAdd(&sh.hist[rank0<KT, LARGEST>(Key<KT>::ord(Rg::key_at(raw, u * V + e)))], 1u);
+    if (sv) atomicAdd(&sh.hist[rank0<KT, LARGEST>(Key<KT>::ord(sx))], 1u);
+    __syncthreads();
+    const Kth kw = wave_find(sh.hist, kBuckets, sg.k_i);  // alike in every wave
+    const bool fits = kw.before + kw.count <= p.stash_cap;
+    if (fits) {
+        const Prefilter pf = prefilter<KT, LARGEST>(kw.b);
+        const bool sin = sv && pf_key(pf, sx);
+        uint32_t c = sin ? 1u : 0u;
+#pragma unroll
+        for (int u = 0; u < Rg::kU; ++u)
+#pragma unroll
+            for (int e = 0; e < V; ++e)
+                c += (vidx[u] != kNone && pf_key(pf, Rg::key_at(raw, u * V + e))) ? 1u : 0u;
+        const uint32_t incl = wave_incl_sum(c);
+        const uint32_t total = wave_bcast(incl, kWave - 1);
+        uint32_t base = 0;
+        if (ln == 0 && total) base = atomicAdd(&sh.ncand, total);
+        uint32_t pos = wave_bcast(base, 0) + incl - c;
+        if (sin) stash[pos++] = make_uint2(sx, si);
+#pragma unroll
+        for (int u = 0; u < Rg::kU; ++u)
+#pragma unroll
+            for (int e = 0; e < V; ++e) {
+                const uint32_t x = Rg::key_at(raw, u * V + e);
+                if (vidx[u] != kNone && pf_key(pf, x)) stash[pos++] = make_uint2(x, vidx[u] + (uint32_t)e);
+            }
+    }
+    __syncthreads();
+    if (w != 0) return;
+    Cands<KT> cand;
+    cand.list = stash;
+    cand.count = fits ? sh.ncand : 0u;
+    cand.lds = fits;  // else the passes read the segment again
+    cand.keys_in = p.keys_in;
+    cand.begin = sg.begin;
+    cand.n = sg.n;
+    cand.nslices = 1;
+    cand.slice = sg.n;
+    cand.slot_info = nullptr;
+    cand.slot_cum = nullptr;
+    cand.slot_data = nullptr;
+    cand.slot_cap = p.stash_cap;
+    cand.bstar = 0;
+    wave_finish<KT, LARGEST>(sh.hist, outbuf, p, sg, cand, kw);
+}
+
+// Waves per SIMD the kernel is built for: 5 (at most 102 VGPRs) for 32-bit
+// keys and 4 for 16-bit keys with 4 loads per lane; 3 and 2 with 8.
+template <int KT, int U> constexpr int topk_waves() {
+    return U == 4 ? (Key<KT>::kBytes == 4 ? 5 : 4) : (Key<KT>::kBytes == 4 ? 3 : 2);
+}
+
+template <int KT, bool LARGEST, int U>
+__global__ __launch_bounds__(kThreads, (topk_waves<KT, U>())) void topk_kernel(Params p) {
     __shared__ Shared sh;
     extern __shared__ uint4 dyn[];
     uint2 *stash = reinterpret_cast<uint2 *>(dyn);  // kWaves regions of capw entries
@@ -1457,6 +1542,10 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(Params p) {
     const uint32_t wlo = lo + (w * part < len ? w * part : len);
     const uint32_t whi = lo + ((w + 1) * part < len ? (w + 1) * part : len);
     const uint32_t capw = p.stash_cap / kWaves;
+    if (ps == 1 && part <= WaveRange<KT, U>::kChunkKeys) {
+        small_block<KT, LARGEST, U>(sh, stash, outbuf, p, sg, wlo, whi);
+        return;
+    }
     for (uint32_t i = t * 4; i < (uint32_t)kBuckets; i += 4 * kThreads)
         *reinterpret_cast<uint4 *>(&sh.hist[i]) = make_uint4(0u, 0u, 0u, 0u);
     if (t == 0) {
