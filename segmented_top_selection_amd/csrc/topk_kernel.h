@@ -307,16 +307,21 @@ struct Kth {
 // crosses the target, then the lanes take one bucket each of that run.
 // hist may be filled concurrently by other waves: every count read is at most
 // the final count, so the bucket found is at or after the final one.
+// The runs are 4..32 buckets (a power of two); lane l reads its 16-byte
+// pieces starting at piece l mod (run / 4), so that each read instruction
+// spreads the wave over all LDS banks (runs are a multiple of 128 bytes
+// apart, which would put every lane on the same banks).
 __device__ __forceinline__ Kth wave_find(const uint32_t *hist, uint32_t nb, uint32_t target) {
     const uint32_t ln = lane_id();
     uint32_t per = (nb + 63u) >> 6;
-    per = (per + 3u) & ~3u;  // 4 .. 32 buckets per lane
+    per = per <= 4u ? 4u : (per <= 8u ? 8u : (per <= 16u ? 16u : 32u));
     const uint32_t b0 = ln * per;
+    const uint32_t pieces = per >> 2;
     uint32_t s = 0;
 #pragma unroll
-    for (uint32_t q = 0; q < 32; q += 4) {
-        const uint32_t b = b0 + q;
-        if (q < per && b < nb) {
+    for (uint32_t q = 0; q < 8; ++q) {
+        const uint32_t b = b0 + 4u * ((q + ln) & (pieces - 1u));
+        if (q < pieces && b < nb) {
             const uint4 h = *reinterpret_cast<const uint4 *>(&hist[b]);
             s += h.x + (b + 1 < nb ? h.y : 0u) + (b + 2 < nb ? h.z : 0u) + (b + 3 < nb ? h.w : 0u);
         }
