@@ -89,25 +89,37 @@ def measure(name, steps, warmup, stream_rotate=True):
         step(i)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    # Whole-job rate: `steps` back-to-back calls between two events.
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    ev[0].record(stream)
+    e0.record(stream)
     for i in range(steps):
         step(warmup + i)
-        ev[i + 1].record(stream)
+    e1.record(stream)
+    enqueue_s = time.perf_counter() - t0
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]  # ms
-    total_ms = ev[0].elapsed_time(ev[steps])
+    total_ms = e0.elapsed_time(e1)
     ms = total_ms / steps
     t = ms / 1e3
+    # Launch duration: events right before and after each call, same stream.
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for i in range(steps):
+        evs[i][0].record(stream)
+        step(warmup + steps + i)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    per = [a.elapsed_time(b) for a, b in evs]  # ms
     bytes_roof = N * (sk + sv) + KK * (sk + sv)          # metric's single-read roofline
     bytes_alg = N * sk + KK * sv + KK * (sk + sv)         # what the method must move
     res = dict(
         workload=name, segments=s, keys=N, k=w["k"], key_type=w["key_type"],
         mode=f"{'Max' if w['largest'] else 'Min'}{'Pairs' if vals is not None else 'Keys'} "
              f"{w['determinism']}/{w['tie_break']}/{w['ordering']}",
-        ms_per_step=ms, ms_min=min(per), ms_median=float(np.median(per)), wall_s=wall,
+        ms_per_step=ms, launch_ms_mean=float(np.mean(per)), launch_ms_min=min(per),
+        launch_ms_median=float(np.median(per)), host_enqueue_us_per_call=enqueue_s / steps * 1e6,
+        wall_s=wall,
         keys_per_s=N / t, input_copies=copies,
         bytes_roof=bytes_roof, hbm_roof_frac=(bytes_roof / (HBM_PEAK_GBS * 1e9)) / t,
         bytes_alg=bytes_alg, alg_gbs=bytes_alg / t / 1e9,
@@ -291,7 +303,7 @@ def main():
             log(name, json.dumps(others[name]))
     cpu = None if a.no_cpu_baseline else cpu_baseline(a.workload)
 
-    kernel_ms = head["ms_per_step"]
+    kernel_ms = head["launch_ms_mean"]
     line = {
         "metric": "segmented top-k keys/sec + % of single-read HBM roofline (fp32, k=64)",
         "value": head["keys_per_s"],
@@ -312,6 +324,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": head["bytes_alg"] / (kernel_ms / 1e3) / 1e9,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": head["bytes_alg"] / (kernel_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+                     "launch_us": kernel_ms * 1e3, "bytes_per_launch": head["bytes_alg"],
                      "traffic": measured_traffic(a.workload)},
         "cpu_baseline": cpu,
         "workloads": {n: {kk: (round(v, 6) if isinstance(v, float) else v)
