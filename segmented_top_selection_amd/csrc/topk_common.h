@@ -15,8 +15,9 @@ namespace segtopk_impl {
 constexpr int kWave = 64;               // wave64
 constexpr int kWaves = 4;               // waves per workgroup
 constexpr int kThreads = kWave * kWaves;
-constexpr int kDigit = 11;              // digit width of every radix pass
+constexpr int kDigit = 11;              // digit width of pass 0 over the keys
 constexpr int kBuckets = 1 << kDigit;   // 2048 histogram buckets
+constexpr int kLaterDigit = 8;          // digit width of the passes over the candidates
 constexpr uint32_t kNone = 0xFFFFFFFFu; // "no element" / sort padding
 constexpr int kSplitU = 8;               // loads per lane per chunk when segments are split
 constexpr size_t kMaxDynLds = 120 * 1024;

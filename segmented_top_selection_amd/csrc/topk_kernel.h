@@ -1123,7 +1123,7 @@ __device__ __forceinline__ void wave_finish(uint32_t *hist, uint2 *outbuf, const
 
     // Key digits.
     while (!done && hi > 0) {
-        const int w = hi < kDigit ? hi : kDigit;
+        const int w = hi < kLaterDigit ? hi : kLaterDigit;
         const int sh = hi - w;
         const uint32_t nb = 1u << w;
         wave_clear(hist, nb);
@@ -1155,7 +1155,7 @@ __device__ __forceinline__ void wave_finish(uint32_t *hist, uint2 *outbuf, const
         by_index = true;
         hi = 32 - __clz((int)(sg.n - 1u));
         while (!done && hi > 0) {
-            const int w = hi < kDigit ? hi : kDigit;
+            const int w = hi < kLaterDigit ? hi : kLaterDigit;
             const int sh = hi - w;
             const uint32_t nb = 1u << w;
             wave_clear(hist, nb);
@@ -1258,6 +1258,7 @@ struct alignas(16) Shared {
     uint32_t rg;
     uint32_t last, total, any_bad, nfront, ntie;  // the last arriver's state
     uint32_t ncand;                               // candidates listed (one-chunk segments)
+    uint32_t kb, kbefore, kcount, pad;            // the k-th bucket found by wave 0 (same)
 };
 
 // The last workgroup of a segment to finish pass 0, all four waves: the
@@ -1447,7 +1448,20 @@ __device__ __forceinline__ void small_block(Shared &sh, uint2 *stash, uint2 *out
                 atomicAdd(&sh.hist[rank0<KT, LARGEST>(Key<KT>::ord(Rg::key_at(raw, u * V + e)))], 1u);
     if (sv) atomicAdd(&sh.hist[rank0<KT, LARGEST>(Key<KT>::ord(sx))], 1u);
     __syncthreads();
-    const Kth kw = wave_find(sh.hist, kBuckets, sg.k_i);  // alike in every wave
+    if (w == 0) {  // one scan, for every wave
+        const Kth f = wave_find(sh.hist, kBuckets, sg.k_i);
+        if (ln == 0) {
+            sh.kb = f.b;
+            sh.kbefore = f.before;
+            sh.kcount = f.count;
+        }
+    }
+    __syncthreads();
+    Kth kw;
+    kw.found = 1;
+    kw.b = sh.kb;
+    kw.before = sh.kbefore;
+    kw.count = sh.kcount;
     const bool fits = kw.before + kw.count <= p.stash_cap;
     if (fits) {
         const Prefilter pf = prefilter<KT, LARGEST>(kw.b);
