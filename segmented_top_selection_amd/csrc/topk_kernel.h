@@ -69,6 +69,10 @@ template <> struct Key<SEGTOPK_KEY_F32> {
         r = (r == 0x80000000u) ? 0u : r;  // -0.0 joins +0.0
         return r ^ ((uint32_t)((int32_t)r >> 31) | 0x80000000u);
     }
+    // The raw bits of an ordered key (+0.0 for the ordered bits of zero).
+    __host__ __device__ __forceinline__ static uint32_t inv_ord(uint32_t o) {
+        return (o & 0x80000000u) ? (o ^ 0x80000000u) : ~o;
+    }
 };
 template <> struct Key<SEGTOPK_KEY_BF16> {
     static constexpr int kBits = 16, kBytes = 2;
@@ -76,6 +80,10 @@ template <> struct Key<SEGTOPK_KEY_BF16> {
     __host__ __device__ __forceinline__ static uint32_t ord(uint32_t r) {
         r = (r == 0x8000u) ? 0u : r;
         return r ^ ((r & 0x8000u) ? 0xFFFFu : 0x8000u);
+    }
+    __host__ __device__ __forceinline__ static uint32_t inv_ord(uint32_t o) {
+        o &= 0xFFFFu;
+        return (o & 0x8000u) ? (o ^ 0x8000u) : (~o & 0xFFFFu);
     }
 };
 template <> struct Key<SEGTOPK_KEY_F16> {
@@ -85,16 +93,22 @@ template <> struct Key<SEGTOPK_KEY_F16> {
         r = (r == 0x8000u) ? 0u : r;
         return r ^ ((r & 0x8000u) ? 0xFFFFu : 0x8000u);
     }
+    __host__ __device__ __forceinline__ static uint32_t inv_ord(uint32_t o) {
+        o &= 0xFFFFu;
+        return (o & 0x8000u) ? (o ^ 0x8000u) : (~o & 0xFFFFu);
+    }
 };
 template <> struct Key<SEGTOPK_KEY_U32> {
     static constexpr int kBits = 32, kBytes = 4;
     static constexpr bool kSignMag = false;
     __host__ __device__ __forceinline__ static uint32_t ord(uint32_t r) { return r; }
+    __host__ __device__ __forceinline__ static uint32_t inv_ord(uint32_t o) { return o; }
 };
 template <> struct Key<SEGTOPK_KEY_I32> {
     static constexpr int kBits = 32, kBytes = 4;
     static constexpr bool kSignMag = false;
     __host__ __device__ __forceinline__ static uint32_t ord(uint32_t r) { return r ^ 0x80000000u; }
+    __host__ __device__ __forceinline__ static uint32_t inv_ord(uint32_t o) { return o ^ 0x80000000u; }
 };
 
 // Pass-0 bucket rank of an ordered key: 0 is the best bucket.
@@ -930,10 +944,9 @@ template <int M> __device__ __forceinline__ uint32_t lane_xor(uint32_t x) {
 
 // One compare-exchange step (block SIZE, distance STRIDE) of a bitonic sort
 // of 64*E register entries, lane l holding entries l*E .. l*E+E-1, ascending
-// by (sk, id); rw and vv ride along.
-template <int E, int SIZE, int STRIDE>
-__device__ __forceinline__ void bitonic_step(uint32_t (&sk)[E], uint32_t (&id)[E], uint32_t (&rw)[E],
-                                             uint32_t (&vv)[E]) {
+// by (sk, id); NP payload arrays ride along (none when NP is 0).
+template <int E, int NP, int SIZE, int STRIDE>
+__device__ __forceinline__ void bitonic_step(uint32_t (&sk)[E], uint32_t (&id)[E], uint32_t (&pl)[NP ? NP : 1][E]) {
     const uint32_t ln = lane_id();
     if constexpr (STRIDE >= E) {
         constexpr int LM = STRIDE / E;
@@ -943,15 +956,16 @@ __device__ __forceinline__ void bitonic_step(uint32_t (&sk)[E], uint32_t (&id)[E
             const uint32_t j = ln * E + e;
             const uint32_t psk = lane_xor<LM>(sk[e]);
             const uint32_t pid = lane_xor<LM>(id[e]);
-            const uint32_t prw = lane_xor<LM>(rw[e]);
-            const uint32_t pvv = lane_xor<LM>(vv[e]);
+            uint32_t ppl[NP ? NP : 1];
+#pragma unroll
+            for (int q = 0; q < NP; ++q) ppl[q] = lane_xor<LM>(pl[q][e]);
             const bool asc = (j & SIZE) == 0;
             const bool pfirst = psk < sk[e] || (psk == sk[e] && pid < id[e]);
             if ((lower == asc) ? pfirst : !pfirst) {
                 sk[e] = psk;
                 id[e] = pid;
-                rw[e] = prw;
-                vv[e] = pvv;
+#pragma unroll
+                for (int q = 0; q < NP; ++q) pl[q][e] = ppl[q];
             }
         }
     } else {
@@ -965,61 +979,65 @@ __device__ __forceinline__ void bitonic_step(uint32_t (&sk)[E], uint32_t (&id)[E
             if (ffirst == asc) {
                 uint32_t t0 = sk[e]; sk[e] = sk[f]; sk[f] = t0;
                 t0 = id[e]; id[e] = id[f]; id[f] = t0;
-                t0 = rw[e]; rw[e] = rw[f]; rw[f] = t0;
-                t0 = vv[e]; vv[e] = vv[f]; vv[f] = t0;
+#pragma unroll
+                for (int q = 0; q < NP; ++q) {
+                    t0 = pl[q][e]; pl[q][e] = pl[q][f]; pl[q][f] = t0;
+                }
             }
         }
     }
 }
 
-template <int E, int SIZE, int STRIDE>
-__device__ __forceinline__ void bitonic_merge(uint32_t (&sk)[E], uint32_t (&id)[E], uint32_t (&rw)[E],
-                                              uint32_t (&vv)[E]) {
-    bitonic_step<E, SIZE, STRIDE>(sk, id, rw, vv);
-    if constexpr (STRIDE > 1) bitonic_merge<E, SIZE, STRIDE / 2>(sk, id, rw, vv);
+template <int E, int NP, int SIZE, int STRIDE>
+__device__ __forceinline__ void bitonic_merge(uint32_t (&sk)[E], uint32_t (&id)[E], uint32_t (&pl)[NP ? NP : 1][E]) {
+    bitonic_step<E, NP, SIZE, STRIDE>(sk, id, pl);
+    if constexpr (STRIDE > 1) bitonic_merge<E, NP, SIZE, STRIDE / 2>(sk, id, pl);
 }
 
 // Bitonic sort of all 64*E entries, blocks of SIZE and up (call with SIZE 2).
-template <int E, int SIZE>
-__device__ __forceinline__ void bitonic_regs(uint32_t (&sk)[E], uint32_t (&id)[E], uint32_t (&rw)[E],
-                                             uint32_t (&vv)[E]) {
-    bitonic_merge<E, SIZE, SIZE / 2>(sk, id, rw, vv);
-    if constexpr (SIZE < kWave * E) bitonic_regs<E, SIZE * 2>(sk, id, rw, vv);
+template <int E, int NP, int SIZE>
+__device__ __forceinline__ void bitonic_regs(uint32_t (&sk)[E], uint32_t (&id)[E], uint32_t (&pl)[NP ? NP : 1][E]) {
+    bitonic_merge<E, NP, SIZE, SIZE / 2>(sk, id, pl);
+    if constexpr (SIZE < kWave * E) bitonic_regs<E, NP, SIZE * 2>(sk, id, pl);
 }
 
-// Output of up to 64*E staged results held in registers, E per lane (lane l
-// holds results l*E .. l*E+E-1).  The values are gathered first so their
-// latency overlaps the sort; sorted output is a bitonic network on
-// (key best-first, index ascending) using lane exchanges for strides of E
-// and more and register swaps below that.
-// Sorts list[0, m) (m <= 64 * E, E entries per lane, in registers) best
-// first, ties by ascending index, and writes the first k_i to the row: the
-// sort is both the selection and the output order.  With prefer_larger_index
-// the entries equal to the k_i-th key keep their largest-index members
-// instead, still written in index order.  Values are loaded before the sort
-// so that their latency overlaps it.
+// Sorts list[0, m) (m <= 64 * E, E entries per lane, lane l holding entries
+// l*E .. l*E+E-1, in registers) best first, ties by ascending index, and
+// writes the first k_i to the row: the sort is both the selection and the
+// output order.  With prefer_larger_index the entries equal to the k_i-th key
+// keep their largest-index members instead, still written in index order.
+// The network carries the ordered key and the index only: the raw key is the
+// inverse of the ordered bits, unless a -0.0 is among the entries (then the
+// raw bits ride along), and the values are gathered after the sort.
 template <int KT, bool LARGEST, int E>
 __device__ __forceinline__ void sort_select(const uint2 *list, uint32_t m, const Params &p,
                                             const Seg &sg) {
+    constexpr uint32_t kNegZero = Key<KT>::kBits == 32 ? 0x80000000u : 0x8000u;
     const uint32_t ln = lane_id();
-    uint32_t sk[E], id[E], rw[E], vv[E];
+    uint32_t sk[E], id[E], pl[1][E];
+    bool negzero = false;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
         const uint32_t j = ln * E + e;
         sk[e] = kNone;
         id[e] = kNone;
-        rw[e] = 0;
-        vv[e] = 0;
+        pl[0][e] = 0;
         if (j < m) {
             const uint2 x = list[j];
             const uint32_t o = Key<KT>::ord(x.x);
             sk[e] = LARGEST ? ~o : o;
             id[e] = x.y;
-            rw[e] = x.x;
-            if (p.vals_in) vv[e] = x.y < sg.n ? p.vals_in[sg.begin + x.y] : kNone;
+            pl[0][e] = x.x;
+            negzero = negzero || (Key<KT>::kSignMag && x.x == kNegZero);
         }
     }
-    if (p.sorted || m > sg.k_i) bitonic_regs<E, 2>(sk, id, rw, vv);
+    const bool carry_raw = Key<KT>::kSignMag && __any(negzero);
+    if (p.sorted || m > sg.k_i) {
+        if (carry_raw)
+            bitonic_regs<E, 1, 2>(sk, id, pl);
+        else
+            bitonic_regs<E, 0, 2>(sk, id, pl);
+    }
     // Output position of sorted position j: j itself, except that with
     // prefer_larger_index the group [a, b) of entries equal to the k_i-th
     // keeps its last k_i - a members, moved down to [a, k_i).
@@ -1041,17 +1059,24 @@ __device__ __forceinline__ void sort_select(const uint2 *list, uint32_t m, const
         a = lt;
         shift = le - sg.k_i;  // b - (k_i - a) - a
     }
+    uint32_t pos[E], vv[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) {
         const uint32_t j = ln * E + e;
-        uint32_t pos = j;
-        if (j >= a) pos = (j >= a + shift) ? j - shift : kNone;
-        if (j < m && pos < sg.k_i) {
-            const size_t o = (size_t)sg.row * p.k + pos;
+        pos[e] = j;
+        if (j >= a) pos[e] = (j >= a + shift) ? j - shift : kNone;
+        if (j >= m) pos[e] = kNone;
+        vv[e] = (p.vals_in && pos[e] < sg.k_i && id[e] < sg.n) ? p.vals_in[sg.begin + id[e]] : kNone;
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        if (pos[e] < sg.k_i) {
+            const size_t o = (size_t)sg.row * p.k + pos[e];
+            const uint32_t rw = carry_raw ? pl[0][e] : Key<KT>::inv_ord(LARGEST ? ~sk[e] : sk[e]);
             if (Key<KT>::kBytes == 4)
-                static_cast<uint32_t *>(p.keys_out)[o] = rw[e];
+                static_cast<uint32_t *>(p.keys_out)[o] = rw;
             else
-                static_cast<uint16_t *>(p.keys_out)[o] = (uint16_t)rw[e];
+                static_cast<uint16_t *>(p.keys_out)[o] = (uint16_t)rw;
             if (p.vals_in) p.vals_out[o] = vv[e];
         }
     }

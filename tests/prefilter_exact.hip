@@ -1,8 +1,10 @@
-// Host check of the raw-bit bound test used by the top-k kernels: for every
-// key type and direction, the test built for a bucket bound passes exactly
+// Host check of the key transforms used by the top-k kernels: for every key
+// type and direction, the raw-bit test built for a bucket bound passes exactly
 // the keys whose order-preserving bits are within the bound (-0.0 counted as
-// +0.0), and the per-lane chunk reduction passes exactly when one of the
-// chunk's keys does.  16-bit keys: every bit pattern against every pass-0
+// +0.0), the per-lane chunk reduction passes exactly when one of the chunk's
+// keys does, and the inverse of the order-preserving bits gives back every
+// key's raw bits (-0.0 comes back as +0.0, which the sort never relies on:
+// it carries the raw bits whenever a -0.0 is present).  16-bit keys: every bit pattern against every pass-0
 // bound; 32-bit keys: boundary patterns plus seeded random ones.  Built
 // host-only; prints the number of mismatches and exits non-zero on any.
 #include "../segmented_top_selection_amd/csrc/topk_kernel.h"
@@ -68,6 +70,16 @@ static void check(const std::vector<uint32_t> &keys, const std::vector<uint32_t>
 
 template <int KT> static void run(const std::vector<uint32_t> &keys, const char *name) {
     constexpr uint32_t H = 1u << (Key<KT>::kBits - 1);
+    long inv_bad = 0;
+    for (uint32_t x : keys) {
+        const uint32_t want = (Key<KT>::kSignMag && x == H) ? 0u : x;
+        if (Key<KT>::inv_ord(Key<KT>::ord(x)) != want) {
+            if (inv_bad < 5) std::printf("  %s inv_ord(ord(%08x)) = %08x\n", name, x, Key<KT>::inv_ord(Key<KT>::ord(x)));
+            ++inv_bad;
+        }
+    }
+    std::printf("%-4s inverse of the ordered bits: %zu keys, %ld mismatches\n", name, keys.size(), inv_bad);
+    g_bad += inv_bad;
     std::vector<uint32_t> tmax, tmin;
     for (uint32_t R = 0; R < (uint32_t)kBuckets; ++R) {
         tmax.push_back(rank_thr<KT, true>(R));
