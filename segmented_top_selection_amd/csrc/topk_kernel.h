@@ -1286,6 +1286,138 @@ struct alignas(16) Shared {
     uint32_t kb, kbefore, kcount, pad;            // the k-th bucket found by wave 0 (same)
 };
 
+// Passes 1.., the tie selection and the output by the four waves of the
+// workgroup together, over the LDS list list[0, count): in every visit each
+// wave takes a quarter of the list; the histograms and the output positions
+// are shared through LDS, with a workgroup barrier between the steps, and
+// every wave finds the same bucket in the shared histogram.  The result is
+// wave_finish's: in the deterministic modes exactly the required ties pass
+// the final test, so arrival order decides only positions, which sorted
+// output fixes afterwards.  Called by all four waves.
+template <int KT, bool LARGEST>
+__device__ __forceinline__ void block_finish(Shared &sh, uint2 *outbuf, const Params &p,
+                                             const Seg &sg, const uint2 *list, uint32_t count,
+                                             Kth k0, uint32_t placed) {
+    constexpr int KB = Key<KT>::kBits;
+    const uint32_t t = threadIdx.x;
+    const uint32_t w = t / kWave;
+    const uint32_t ln = lane_id();
+    const bool pl = p.prefer_larger != 0;
+    uint32_t *hist = sh.hist;
+    const uint32_t chunks = (count + kWave - 1) / kWave;
+    const uint32_t c0 = chunks * w / kWaves, c1 = chunks * (w + 1) / kWaves;
+    auto visit = [&](auto &&f) {
+        for (uint32_t c = c0; c < c1; ++c) {
+            const uint32_t i = c * kWave + ln;
+            const bool act = i < count;
+            const uint2 e = act ? list[i] : make_uint2(0u, 0u);
+            f(e.x, e.y, act);
+        }
+    };
+
+    int hi = KB - kDigit;
+    uint32_t kmask = (uint32_t)(kBuckets - 1) << hi;
+    uint32_t kpref = (LARGEST ? (uint32_t)(kBuckets - 1) - k0.b : k0.b) << hi;
+    uint32_t krem = sg.k_i - k0.before;
+    uint32_t front = k0.before;
+    bool done = (k0.count == krem);
+
+    // Key digits.
+    while (!done && hi > 0) {
+        const int wd = hi < kLaterDigit ? hi : kLaterDigit;
+        const int sh_ = hi - wd;
+        const uint32_t nb = 1u << wd;
+        for (uint32_t i = t; i < nb; i += kThreads) hist[i] = 0u;
+        __syncthreads();
+        visit([&](uint32_t r, uint32_t idx, bool act) {
+            const uint32_t o = Key<KT>::ord(r);
+            if (act && (o & kmask) == kpref) {
+                const uint32_t d = (o >> sh_) & (nb - 1);
+                atomicAdd(&hist[LARGEST ? nb - 1 - d : d], 1u);
+            }
+        });
+        __syncthreads();
+        const Kth f = wave_find(hist, nb, krem);
+        krem -= f.before;
+        front += f.before;
+        kpref |= (LARGEST ? nb - 1 - f.b : f.b) << sh_;
+        kmask |= (nb - 1) << sh_;
+        done = (f.count == krem);
+        hi = sh_;
+        __syncthreads();
+    }
+
+    // Deterministic modes: narrow the splitter-equal keys by source index.
+    const uint32_t ties = krem;
+    bool by_index = false;
+    uint32_t imask = 0, ipref = 0;
+    if (!done && p.det) {
+        by_index = true;
+        hi = 32 - __clz((int)(sg.n - 1u));
+        while (!done && hi > 0) {
+            const int wd = hi < kLaterDigit ? hi : kLaterDigit;
+            const int sh_ = hi - wd;
+            const uint32_t nb = 1u << wd;
+            for (uint32_t i = t; i < nb; i += kThreads) hist[i] = 0u;
+            __syncthreads();
+            visit([&](uint32_t r, uint32_t idx, bool act) {
+                if (act && (Key<KT>::ord(r) & kmask) == kpref && (idx & imask) == ipref) {
+                    const uint32_t d = (idx >> sh_) & (nb - 1);
+                    atomicAdd(&hist[pl ? nb - 1 - d : d], 1u);
+                }
+            });
+            __syncthreads();
+            const Kth f = wave_find(hist, nb, krem);
+            krem -= f.before;
+            ipref |= (pl ? nb - 1 - f.b : f.b) << sh_;
+            imask |= (nb - 1) << sh_;
+            done = (f.count == krem);
+            hi = sh_;
+            __syncthreads();
+        }
+    }
+
+    // Final filter: keys better than the splitter to [placed, front), the
+    // chosen ties to [front, k_i); each wave reserves its positions per 64
+    // entries with one LDS atomic per kind.
+    if (t == 0) {
+        sh.nfront = placed;
+        sh.ntie = 0;
+    }
+    __syncthreads();
+    visit([&](uint32_t r, uint32_t idx, bool act) {
+        const uint32_t km = Key<KT>::ord(r) & kmask;
+        const bool better = act && (LARGEST ? km > kpref : km < kpref);
+        bool tie = act && km == kpref;
+        if (by_index) {
+            const uint32_t im = idx & imask;
+            tie = tie && (pl ? im >= ipref : im <= ipref);
+        }
+        const uint64_t mb = __ballot(better);
+        const uint64_t mt = __ballot(tie);
+        uint32_t fb = 0, tb = 0;
+        if (ln == 0) {
+            fb = mb ? atomicAdd(&sh.nfront, (uint32_t)__popcll(mb)) : 0u;
+            tb = mt ? atomicAdd(&sh.ntie, (uint32_t)__popcll(mt)) : 0u;
+        }
+        const uint32_t pb = wave_bcast(fb, 0) + lanes_below(mb);
+        const uint32_t pt = wave_bcast(tb, 0) + lanes_below(mt);
+        uint32_t pos = kNone;
+        if (better && pb < front) pos = pb;
+        if (tie && pt < ties) pos = front + pt;
+        if (pos != kNone) {
+            if (outbuf)
+                outbuf[pos] = make_uint2(r, idx);
+            else
+                write_out<KT>(p, sg, pos, r, idx);
+        }
+    });
+    if (outbuf) {
+        __syncthreads();
+        if (w == 0) write_staged<KT, LARGEST>(outbuf, p, sg);
+    }
+}
+
 // The last workgroup of a segment to finish pass 0, all four waves: the
 // segment's exact k-th bucket b* from the merged histogram, then every slot's
 // entries up to b* (a prefix, as the slots are sorted by bucket): those of
@@ -1397,6 +1529,12 @@ __device__ __forceinline__ void slice_last(Shared &sh, uint2 *stash, uint2 *outb
         }
     }
     __syncthreads();
+    if (fast) {
+        // The four waves finish together on bucket b*'s list.
+        block_finish<KT, LARGEST>(sh, outbuf, p, sg, stash,
+                                  sh.ntie < p.stash_cap ? sh.ntie : p.stash_cap, ks, ks.before);
+        return;
+    }
     if (w != 0) return;
 
     Cands<KT> cand;
