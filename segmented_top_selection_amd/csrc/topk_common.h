@@ -18,6 +18,7 @@ constexpr int kThreads = kWave * kWaves;
 constexpr int kDigit = 11;              // digit width of pass 0 over the keys
 constexpr int kBuckets = 1 << kDigit;   // 2048 histogram buckets
 constexpr int kLaterDigit = 8;          // digit width of the passes over the candidates
+constexpr uint32_t kBlockFinishMin = 512;  // longer candidate lists are finished by all four waves
 constexpr uint32_t kNone = 0xFFFFFFFFu; // "no element" / sort padding
 constexpr int kSplitU = 8;               // loads per lane per chunk when segments are split
 constexpr size_t kMaxDynLds = 120 * 1024;

@@ -537,6 +537,7 @@ struct Pass0 {
     uint32_t R;      // the wave's final bound (rank)
     uint32_t count;  // stash entries
     uint32_t defer;  // chunks [0, defer) were counted but not stashed
+    uint32_t nch;    // chunks of the wave's range
 };
 
 // Drops, in place, the stash entries whose pass-0 rank is beyond the bound.
@@ -744,6 +745,7 @@ __device__ __forceinline__ Pass0 wave_pass0(uint32_t *hist, uint2 *stash, uint32
             }
         }
     }
+    r.nch = nch;
     return r;
 }
 
@@ -792,6 +794,29 @@ __device__ __forceinline__ bool wave_reread(uint2 *stash, uint32_t cap, uint32_t
             }
     }
     return ok;
+}
+
+// Pass 0 of one wave, then its deferred chunks read again at once under the
+// wave's own final bound (valid for the workgroup: bounds only tighten), so
+// that the re-read overlaps the other waves' streaming instead of following
+// the workgroup barrier.  If they do not fit, every chunk stays deferred and
+// is read again after the barrier under the workgroup's bound.
+template <int KT, bool LARGEST, int U>
+__device__ __forceinline__ Pass0 wave_pass0_stash(uint32_t *hist, uint2 *stash, uint32_t cap,
+                                                  const void *keys, int64_t begin, uint32_t lo,
+                                                  uint32_t hi, uint32_t target, const Share &sh) {
+    Pass0 r = wave_pass0<KT, LARGEST, U>(hist, stash, cap, keys, begin, lo, hi, target, sh);
+    if (r.defer != 0) {
+        uint32_t cnt = r.count;
+        if (wave_reread<KT, LARGEST, U>(stash, cap, cnt, keys, begin, lo, hi, r.defer, r.R)) {
+            r.count = cnt;
+            r.defer = 0;
+        } else {
+            r.count = 0;
+            r.defer = r.nch;
+        }
+    }
+    return r;
 }
 
 // ---------------------------------------------------------------------------
@@ -1650,6 +1675,10 @@ __device__ __forceinline__ void small_block(Shared &sh, uint2 *stash, uint2 *out
             }
     }
     __syncthreads();
+    if (fits && sh.ncand > kBlockFinishMin) {
+        block_finish<KT, LARGEST>(sh, outbuf, p, sg, stash, sh.ncand, kw, 0u);
+        return;
+    }
     if (w != 0) return;
     Cands<KT> cand;
     cand.list = stash;
@@ -1739,8 +1768,8 @@ __global__ __launch_bounds__(kThreads, (topk_waves<KT, U>())) void topk_kernel(P
     share.gearly = ps > 1 ? p.ws_early + (size_t)s * kBuckets : nullptr;
     share.glast = ps > 1 ? p.ws_slot_cum + ((size_t)s * P + q) * kBuckets : nullptr;
     share.wave = w;
-    const Pass0 r0 = wave_pass0<KT, LARGEST, U>(sh.hist, stash + w * capw, capw, p.keys_in,
-                                             sg.begin, wlo, whi, sg.k_i, share);
+    const Pass0 r0 = wave_pass0_stash<KT, LARGEST, U>(sh.hist, stash + w * capw, capw, p.keys_in,
+                                                   sg.begin, wlo, whi, sg.k_i, share);
     if (ln == 0) {
         sh.wcount[w] = r0.count;
         sh.wbad[w] = 0;
@@ -1766,10 +1795,22 @@ __global__ __launch_bounds__(kThreads, (topk_waves<KT, U>())) void topk_kernel(P
         __syncthreads();
     }
     if (w != 0) {
-        // Wave 0 finishes the workgroup's work alone; with several workgroups
-        // per segment the others wait for the ticket and help the last one.
-        if (ps == 1) return;
+        // Wave 0 gathers the workgroup's candidates; with one workgroup per
+        // segment a long list is finished by the four waves together, with
+        // several workgroups per segment the others wait for the ticket and
+        // help the last one.
         __syncthreads();
+        if (ps == 1) {
+            if (sh.ncand != kNone && sh.ncand > kBlockFinishMin) {
+                Kth kb;
+                kb.found = 1;
+                kb.b = sh.kb;
+                kb.before = sh.kbefore;
+                kb.count = sh.kcount;
+                block_finish<KT, LARGEST>(sh, outbuf, p, sg, stash, sh.ncand, kb, 0u);
+            }
+            return;
+        }
         if (!sh.last) return;
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         slice_last<KT, LARGEST>(sh, stash, outbuf, p, sg, s, P, ps, slice);
@@ -1821,6 +1862,19 @@ __global__ __launch_bounds__(kThreads, (topk_waves<KT, U>())) void topk_kernel(P
     cand.bstar = 0;
 
     if (ps == 1) {
+        // Publish the list; a long one is finished by the four waves.
+        const bool blk = !bad && ncand > kBlockFinishMin;
+        if (ln == 0) {
+            sh.ncand = bad ? kNone : ncand;
+            sh.kb = kw.b;
+            sh.kbefore = kw.before;
+            sh.kcount = kw.count;
+        }
+        __syncthreads();
+        if (blk) {
+            block_finish<KT, LARGEST>(sh, outbuf, p, sg, stash, ncand, kw, 0u);
+            return;
+        }
         wave_finish<KT, LARGEST>(sh.hist, outbuf, p, sg, cand, kw);
         return;
     }
