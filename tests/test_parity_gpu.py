@@ -378,3 +378,78 @@ def test_repeat_runs_identical():
         again = run_gpu(keys, vals, off, 256, "f32", False, "gpu_to_gpu",
                         "prefer_smaller_index", "stable_sorted")
         assert np.array_equal(first[0], again[0]) and np.array_equal(first[1], again[1])
+
+
+# ---------------------------------------------------------------------------
+# Extreme bit patterns: denormals of both signs next to +-0.0, the largest
+# finite values, infinities; integer extremes.  Segment sizes cover the
+# one-chunk path and the streaming path.
+# ---------------------------------------------------------------------------
+def _extreme_keys(key_type, n, rng):
+    if key_type == "f32":
+        pool = np.array([0x00000000, 0x80000000, 0x00000001, 0x80000001, 0x007FFFFF, 0x807FFFFF,
+                         0x00800000, 0x80800000, 0x7F7FFFFF, 0xFF7FFFFF, 0x7F800000, 0xFF800000,
+                         0x3F800000, 0xBF800000], dtype=np.uint32)
+        bits = rng.choice(pool, n)
+        return torch.from_numpy(bits.view(np.int32)).view(torch.float32).to(DEV)
+    if key_type in ("bf16", "f16"):
+        if key_type == "bf16":
+            pool = [0x0000, 0x8000, 0x0001, 0x8001, 0x007F, 0x807F, 0x0080, 0x8080, 0x7F7F, 0xFF7F,
+                    0x7F80, 0xFF80, 0x3F80, 0xBF80]
+        else:
+            pool = [0x0000, 0x8000, 0x0001, 0x8001, 0x03FF, 0x83FF, 0x0400, 0x8400, 0x7BFF, 0xFBFF,
+                    0x7C00, 0xFC00, 0x3C00, 0xBC00]
+        bits = rng.choice(np.array(pool, dtype=np.uint16), n).view(np.int16)
+        t = torch.from_numpy(bits.copy())
+        return t.view(torch.bfloat16 if key_type == "bf16" else torch.float16).to(DEV)
+    if key_type == "u32":
+        pool = np.array([0, 1, 2, 0x7FFFFFFF, 0x80000000, 0xFFFFFFFE, 0xFFFFFFFF], dtype=np.uint32)
+        return torch.from_numpy(rng.choice(pool, n).view(np.int32)).to(DEV)
+    pool = np.array([-2 ** 31, -2 ** 31 + 1, -1, 0, 1, 2 ** 31 - 2, 2 ** 31 - 1], dtype=np.int64)
+    return torch.from_numpy(rng.choice(pool, n).astype(np.int32)).to(DEV)
+
+
+@pytest.mark.parametrize("key_type", KEY_TYPES)
+def test_extreme_bit_patterns(key_type):
+    rng = np.random.default_rng(21)
+    sizes = [7, 300, 4096, 5000, 40000]
+    off = torch.tensor(np.cumsum([0] + sizes), dtype=torch.int64, device=DEV)
+    keys = _extreme_keys(key_type, int(off[-1]), rng)
+    vals = index_values(off)
+    for k in (1, 16, 700):
+        for largest in (True, False):
+            for det, tb in MODES:
+                for ordering in ("unsorted", "stable_sorted"):
+                    check(keys, vals, off, k, key_type, largest, det, tb, ordering)
+
+
+def test_many_segments_all_equal_keys():
+    """2048+ segments of identical keys: every key is a candidate, more than
+    the on-chip list holds for the longer segments."""
+    sizes = [300, 4096, 1000, 4000] * 520
+    off = torch.tensor(np.cumsum([0] + sizes), dtype=torch.int64, device=DEV)
+    keys = torch.full((int(off[-1]),), 2.5, dtype=torch.float32, device=DEV)
+    vals = index_values(off)
+    say(f"[all equal] segments={len(sizes)} keys={int(off[-1])}")
+    for k in (33, 100):
+        for largest in (True, False):
+            for det, tb in [MODES[0], MODES[3], MODES[4]]:
+                for ordering in ("unsorted", "stable_sorted"):
+                    check(keys, vals, off, k, "f32", largest, det, tb, ordering)
+
+
+@pytest.mark.parametrize("key_type", ["f32", "bf16"])
+def test_many_segments_large_k(key_type):
+    """k above the register sort (LDS sort) and unsorted direct writes, with
+    one workgroup per segment."""
+    g = torch.Generator(device=DEV)
+    g.manual_seed(31)
+    off, total = _many_segments(13)
+    vals = torch.arange(total, dtype=torch.int32, device=DEV)
+    keys = random_keys(total, key_type, g, 7)
+    for k in (300, 1500):
+        for largest in (True, False):
+            for det, tb in [MODES[0], MODES[3], MODES[4]]:
+                for ordering in ("unsorted", "stable_sorted"):
+                    check(keys, vals, off, k, key_type, largest, det, tb, ordering,
+                          values_are="position")
