@@ -22,12 +22,50 @@ __global__ void zero_kernel(uint32_t *p, size_t n) {
         p[i] = 0u;
 }
 
+// Processing order for a batch with one workgroup per segment: segments by
+// size class (floor(log2 n) + 1), largest class first, so that the longest
+// segments start first and the short ones fill the workgroup slots as they
+// free up.  One workgroup of 1024 threads, num_segments <= 2048.
+__global__ __launch_bounds__(1024) void order_kernel(const int64_t *off, int64_t num_segments,
+                                                    uint32_t *order) {
+    __shared__ uint32_t cnt[33];
+    const uint32_t t = threadIdx.x;
+    if (t < 33) cnt[t] = 0u;
+    __syncthreads();
+    uint32_t cls[2];
+    for (int j = 0; j < 2; ++j) {
+        const int64_t i = (int64_t)t + (int64_t)j * 1024;
+        cls[j] = 0u;
+        if (i < num_segments) {
+            const int64_t d = off[i + 1] - off[i];
+            const uint32_t n = d > 0 ? (uint32_t)d : 0u;
+            cls[j] = n ? 32u - (uint32_t)__clz((int)n) : 0u;
+            atomicAdd(&cnt[cls[j]], 1u);
+        }
+    }
+    __syncthreads();
+    if (t == 0) {  // exclusive prefix, largest class first
+        uint32_t run = 0;
+        for (int c = 32; c >= 0; --c) {
+            const uint32_t n = cnt[c];
+            cnt[c] = run;
+            run += n;
+        }
+    }
+    __syncthreads();
+    for (int j = 0; j < 2; ++j) {
+        const int64_t i = (int64_t)t + (int64_t)j * 1024;
+        if (i < num_segments) order[atomicAdd(&cnt[cls[j]], 1u)] = (uint32_t)i;
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Host side.
 // ---------------------------------------------------------------------------
 constexpr uint32_t kTargetWorkgroups = 2048;  // enough to fill 256 CUs several times
 constexpr uint32_t kMaxWgPerSeg = 256;
 constexpr uint32_t kMinSlice = 16384;
+constexpr int64_t kOrderMinSegments = 256;  // fewer segments: no processing order
 
 int key_bytes(int type) { return (type == SEGTOPK_KEY_BF16 || type == SEGTOPK_KEY_F16) ? 2 : 4; }
 
@@ -196,7 +234,18 @@ extern "C" int batched_topk(const segtopk_keys *keys, const segtopk_values *valu
 
     void *ws = nullptr;
     hipError_t err = hipSuccess;
-    if (P > 1) {
+    if (split && P == 1 && num_segments >= kOrderMinSegments) {
+        // One workgroup per segment for many segments of unknown sizes:
+        // process the largest first.
+        if (hipGetDevice(&dev) != hipSuccess) return SEGTOPK_HIP_ERROR;
+        prepare_pool(dev);
+        if (hipMallocAsync(&ws, (size_t)num_segments * sizeof(uint32_t), stream) != hipSuccess)
+            return SEGTOPK_HIP_ERROR;
+        p.order = static_cast<const uint32_t *>(ws);
+        hipLaunchKernelGGL(order_kernel, dim3(1), dim3(1024), 0, stream, segment_offsets,
+                           num_segments, static_cast<uint32_t *>(ws));
+        err = hipGetLastError();
+    } else if (P > 1) {
         prepare_pool(dev);
         const size_t S = (size_t)num_segments;
         const size_t n_hist = S * kBuckets, n_ticket = S;

@@ -47,6 +47,7 @@ struct Params {
     uint32_t *ws_slot_info;  // [segments][P][4]        (count, overflowed, bound, -)
     uint32_t *ws_slot_cum;   // [segments][P][kBuckets] entries with rank <= r
     uint2 *ws_slot_data;     // [segments][P][stash_cap] candidates sorted by rank
+    const uint32_t *order;   // [segments] processing order (one workgroup each), or nullptr
 };
 
 // Launches the top-k kernel for key type KT on `st`: grid workgroups of

@@ -1716,8 +1716,12 @@ __global__ __launch_bounds__(kThreads, (topk_waves<KT, U>())) void topk_kernel(P
     const uint32_t P = p.wg_per_seg;
     const uint32_t b = blockIdx.x;
     const uint32_t qq = b >> 3;
-    const int64_t s = (int64_t)(qq / P) * 8 + (b & 7u);
+    int64_t s = (int64_t)(qq / P) * 8 + (b & 7u);
     const uint32_t q = qq % P;
+    if (p.order) {  // one workgroup per segment, largest segments first
+        if ((int64_t)b >= p.num_segments) return;
+        s = p.order[b];
+    }
     if (s >= p.num_segments) return;
 
     Seg sg;

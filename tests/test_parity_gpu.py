@@ -453,3 +453,28 @@ def test_many_segments_large_k(key_type):
                 for ordering in ("unsorted", "stable_sorted"):
                     check(keys, vals, off, k, key_type, largest, det, tb, ordering,
                           values_are="position")
+
+
+@pytest.mark.parametrize("key_type", KEY_TYPES)
+def test_ordered_one_workgroup_per_segment(key_type):
+    """700 segments of mixed sizes: one workgroup each, taken largest first
+    (the order is decided on the device); every row compared in full."""
+    rng = np.random.default_rng(41)
+    sizes = rng.integers(0, 12000, 700)
+    sizes[::50] = 0
+    sizes[1::97] = 5
+    sizes[2::31] = 30000
+    off = torch.tensor(np.cumsum([3] + sizes.tolist()), dtype=torch.int64, device=DEV)
+    total = int(off[-1]) + 1
+    g = torch.Generator(device=DEV)
+    g.manual_seed(43)
+    vals = torch.arange(total, dtype=torch.int32, device=DEV)
+    say(f"[ordered {key_type}] segments=700 keys={total}")
+    for levels in (None, 9):
+        keys = random_keys(total, key_type, g, levels)
+        for k in (40, 256):
+            for largest in (True, False):
+                for det, tb in ([MODES[0], MODES[3], MODES[4]] if levels else [MODES[4]]):
+                    for ordering in ("unsorted", "stable_sorted"):
+                        check(keys, vals, off, k, key_type, largest, det, tb, ordering,
+                              values_are="position")
