@@ -1652,26 +1652,39 @@ __device__ __forceinline__ void small_block(Shared &sh, uint2 *stash, uint2 *out
     kw.count = sh.kcount;
     const bool fits = kw.before + kw.count <= p.stash_cap;
     if (fits) {
+        // Count this wave's candidates (ballots only), reserve their places
+        // with one LDS atomic, then write them: per key one compare whose
+        // ballot is masked by the load's validity on the scalar unit.
         const Prefilter pf = prefilter<KT, LARGEST>(kw.b);
-        const bool sin = sv && pf_key(pf, sx);
-        uint32_t c = sin ? 1u : 0u;
+        const uint64_t ms = __builtin_amdgcn_ballot_w64(pf_key(pf, sx)) & __ballot(sv);
+        uint64_t vm[Rg::kU];
+        uint32_t total = (uint32_t)__popcll(ms);
 #pragma unroll
-        for (int u = 0; u < Rg::kU; ++u)
+        for (int u = 0; u < Rg::kU; ++u) {
+            vm[u] = __ballot(vidx[u] != kNone);
 #pragma unroll
             for (int e = 0; e < V; ++e)
-                c += (vidx[u] != kNone && pf_key(pf, Rg::key_at(raw, u * V + e))) ? 1u : 0u;
-        const uint32_t incl = wave_incl_sum(c);
-        const uint32_t total = wave_bcast(incl, kWave - 1);
+                total += (uint32_t)__popcll(
+                    __builtin_amdgcn_ballot_w64(pf_key(pf, Rg::key_at(raw, u * V + e))) & vm[u]);
+        }
         uint32_t base = 0;
         if (ln == 0 && total) base = atomicAdd(&sh.ncand, total);
-        uint32_t pos = wave_bcast(base, 0) + incl - c;
-        if (sin) stash[pos++] = make_uint2(sx, si);
+        uint32_t pos = __builtin_amdgcn_readfirstlane(wave_bcast(base, 0));
+        auto put = [&](uint64_t m, uint32_t x, uint32_t idx) {
+            if (m == 0) return;
+            if (__builtin_amdgcn_inverse_ballot_w64(m))
+                stash[__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                __builtin_amdgcn_mbcnt_lo((uint32_t)m, pos))] =
+                    make_uint2(x, idx);
+            pos += (uint32_t)__popcll(m);
+        };
+        put(ms, sx, si);
 #pragma unroll
         for (int u = 0; u < Rg::kU; ++u)
 #pragma unroll
             for (int e = 0; e < V; ++e) {
                 const uint32_t x = Rg::key_at(raw, u * V + e);
-                if (vidx[u] != kNone && pf_key(pf, x)) stash[pos++] = make_uint2(x, vidx[u] + (uint32_t)e);
+                put(__builtin_amdgcn_ballot_w64(pf_key(pf, x)) & vm[u], x, vidx[u] + (uint32_t)e);
             }
     }
     __syncthreads();
