@@ -1710,10 +1710,13 @@ __device__ __forceinline__ void small_block(Shared &sh, uint2 *stash, uint2 *out
     wave_finish<KT, LARGEST>(sh.hist, outbuf, p, sg, cand, kw);
 }
 
-// Waves per SIMD the kernel is built for: 5 (at most 102 VGPRs) for 32-bit
-// keys and 4 for 16-bit keys with 4 loads per lane; 3 and 2 with 8.
+// Waves per SIMD the kernel is built for.  With 4 loads per lane: 6 for
+// 32-bit keys (at most 80 VGPRs; some spill, but the many-small-segment
+// batches this serves gain more from the extra resident workgroups than they
+// lose: on the 4096 x 4096 workload 6 beat 5, 7 and 8), 4 for 16-bit keys.
+// With 8 loads per lane: 3 and 2.
 template <int KT, int U> constexpr int topk_waves() {
-    return U == 4 ? (Key<KT>::kBytes == 4 ? 5 : 4) : (Key<KT>::kBytes == 4 ? 3 : 2);
+    return U == 4 ? (Key<KT>::kBytes == 4 ? 6 : 4) : (Key<KT>::kBytes == 4 ? 3 : 2);
 }
 
 template <int KT, bool LARGEST, int U>
