@@ -560,16 +560,17 @@ __device__ __forceinline__ uint32_t wave_compact(uint2 *stash, uint32_t cnt, con
 }
 
 // Appends the lanes' entries with `ex` set to the stash; false when they do
-// not fit even after dropping the entries beyond bound R.
+// not fit even after dropping the entries that fail pf (the test for the
+// current bound, which the caller holds already).
 template <int KT, bool LARGEST>
-__device__ __forceinline__ bool wave_push(uint2 *stash, uint32_t cap, uint32_t &count, uint32_t R,
-                                          bool ex, uint32_t x, uint32_t idx) {
+__device__ __forceinline__ bool wave_push(uint2 *stash, uint32_t cap, uint32_t &count,
+                                          const Prefilter &pf, bool ex, uint32_t x, uint32_t idx) {
     const uint64_t m = __ballot(ex);
     const uint32_t n = (uint32_t)__popcll(m);
     if (n == 0) return true;
     if (count + n > cap) {
         wave_sync();
-        count = wave_compact<KT, LARGEST>(stash, count, prefilter<KT, LARGEST>(R));
+        count = wave_compact<KT, LARGEST>(stash, count, pf);
         if (count + n > cap) return false;
     }
     if (ex) stash[count + lanes_below(m)] = make_uint2(x, idx);
@@ -721,7 +722,7 @@ __device__ __forceinline__ Pass0 wave_pass0(uint32_t *hist, uint2 *stash, uint32
             const bool ex = pv && rk <= r.R;
             if (ex) atomicAdd(&hist[rk], 1u);
             counted += (uint32_t)__popcll(__ballot(ex));
-            if (ok) ok = wave_push<KT, LARGEST>(stash, cap, r.count, r.R, ex, x, idx);
+            if (ok) ok = wave_push<KT, LARGEST>(stash, cap, r.count, pf, ex, x, idx);
         };
         take(sx, si, s0);
 #pragma unroll
@@ -768,7 +769,7 @@ __device__ __forceinline__ bool wave_reread(uint2 *stash, uint32_t cap, uint32_t
         const bool sv = ln < L.nscalar;
         const uint32_t si = sv ? L.scalar_idx(ln) : 0u;
         const uint32_t x = sv ? L.load_scalar(si) : 0u;
-        ok = wave_push<KT, LARGEST>(stash, cap, count, R, sv && pf_key(pf, x), x, si);
+        ok = wave_push<KT, LARGEST>(stash, cap, count, pf, sv && pf_key(pf, x), x, si);
     }
     const uint32_t nre = defer < L.nchunks ? defer : L.nchunks;
     uint32_t raw[K], vidx[Rg::kU];
@@ -789,7 +790,7 @@ __device__ __forceinline__ bool wave_reread(uint2 *stash, uint32_t cap, uint32_t
             for (int e = 0; e < V; ++e) {
                 const uint32_t x = Rg::key_at(cur, u * V + e);
                 if (ok)
-                    ok = wave_push<KT, LARGEST>(stash, cap, count, R, cv[u] != kNone && pf_key(pf, x),
+                    ok = wave_push<KT, LARGEST>(stash, cap, count, pf, cv[u] != kNone && pf_key(pf, x),
                                                 x, cv[u] + (uint32_t)e);
             }
     }
