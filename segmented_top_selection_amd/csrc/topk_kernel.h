@@ -603,6 +603,17 @@ __device__ __forceinline__ Pass0 wave_pass0(uint32_t *hist, uint2 *stash, uint32
     bool bounded = false;
     bool contributed = false;
     Prefilter pf = prefilter<KT, LARGEST>(kBuckets - 1);
+    // 16-bit keys: when the bound was last computed from the histogram,
+    // `below` keys of the workgroup lay in buckets before it; this wave has
+    // counted `nbelow` more there since.  The bound can only move once
+    // `below` plus the new counts of all four waves reach the target, so the
+    // scan waits for that (taking the other waves to count about as many as
+    // this one).  The 2-mantissa-bit buckets of 16-bit floats keep the bound
+    // in one bucket for most of a long stream, and this saves a scan per
+    // chunk there.  32-bit keys rescan after every chunk that counted
+    // anything.
+    constexpr bool kLazy = Key<KT>::kBytes == 2;
+    uint32_t below = 0, nbelow = 0;
 
     // The unaligned head and tail ride along with chunk 0.
     const bool sv = ln < L.nscalar;
@@ -627,6 +638,7 @@ __device__ __forceinline__ Pass0 wave_pass0(uint32_t *hist, uint2 *stash, uint32
                 __hip_atomic_load(sh.rg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
             if (rg < r.R) {
                 r.R = rg;
+                below = 0;  // not known for a bound found elsewhere
                 bounded = true;
                 pf = prefilter<KT, LARGEST>(r.R);
             }
@@ -648,6 +660,7 @@ __device__ __forceinline__ Pass0 wave_pass0(uint32_t *hist, uint2 *stash, uint32
                     const Kth g = wave_find_global(sh.gearly, r.R + 1, target);
                     if (g.found && g.b < r.R) {
                         r.R = g.b;
+                        below = 0;
                         pf = prefilter<KT, LARGEST>(r.R);
                         if (ln == 0) atomicMin(sh.rg, g.b);
                     }
@@ -677,6 +690,7 @@ __device__ __forceinline__ Pass0 wave_pass0(uint32_t *hist, uint2 *stash, uint32
             const Kth f = wave_find(hist, kBuckets, target);
             if (!f.found) continue;
             r.R = f.b;
+            below = f.before;
             bounded = true;
             pf = prefilter<KT, LARGEST>(r.R);
             // Stash this chunk's keys within the bound from the registers,
@@ -713,7 +727,6 @@ __device__ __forceinline__ Pass0 wave_pass0(uint32_t *hist, uint2 *stash, uint32
         const bool cp = pf_chunk<KT>(pf, cur);
         const bool sp = s0 && pf_key(pf, sx);
         if (!__any(cp || sp)) continue;
-        uint32_t counted = 0;
         bool ok = true;
         auto take = [&](uint32_t x, uint32_t idx, bool valid) {
             const bool pv = valid && pf_key(pf, x);
@@ -721,7 +734,7 @@ __device__ __forceinline__ Pass0 wave_pass0(uint32_t *hist, uint2 *stash, uint32
             const uint32_t rk = rank0<KT, LARGEST>(Key<KT>::ord(x));
             const bool ex = pv && rk <= r.R;
             if (ex) atomicAdd(&hist[rk], 1u);
-            counted += (uint32_t)__popcll(__ballot(ex));
+            nbelow += (uint32_t)__popcll(__ballot(ex && (!kLazy || rk < r.R)));
             if (ok) ok = wave_push<KT, LARGEST>(stash, cap, r.count, pf, ex, x, idx);
         };
         take(sx, si, s0);
@@ -736,13 +749,17 @@ __device__ __forceinline__ Pass0 wave_pass0(uint32_t *hist, uint2 *stash, uint32
             r.count = 0;
             r.defer = c + 1;
         }
-        if (counted) {
-            // Tighten the bound from everything counted so far.
+        if (nbelow != 0 && (!kLazy || below + (uint32_t)kWaves * nbelow >= target)) {
+            // The bound may move: recompute it from everything counted.
+            nbelow = 0;
             wave_sync();
             const Kth f = wave_find(hist, r.R + 1, target);
-            if (f.found && f.b < r.R) {
-                r.R = f.b;
-                pf = prefilter<KT, LARGEST>(r.R);
+            if (f.found) {
+                below = f.before;
+                if (f.b < r.R) {
+                    r.R = f.b;
+                    pf = prefilter<KT, LARGEST>(r.R);
+                }
             }
         }
     }
