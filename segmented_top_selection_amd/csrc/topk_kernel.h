@@ -481,6 +481,41 @@ template <int KT, int NT, int U> struct Range {
             raw[u * 4 + 3] = v.w;
         }
     }
+    // Chunk c without the element indices: the loads of a chunk wholly
+    // inside the aligned body (every chunk but the last) take no bounds
+    // tests; slots past the end are zero.
+    template <bool STREAM = false>
+    __device__ __forceinline__ void load_body(uint32_t c, uint32_t t, uint32_t (&raw)[kDw]) const {
+        typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+        const v4u *src = reinterpret_cast<const v4u *>(vbase) + c * kChunkVecs + t;
+        if ((c + 1) * kChunkVecs <= nvec) {
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+                const v4u v = STREAM ? __builtin_nontemporal_load(src + u * NT) : src[u * NT];
+                raw[u * 4 + 0] = v.x;
+                raw[u * 4 + 1] = v.y;
+                raw[u * 4 + 2] = v.z;
+                raw[u * 4 + 3] = v.w;
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+                v4u v = {0u, 0u, 0u, 0u};
+                if (c * kChunkVecs + (uint32_t)u * NT + t < nvec)
+                    v = STREAM ? __builtin_nontemporal_load(src + u * NT) : src[u * NT];
+                raw[u * 4 + 0] = v.x;
+                raw[u * 4 + 1] = v.y;
+                raw[u * 4 + 2] = v.z;
+                raw[u * 4 + 3] = v.w;
+            }
+        }
+    }
+    // Element index of the first key of thread t's load u of chunk c, kNone
+    // past the end.
+    __device__ __forceinline__ uint32_t vec_idx(uint32_t c, uint32_t t, int u) const {
+        const uint32_t vj = c * kChunkVecs + (uint32_t)u * NT + t;
+        return vj < nvec ? lo + head + vj * kVec : kNone;
+    }
     // Key j of a thread's chunk as raw bits, zero-extended.
     __device__ __forceinline__ static uint32_t key_at(const uint32_t (&raw)[kDw], int j) {
         if (kBytes == 4) return raw[j];
@@ -621,15 +656,26 @@ __device__ __forceinline__ Pass0 wave_pass0(uint32_t *hist, uint2 *stash, uint32
     const uint32_t sx = sv ? L.load_scalar(si) : 0u;
 
     uint32_t raw[K], vidx[Rg::kU];
-    L.template load_chunk<true>(0, ln, raw, vidx);
+    if constexpr (kLazy)
+        L.template load_body<true>(0, ln, raw);
+    else
+        L.template load_chunk<true>(0, ln, raw, vidx);
     for (uint32_t c = 0; c < nch; ++c) {
         uint32_t cur[K], cv[Rg::kU];
 #pragma unroll
         for (int j = 0; j < K; ++j) cur[j] = raw[j];
-#pragma unroll
-        for (int u = 0; u < Rg::kU; ++u) cv[u] = vidx[u];
         const bool s0 = sv && c == 0;  // this lane carries a head/tail key now
-        if (c + 1 < nch) L.template load_chunk<true>(c + 1, ln, raw, vidx);  // prefetch
+        if constexpr (kLazy) {
+            // 16-bit keys: unchecked loads for full chunks, the element
+            // indices computed from c (they are needed only where keys pass).
+            if (c + 1 < nch) L.template load_body<true>(c + 1, ln, raw);  // prefetch
+#pragma unroll
+            for (int u = 0; u < Rg::kU; ++u) cv[u] = L.vec_idx(c, ln, u);
+        } else {
+#pragma unroll
+            for (int u = 0; u < Rg::kU; ++u) cv[u] = vidx[u];
+            if (c + 1 < nch) L.template load_chunk<true>(c + 1, ln, raw, vidx);  // prefetch
+        }
 
         if (sh.gearly) {
             // Adopt a tighter bound found by another wave of this workgroup
@@ -724,9 +770,22 @@ __device__ __forceinline__ Pass0 wave_pass0(uint32_t *hist, uint2 *stash, uint32
         // chunk can be within the bound; only then are the keys tested one
         // by one, and only a key position in which some lane passes takes
         // the exact rank test, the count and the stash push.
-        const bool cp = pf_chunk<KT>(pf, cur);
-        const bool sp = s0 && pf_key(pf, sx);
-        if (!__any(cp || sp)) continue;
+        // 16-bit keys test load by load, so that only the loads in which
+        // some lane passes have their key positions tested one by one.
+        bool lp[Rg::kU];
+        if constexpr (kLazy) {
+            bool cp = s0 && pf_key(pf, sx);
+#pragma unroll
+            for (int u = 0; u < Rg::kU; ++u) {
+                lp[u] = pf_chunk<KT>(pf, *reinterpret_cast<const uint32_t(*)[4]>(&cur[u * 4]));
+                cp = cp | lp[u];
+            }
+            if (!__any(cp)) continue;
+        } else {
+            const bool cp = pf_chunk<KT>(pf, cur);
+            const bool sp = s0 && pf_key(pf, sx);
+            if (!__any(cp || sp)) continue;
+        }
         bool ok = true;
         auto take = [&](uint32_t x, uint32_t idx, bool valid) {
             const bool pv = valid && pf_key(pf, x);
@@ -739,10 +798,13 @@ __device__ __forceinline__ Pass0 wave_pass0(uint32_t *hist, uint2 *stash, uint32
         };
         take(sx, si, s0);
 #pragma unroll
-        for (int u = 0; u < Rg::kU; ++u)
+        for (int u = 0; u < Rg::kU; ++u) {
+            if constexpr (kLazy)
+                if (!__any(lp[u])) continue;
 #pragma unroll
             for (int e = 0; e < V; ++e)
                 take(Rg::key_at(cur, u * V + e), cv[u] + (uint32_t)e, cv[u] != kNone);
+        }
         if (!ok) {
             // The stash is full even within the bound: drop it and read this
             // and every earlier chunk again later.
