@@ -133,10 +133,15 @@ typedef struct segtopk_values {
  *
  * The call is asynchronous: it validates the request, queues kernels on
  * `stream` and returns without waiting.  It never copies data to the host.
- * Internal scratch (only for batches with few, long segments) is taken from
- * the device's stream-ordered memory pool on `stream` and returned to it on
- * the same stream.  Outputs must not overlap the inputs.  Calls on different
- * streams are independent.
+ * Internal scratch (only for batches of fewer than 2048 segments) is one
+ * buffer per (device, stream), taken from the device's stream-ordered memory
+ * pool on `stream` the first time a call on that stream needs it and grown
+ * (the old buffer freed on `stream`) when a later call needs more.  Calls on
+ * one stream reuse it in stream order; it is held until the process ends.
+ * A stream handle that is destroyed and created again may inherit the buffer
+ * of its predecessor, which is safe because the old stream has no work left.
+ * Outputs must not overlap the inputs.  Calls on different streams are
+ * independent.
  *
  * Returns SEGTOPK_OK, or SEGTOPK_INVALID_ARGUMENT for a NULL required pointer,
  * an out-of-range enum, k or num_segments, values.in without values.out, or a

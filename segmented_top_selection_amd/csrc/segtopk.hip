@@ -8,7 +8,9 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <map>
 #include <mutex>
+#include <thread>
 
 #include "topk_common.h"
 
@@ -88,6 +90,63 @@ void prepare_pool(int dev) {
         (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &thr);
     }
     g_pool_ready[dev] = true;
+}
+
+// Scratch reused across the calls on one stream.  Stream order keeps the
+// calls on a stream from overlapping, so one buffer per (device, stream)
+// suffices; a stream-ordered malloc/free pair in every call made the host
+// wait for the device each time.  A call that needs more grows the buffer
+// (the old one is freed in stream order); buffers are held until the process
+// ends.  The per-thread default stream is one handle for many streams, so
+// that key also holds the calling thread.  Each buffer carries an event
+// recorded after its last use: a call first makes its stream wait for it,
+// so that a stream created with the handle of a destroyed one that still
+// has work queued cannot overlap that work.  The caller holds g_ws_mu from
+// stream_scratch until it has queued its kernels and recorded the event.
+struct WsKey {
+    int dev;
+    hipStream_t stream;
+    std::thread::id thread;
+    bool operator<(const WsKey &o) const {
+        if (dev != o.dev) return dev < o.dev;
+        if (stream != o.stream) return stream < o.stream;
+        return thread < o.thread;
+    }
+};
+struct WsBuf {
+    void *ptr = nullptr;
+    size_t bytes = 0;
+    hipEvent_t done = nullptr;
+};
+std::mutex g_ws_mu;
+std::map<WsKey, WsBuf> g_ws;
+
+hipError_t stream_scratch(int dev, hipStream_t stream, size_t bytes, WsBuf **out) {
+    const WsKey key{dev, stream,
+                    stream == hipStreamPerThread ? std::this_thread::get_id() : std::thread::id()};
+    WsBuf &b = g_ws[key];
+    if (!b.done) {
+        const hipError_t e = hipEventCreateWithFlags(&b.done, hipEventDisableTiming);
+        if (e != hipSuccess) {
+            b.done = nullptr;
+            return e;
+        }
+    } else {
+        const hipError_t e = hipStreamWaitEvent(stream, b.done, 0);
+        if (e != hipSuccess) return e;
+    }
+    if (b.bytes < bytes) {
+        size_t want = bytes + (bytes >> 2);
+        want = (want + ((size_t)1 << 20) - 1) & ~(((size_t)1 << 20) - 1);
+        void *np = nullptr;
+        const hipError_t e = hipMallocAsync(&np, want, stream);
+        if (e != hipSuccess) return e;
+        if (b.ptr) (void)hipFreeAsync(b.ptr, stream);
+        b.ptr = np;
+        b.bytes = want;
+    }
+    *out = &b;
+    return hipSuccess;
 }
 
 // Workgroups of the split kernel of (key type, direction) that the device
@@ -233,14 +292,18 @@ extern "C" int batched_topk(const segtopk_keys *keys, const segtopk_values *valu
     if (grid > 0x7FFFFFFFull) return SEGTOPK_NOT_SUPPORTED;
 
     void *ws = nullptr;
+    WsBuf *wsb = nullptr;
+    std::unique_lock<std::mutex> ws_lock(g_ws_mu, std::defer_lock);
     hipError_t err = hipSuccess;
     if (split && P == 1 && num_segments >= kOrderMinSegments) {
         // One workgroup per segment for many segments of unknown sizes:
         // process the largest first.
         if (hipGetDevice(&dev) != hipSuccess) return SEGTOPK_HIP_ERROR;
         prepare_pool(dev);
-        if (hipMallocAsync(&ws, (size_t)num_segments * sizeof(uint32_t), stream) != hipSuccess)
+        ws_lock.lock();
+        if (stream_scratch(dev, stream, (size_t)num_segments * sizeof(uint32_t), &wsb) != hipSuccess)
             return SEGTOPK_HIP_ERROR;
+        ws = wsb->ptr;
         p.order = static_cast<const uint32_t *>(ws);
         hipLaunchKernelGGL(order_kernel, dim3(1), dim3(1024), 0, stream, segment_offsets,
                            num_segments, static_cast<uint32_t *>(ws));
@@ -256,7 +319,9 @@ extern "C" int batched_topk(const segtopk_keys *keys, const segtopk_values *valu
         bytes = (bytes + 255) & ~(size_t)255;
         const size_t data_off = bytes;
         bytes += S * P * (size_t)stash_cap * sizeof(uint2);
-        if (hipMallocAsync(&ws, bytes, stream) != hipSuccess) return SEGTOPK_HIP_ERROR;
+        ws_lock.lock();
+        if (stream_scratch(dev, stream, bytes, &wsb) != hipSuccess) return SEGTOPK_HIP_ERROR;
+        ws = wsb->ptr;
         uint32_t *wsw = static_cast<uint32_t *>(ws);
         p.ws_hist = wsw;
         p.ws_early = wsw + n_hist;
@@ -273,8 +338,9 @@ extern "C" int batched_topk(const segtopk_keys *keys, const segtopk_values *valu
         const bool largest = direction == SEGTOPK_MAX;
         err = launch(type, p, largest, split, (uint32_t)grid, lds, stream);
     }
-    if (ws) {
-        if (hipFreeAsync(ws, stream) != hipSuccess && err == hipSuccess) err = hipErrorUnknown;
+    if (wsb) {
+        const hipError_t e = hipEventRecord(wsb->done, stream);
+        if (err == hipSuccess) err = e;
     }
     return err == hipSuccess ? SEGTOPK_OK : SEGTOPK_HIP_ERROR;
 }

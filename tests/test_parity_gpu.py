@@ -13,7 +13,7 @@ import pytest
 import torch
 
 import workloads
-from parity import check, run_gpu, KEY_CANARY
+from parity import check, key_bits_np, run_gpu, KEY_CANARY
 
 pytestmark = pytest.mark.gpu
 
@@ -478,3 +478,55 @@ def test_ordered_one_workgroup_per_segment(key_type):
                     for ordering in ("unsorted", "stable_sorted"):
                         check(keys, vals, off, k, key_type, largest, det, tb, ordering,
                               values_are="position")
+
+
+def test_scratch_reuse_across_streams():
+    # Plans that take internal scratch (several workgroups per segment; the
+    # largest-first order) reuse one buffer per stream, grown on demand.
+    # Three problems, each first checked against the oracle on the current
+    # stream, then queued back to back on two streams with no synchronisation
+    # between calls (larger and smaller scratch in turn on each stream): every
+    # result must equal the checked one bit for bit (as a set of (key, value)
+    # pairs per row where the output order is unspecified).
+    import segmented_top_selection_amd as st
+    probs = [
+        _workload("uniform_u32_32x4Mi_k2048", num_segments=4, seg_len=1 << 20),   # slice mode
+        _workload("normal10_f32_32x4Mi_k2048", num_segments=2, seg_len=1 << 18),  # slice mode, less
+        _workload("quantized_f32_1024xU65536_k256", num_segments=300),           # largest first
+    ]
+    expect = []
+    for w, keys, vals, off in probs:
+        gk, gv = check(keys, vals, off, w["k"], w["key_type"], w["largest"], w["determinism"],
+                       w["tie_break"], w["ordering"])
+        expect.append((gk, gv))
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    plan = [(0, 0), (1, 2), (0, 1), (1, 0), (0, 2), (1, 1), (0, 0)]
+    outs = []
+    torch.cuda.synchronize()
+    for si, pi in plan:
+        w, keys, vals, off = probs[pi]
+        s = off.numel() - 1
+        with torch.cuda.stream(streams[si]):
+            ok = torch.empty((s, w["k"]), dtype=keys.dtype, device=DEV)
+            ov = torch.empty((s, w["k"]), dtype=torch.int32, device=DEV) if vals is not None else None
+            st.batched_topk(keys, off, w["k"], values=vals, largest=w["largest"],
+                            determinism=w["determinism"], tie_break=w["tie_break"],
+                            ordering=w["ordering"], key_type=w["key_type"], out_keys=ok,
+                            out_values=ov, stream=streams[si])
+        outs.append((pi, ok, ov))
+    torch.cuda.synchronize()
+    for pi, ok, ov in outs:
+        gk, gv = expect[pi]
+        w, keys, _, off = probs[pi]
+        s = off.numel() - 1
+        sizes = (off[1:] - off[:-1]).cpu().numpy()
+        bits = key_bits_np(ok).reshape(s, w["k"])
+        vbits = ov.cpu().numpy().view(np.uint32).reshape(s, w["k"]) if ov is not None else None
+        for r in range(s):
+            n = min(int(sizes[r]), w["k"])
+            got = [bits[r, :n], vbits[r, :n] if vbits is not None else np.zeros(n, np.uint32)]
+            ref = [gk[r, :n], gv[r, :n] if gv is not None else np.zeros(n, np.uint32)]
+            if w["ordering"] == "unsorted":  # the order within a row is not specified
+                got = [a[np.lexsort((got[1], got[0]))] for a in got]
+                ref = [a[np.lexsort((ref[1], ref[0]))] for a in ref]
+            assert np.array_equal(got[0], ref[0]) and np.array_equal(got[1], ref[1]), (pi, r)
