@@ -649,6 +649,29 @@ __device__ __forceinline__ Pass0 wave_pass0(uint32_t *hist, uint2 *stash, uint32
     // anything.
     constexpr bool kLazy = Key<KT>::kBytes == 2;
     uint32_t below = 0, nbelow = 0;
+    // 16-bit keys also defer the histogram counts of the keys they stash:
+    // stash entries [flushed, count) are not counted yet, and flush() counts
+    // them 64 at a time, with every lane busy, instead of one sparse atomic
+    // per passing key position.  A key position only appends to the stash
+    // while there is room; a key that finds none is counted at once and the
+    // stash is dropped after the chunk.  Counts are flushed after a chunk
+    // before a rescan of the bound, a compaction or a drop, and at the end of
+    // the stream; until then the histogram only undercounts, and any bound
+    // found from an undercount is still valid.
+    uint32_t flushed = 0;
+    uint32_t compR = kBuckets;  // the bound at the last compaction
+    auto flush = [&]() {
+        for (uint32_t base = flushed; base < r.count; base += kWave) {
+            const uint32_t i = base + ln;
+            uint32_t rk = kBuckets;
+            if (i < r.count) {
+                rk = rank0<KT, LARGEST>(Key<KT>::ord(stash[i].x));
+                atomicAdd(&hist[rk], 1u);
+            }
+            nbelow += (uint32_t)__popcll(__ballot(rk < r.R));
+        }
+        flushed = r.count;
+    };
 
     // The unaligned head and tail ride along with chunk 0.
     const bool sv = ln < L.nscalar;
@@ -762,6 +785,7 @@ __device__ __forceinline__ Pass0 wave_pass0(uint32_t *hist, uint2 *stash, uint32
                         stash[pos++] = make_uint2(x, cv[u] + (uint32_t)e);
                 }
             r.count += total;
+            if constexpr (kLazy) flushed = r.count;  // counted above already
             r.defer = c;
             continue;
         }
@@ -790,6 +814,24 @@ __device__ __forceinline__ Pass0 wave_pass0(uint32_t *hist, uint2 *stash, uint32
         auto take = [&](uint32_t x, uint32_t idx, bool valid) {
             const bool pv = valid && pf_key(pf, x);
             if (!__any(pv)) return;
+            if constexpr (kLazy) {
+                // The bound test is exact, so pv already means rank <= R.
+                if (ok) {
+                    const uint64_t m = __ballot(pv);
+                    const uint32_t n = (uint32_t)__popcll(m);
+                    if (r.count + n <= cap) {
+                        if (pv) stash[r.count + lanes_below(m)] = make_uint2(x, idx);
+                        r.count += n;
+                        return;
+                    }
+                    ok = false;
+                }
+                // Not stashed (the stash is dropped after this chunk): count now.
+                const uint32_t rk = rank0<KT, LARGEST>(Key<KT>::ord(x));
+                if (pv) atomicAdd(&hist[rk], 1u);
+                nbelow += (uint32_t)__popcll(__ballot(pv && rk < r.R));
+                return;
+            }
             const uint32_t rk = rank0<KT, LARGEST>(Key<KT>::ord(x));
             const bool ex = pv && rk <= r.R;
             if (ex) atomicAdd(&hist[rk], 1u);
@@ -805,11 +847,29 @@ __device__ __forceinline__ Pass0 wave_pass0(uint32_t *hist, uint2 *stash, uint32
             for (int e = 0; e < V; ++e)
                 take(Rg::key_at(cur, u * V + e), cv[u] + (uint32_t)e, cv[u] != kNone);
         }
+        if constexpr (kLazy) {
+            // One place for the deferred counts: before a drop, before a
+            // compaction (the stash half full and the bound tighter than at
+            // the last one), and when the bound may move (unflushed entries
+            // bound the uncounted keys before its bucket).
+            const bool half = r.count > cap / 2u && r.R < compR;
+            if (!ok || half ||
+                below + (uint32_t)kWaves * (nbelow + (r.count - flushed)) >= target) {
+                flush();
+                if (ok && half) {
+                    wave_sync();
+                    r.count = wave_compact<KT, LARGEST>(stash, r.count, pf);
+                    flushed = r.count;
+                    compR = r.R;
+                }
+            }
+        }
         if (!ok) {
             // The stash is full even within the bound: drop it and read this
             // and every earlier chunk again later.
             r.count = 0;
             r.defer = c + 1;
+            if constexpr (kLazy) flushed = 0;
         }
         if (nbelow != 0 && (!kLazy || below + (uint32_t)kWaves * nbelow >= target)) {
             // The bound may move: recompute it from everything counted.
@@ -825,6 +885,7 @@ __device__ __forceinline__ Pass0 wave_pass0(uint32_t *hist, uint2 *stash, uint32
             }
         }
     }
+    if constexpr (kLazy) flush();
     r.nch = nch;
     return r;
 }
