@@ -3,6 +3,6 @@
 #include "topk_kernel.h"
 
 namespace segtopk_impl {
-template hipError_t launch_topk<SEGTOPK_KEY_I32>(const Params &, bool, bool, uint32_t, size_t, hipStream_t);
+template hipError_t launch_topk<SEGTOPK_KEY_I32>(const Params &, bool, int, uint32_t, size_t, hipStream_t);
 template int topk_per_cu<SEGTOPK_KEY_I32>(bool, size_t);
 }  // namespace segtopk_impl

@@ -189,14 +189,14 @@ uint32_t resident_wgs_for(int type, int dev, bool largest, size_t lds) {
     return wgs;
 }
 
-hipError_t launch(int type, const Params &p, bool largest, bool split, uint32_t grid, size_t lds,
+hipError_t launch(int type, const Params &p, bool largest, int variant, uint32_t grid, size_t lds,
                   hipStream_t st) {
     switch (type) {
-    case SEGTOPK_KEY_F32: return launch_topk<SEGTOPK_KEY_F32>(p, largest, split, grid, lds, st);
-    case SEGTOPK_KEY_BF16: return launch_topk<SEGTOPK_KEY_BF16>(p, largest, split, grid, lds, st);
-    case SEGTOPK_KEY_U32: return launch_topk<SEGTOPK_KEY_U32>(p, largest, split, grid, lds, st);
-    case SEGTOPK_KEY_I32: return launch_topk<SEGTOPK_KEY_I32>(p, largest, split, grid, lds, st);
-    default: return launch_topk<SEGTOPK_KEY_F16>(p, largest, split, grid, lds, st);
+    case SEGTOPK_KEY_F32: return launch_topk<SEGTOPK_KEY_F32>(p, largest, variant, grid, lds, st);
+    case SEGTOPK_KEY_BF16: return launch_topk<SEGTOPK_KEY_BF16>(p, largest, variant, grid, lds, st);
+    case SEGTOPK_KEY_U32: return launch_topk<SEGTOPK_KEY_U32>(p, largest, variant, grid, lds, st);
+    case SEGTOPK_KEY_I32: return launch_topk<SEGTOPK_KEY_I32>(p, largest, variant, grid, lds, st);
+    default: return launch_topk<SEGTOPK_KEY_F16>(p, largest, variant, grid, lds, st);
     }
 }
 
@@ -336,7 +336,8 @@ extern "C" int batched_topk(const segtopk_keys *keys, const segtopk_values *valu
     }
     if (err == hipSuccess) {
         const bool largest = direction == SEGTOPK_MAX;
-        err = launch(type, p, largest, split, (uint32_t)grid, lds, stream);
+        const int variant = !split ? kVariantOne : (P > 1 ? kVariantSliced : kVariantSplit);
+        err = launch(type, p, largest, variant, (uint32_t)grid, lds, stream);
     }
     if (wsb) {
         const hipError_t e = hipEventRecord(wsb->done, stream);

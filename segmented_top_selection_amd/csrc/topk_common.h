@@ -50,11 +50,17 @@ struct Params {
     const uint32_t *order;   // [segments] processing order (one workgroup each), or nullptr
 };
 
+// Kernel variants: one workgroup per segment for many segments (4 loads per
+// lane); the plan for fewer segments (8 loads per lane) with one workgroup
+// per segment; and the same with several workgroups per segment (slices).
+constexpr int kVariantOne = 0;
+constexpr int kVariantSplit = 1;
+constexpr int kVariantSliced = 2;
+
 // Launches the top-k kernel for key type KT on `st`: grid workgroups of
-// kThreads threads with `lds` bytes of dynamic LDS.  `split` selects the
-// variant for segments spread over several workgroups.
+// kThreads threads with `lds` bytes of dynamic LDS, in the given variant.
 template <int KT>
-hipError_t launch_topk(const Params &p, bool largest, bool split, uint32_t grid, size_t lds,
+hipError_t launch_topk(const Params &p, bool largest, int variant, uint32_t grid, size_t lds,
                        hipStream_t st);
 
 // Workgroups of the split variant of that kernel that fit on one CU of the

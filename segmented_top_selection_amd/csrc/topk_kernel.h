@@ -619,8 +619,9 @@ __device__ __forceinline__ bool wave_push(uint2 *stash, uint32_t cap, uint32_t &
 // bucket is within the running bound R, which only tightens.  Chunks that were
 // counted but not stashed (before the bound, or dropped when the stash
 // overflowed) are read again by wave_reread once the workgroup's bound is
-// final.
-template <int KT, bool LARGEST, int U>
+// final.  SLICED: the variant for slices of a segment shared by several
+// workgroups (see kLazy below).
+template <int KT, bool LARGEST, int U, bool SLICED>
 __device__ __forceinline__ Pass0 wave_pass0(uint32_t *hist, uint2 *stash, uint32_t cap,
                                             const void *keys, int64_t begin, uint32_t lo,
                                             uint32_t hi, uint32_t target, const Share &sh) {
@@ -645,9 +646,12 @@ __device__ __forceinline__ Pass0 wave_pass0(uint32_t *hist, uint2 *stash, uint32
     // scan waits for that (taking the other waves to count about as many as
     // this one).  The 2-mantissa-bit buckets of 16-bit floats keep the bound
     // in one bucket for most of a long stream, and this saves a scan per
-    // chunk there.  32-bit keys rescan after every chunk that counted
-    // anything.
-    constexpr bool kLazy = Key<KT>::kBytes == 2;
+    // chunk there; so do the long slices of slice mode (f32 keys have the
+    // same 2 mantissa bits in the pass-0 digit).  Otherwise 32-bit keys
+    // rescan after every chunk that counted anything: with one workgroup per
+    // segment the deferred path measured slower for them (code generation of
+    // the whole kernel, not the extra work).
+    constexpr bool kLazy = Key<KT>::kBytes == 2 || SLICED;
     uint32_t below = 0, nbelow = 0;
     // 16-bit keys also defer the histogram counts of the keys they stash:
     // stash entries [flushed, count) are not counted yet, and flush() counts
@@ -942,11 +946,11 @@ __device__ __forceinline__ bool wave_reread(uint2 *stash, uint32_t cap, uint32_t
 // that the re-read overlaps the other waves' streaming instead of following
 // the workgroup barrier.  If they do not fit, every chunk stays deferred and
 // is read again after the barrier under the workgroup's bound.
-template <int KT, bool LARGEST, int U>
+template <int KT, bool LARGEST, int U, bool SLICED>
 __device__ __forceinline__ Pass0 wave_pass0_stash(uint32_t *hist, uint2 *stash, uint32_t cap,
                                                   const void *keys, int64_t begin, uint32_t lo,
                                                   uint32_t hi, uint32_t target, const Share &sh) {
-    Pass0 r = wave_pass0<KT, LARGEST, U>(hist, stash, cap, keys, begin, lo, hi, target, sh);
+    Pass0 r = wave_pass0<KT, LARGEST, U, SLICED>(hist, stash, cap, keys, begin, lo, hi, target, sh);
     if (r.defer != 0) {
         uint32_t cnt = r.count;
         if (wave_reread<KT, LARGEST, U>(stash, cap, cnt, keys, begin, lo, hi, r.defer, r.R)) {
@@ -1860,7 +1864,7 @@ template <int KT, int U> constexpr int topk_waves() {
     return U == 4 ? (Key<KT>::kBytes == 4 ? 6 : 4) : (Key<KT>::kBytes == 4 ? 3 : 2);
 }
 
-template <int KT, bool LARGEST, int U>
+template <int KT, bool LARGEST, int U, bool SLICED>
 __global__ __launch_bounds__(kThreads, (topk_waves<KT, U>())) void topk_kernel(Params p) {
     __shared__ Shared sh;
     extern __shared__ uint4 dyn[];
@@ -1929,7 +1933,7 @@ __global__ __launch_bounds__(kThreads, (topk_waves<KT, U>())) void topk_kernel(P
     share.gearly = ps > 1 ? p.ws_early + (size_t)s * kBuckets : nullptr;
     share.glast = ps > 1 ? p.ws_slot_cum + ((size_t)s * P + q) * kBuckets : nullptr;
     share.wave = w;
-    const Pass0 r0 = wave_pass0_stash<KT, LARGEST, U>(sh.hist, stash + w * capw, capw, p.keys_in,
+    const Pass0 r0 = wave_pass0_stash<KT, LARGEST, U, SLICED>(sh.hist, stash + w * capw, capw, p.keys_in,
                                                    sg.begin, wlo, whi, sg.k_i, share);
     if (ln == 0) {
         sh.wcount[w] = r0.count;
@@ -2099,29 +2103,32 @@ template <typename K> hipError_t allow_lds(K kernel, size_t lds) {
                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxDynLds);
 }
 
-template <int KT, bool LARGEST, int U>
+template <int KT, bool LARGEST, int U, bool SLICED>
 hipError_t launch_u(const Params &p, uint32_t grid, size_t lds, hipStream_t st) {
     hipError_t e;
-    if ((e = allow_lds(topk_kernel<KT, LARGEST, U>, lds)) != hipSuccess) return e;
-    hipLaunchKernelGGL((topk_kernel<KT, LARGEST, U>), dim3(grid), dim3(kThreads), lds, st, p);
+    if ((e = allow_lds(topk_kernel<KT, LARGEST, U, SLICED>, lds)) != hipSuccess) return e;
+    hipLaunchKernelGGL((topk_kernel<KT, LARGEST, U, SLICED>), dim3(grid), dim3(kThreads), lds, st, p);
     return hipGetLastError();
 }
 
 }  // namespace
 
 template <int KT>
-hipError_t launch_topk(const Params &p, bool largest, bool split, uint32_t grid, size_t lds,
+hipError_t launch_topk(const Params &p, bool largest, int variant, uint32_t grid, size_t lds,
                        hipStream_t st) {
-    if (largest)
-        return split ? launch_u<KT, true, kSplitU>(p, grid, lds, st)
-                     : launch_u<KT, true, 4>(p, grid, lds, st);
-    return split ? launch_u<KT, false, kSplitU>(p, grid, lds, st)
-                 : launch_u<KT, false, 4>(p, grid, lds, st);
+    if (largest) {
+        if (variant == kVariantSliced) return launch_u<KT, true, kSplitU, true>(p, grid, lds, st);
+        return variant == kVariantSplit ? launch_u<KT, true, kSplitU, false>(p, grid, lds, st)
+                                        : launch_u<KT, true, 4, false>(p, grid, lds, st);
+    }
+    if (variant == kVariantSliced) return launch_u<KT, false, kSplitU, true>(p, grid, lds, st);
+    return variant == kVariantSplit ? launch_u<KT, false, kSplitU, false>(p, grid, lds, st)
+                                    : launch_u<KT, false, 4, false>(p, grid, lds, st);
 }
 
 template <int KT> int topk_per_cu(bool largest, size_t lds) {
-    const void *fn = largest ? reinterpret_cast<const void *>(topk_kernel<KT, true, kSplitU>)
-                             : reinterpret_cast<const void *>(topk_kernel<KT, false, kSplitU>);
+    const void *fn = largest ? reinterpret_cast<const void *>(topk_kernel<KT, true, kSplitU, true>)
+                             : reinterpret_cast<const void *>(topk_kernel<KT, false, kSplitU, true>);
     if (lds > 64 * 1024)
         (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxDynLds);
     int per_cu = 0;
