@@ -530,3 +530,36 @@ def test_scratch_reuse_across_streams():
                 got = [a[np.lexsort((got[1], got[0]))] for a in got]
                 ref = [a[np.lexsort((ref[1], ref[0]))] for a in ref]
             assert np.array_equal(got[0], ref[0]) and np.array_equal(got[1], ref[1]), (pi, r)
+
+
+def test_heavy_ties_long_segments_bf16():
+    """16-bit keys whose passing keys overflow the stash: the deferred counts
+    are flushed before the stash is dropped or compacted.  2048 segments (one
+    workgroup each; the oracle checks sampled rows) and 3 long segments
+    (several workgroups each)."""
+    rng = np.random.default_rng(12)
+
+    def pattern(r, n):
+        kind = r % 4
+        if kind == 0:
+            return np.full(n, 2.0)                              # all equal
+        if kind == 1:
+            return rng.integers(0, 3, n) * 1.0                  # three levels
+        if kind == 2:
+            return np.where(rng.random(n) < 0.5, 0.0, -0.0)     # +0 and -0
+        return np.round(rng.normal(0, 3, n) * 4) / 4            # coarse normal
+
+    for count, n, rows in ((2048, 16384, [0, 1, 2, 3, 1001, 1002, 2046, 2047]),
+                           (3, 200000, None)):
+        segs = [pattern(r, n) for r in range(count)]
+        t = torch.tensor(np.concatenate(segs))
+        keys = t.to(torch.bfloat16).to(DEV)
+        off = torch.tensor(np.cumsum([0] + [n] * count), dtype=torch.int64, device=DEV)
+        vals = index_values(off)
+        say(f"[heavy ties bf16] {count} x {n}")
+        for k in (50, 2000):
+            for largest in (True, False):
+                for det, tb in MODES:
+                    check(keys, vals, off, k, "bf16", largest, det, tb, "unsorted", rows=rows)
+        del keys, vals, off, t
+        torch.cuda.empty_cache()
