@@ -117,6 +117,9 @@ struct WsBuf {
     void *ptr = nullptr;
     size_t bytes = 0;
     hipEvent_t done = nullptr;
+    // Leading 32-bit words that are zero once the stream's queued work is
+    // done: slice mode leaves its histograms and tickets cleared again.
+    size_t clean_words = 0;
 };
 std::mutex g_ws_mu;
 std::map<WsKey, WsBuf> g_ws;
@@ -144,6 +147,7 @@ hipError_t stream_scratch(int dev, hipStream_t stream, size_t bytes, WsBuf **out
         if (b.ptr) (void)hipFreeAsync(b.ptr, stream);
         b.ptr = np;
         b.bytes = want;
+        b.clean_words = 0;
     }
     *out = &b;
     return hipSuccess;
@@ -293,6 +297,7 @@ extern "C" int batched_topk(const segtopk_keys *keys, const segtopk_values *valu
 
     void *ws = nullptr;
     WsBuf *wsb = nullptr;
+    size_t zero_words_used = 0;
     std::unique_lock<std::mutex> ws_lock(g_ws_mu, std::defer_lock);
     hipError_t err = hipSuccess;
     if (split && P == 1 && num_segments >= kOrderMinSegments) {
@@ -304,6 +309,7 @@ extern "C" int batched_topk(const segtopk_keys *keys, const segtopk_values *valu
         if (stream_scratch(dev, stream, (size_t)num_segments * sizeof(uint32_t), &wsb) != hipSuccess)
             return SEGTOPK_HIP_ERROR;
         ws = wsb->ptr;
+        wsb->clean_words = 0;  // the order overwrites the front
         p.order = static_cast<const uint32_t *>(ws);
         hipLaunchKernelGGL(order_kernel, dim3(1), dim3(1024), 0, stream, segment_offsets,
                            num_segments, static_cast<uint32_t *>(ws));
@@ -313,6 +319,7 @@ extern "C" int batched_topk(const segtopk_keys *keys, const segtopk_values *valu
         const size_t S = (size_t)num_segments;
         const size_t n_hist = S * kBuckets, n_ticket = S;
         const size_t zero_words = 2 * n_hist + n_ticket;
+        zero_words_used = zero_words;
         const size_t info_words = S * P * 4;
         const size_t cum_words = S * P * kBuckets;
         size_t bytes = (zero_words + info_words + cum_words) * 4;
@@ -329,15 +336,21 @@ extern "C" int batched_topk(const segtopk_keys *keys, const segtopk_values *valu
         p.ws_slot_info = wsw + zero_words;
         p.ws_slot_cum = wsw + zero_words + info_words;
         p.ws_slot_data = reinterpret_cast<uint2 *>(static_cast<char *>(ws) + data_off);
-        size_t zb = (zero_words + 255) / 256;
-        if (zb > 1024) zb = 1024;
-        hipLaunchKernelGGL(zero_kernel, dim3((unsigned)zb), dim3(256), 0, stream, wsw, zero_words);
-        err = hipGetLastError();
+        if (wsb->clean_words < zero_words) {
+            size_t zb = (zero_words + 255) / 256;
+            if (zb > 1024) zb = 1024;
+            hipLaunchKernelGGL(zero_kernel, dim3((unsigned)zb), dim3(256), 0, stream, wsw, zero_words);
+            err = hipGetLastError();
+        }
+        // The slots (after the cleared words) are written by this call; the
+        // sliced kernel clears the histograms and tickets it used.
+        wsb->clean_words = 0;
     }
     if (err == hipSuccess) {
         const bool largest = direction == SEGTOPK_MAX;
         const int variant = !split ? kVariantOne : (P > 1 ? kVariantSliced : kVariantSplit);
         err = launch(type, p, largest, variant, (uint32_t)grid, lds, stream);
+        if (err == hipSuccess && variant == kVariantSliced) wsb->clean_words = zero_words_used;
     }
     if (wsb) {
         const hipError_t e = hipEventRecord(wsb->done, stream);

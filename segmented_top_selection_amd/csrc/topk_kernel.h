@@ -1593,7 +1593,10 @@ __device__ __forceinline__ void block_finish(Shared &sh, uint2 *outbuf, const Pa
 // entries up to b* (a prefix, as the slots are sorted by bucket): those of
 // better buckets are winners and are written at once, those of b* go to the
 // LDS list for the remaining passes (wave 0).
-template <int KT, bool LARGEST>
+// CLEAN: once the merged histogram is in LDS, the segment's scratch words
+// that a call expects zero (merged and shared histograms, ticket) are cleared
+// again, so that the next call on the same scratch needs no clearing pass.
+template <int KT, bool LARGEST, bool CLEAN>
 __device__ __forceinline__ void slice_last(Shared &sh, uint2 *stash, uint2 *outbuf,
                                            const Params &p, const Seg &sg, int64_t s, uint32_t P,
                                            uint32_t ps, uint32_t slice) {
@@ -1612,6 +1615,16 @@ __device__ __forceinline__ void slice_last(Shared &sh, uint2 *stash, uint2 *outb
         for (uint32_t i = threadIdx.x; i < (uint32_t)kBuckets / 4; i += kThreads) h4[i] = g4[i];
     }
     __syncthreads();
+    if constexpr (CLEAN) {
+        // Every other slice has taken its ticket: none reads these any more.
+        uint4 *m4 = reinterpret_cast<uint4 *>(p.ws_hist + (size_t)s * kBuckets);
+        uint4 *e4 = reinterpret_cast<uint4 *>(p.ws_early + (size_t)s * kBuckets);
+        for (uint32_t i = threadIdx.x; i < (uint32_t)kBuckets / 4; i += kThreads) {
+            m4[i] = make_uint4(0u, 0u, 0u, 0u);
+            e4[i] = make_uint4(0u, 0u, 0u, 0u);
+        }
+        if (threadIdx.x == 0) p.ws_ticket[s] = 0u;
+    }
     const Kth ks = wave_find(sh.hist, kBuckets, sg.k_i);  // alike in every wave
     __syncthreads();
 
@@ -1978,7 +1991,7 @@ __global__ __launch_bounds__(kThreads, (topk_waves<KT, U>())) void topk_kernel(P
         }
         if (!sh.last) return;
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        slice_last<KT, LARGEST>(sh, stash, outbuf, p, sg, s, P, ps, slice);
+        slice_last<KT, LARGEST, SLICED>(sh, stash, outbuf, p, sg, s, P, ps, slice);
         return;
     }
 
@@ -2093,7 +2106,7 @@ __global__ __launch_bounds__(kThreads, (topk_waves<KT, U>())) void topk_kernel(P
     __syncthreads();  // pairs with the one the other waves wait in
     if (!last) return;
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    slice_last<KT, LARGEST>(sh, stash, outbuf, p, sg, s, P, ps, slice);
+    slice_last<KT, LARGEST, SLICED>(sh, stash, outbuf, p, sg, s, P, ps, slice);
 }
 
 // Dynamic LDS above 64 KiB has to be allowed per kernel.
