@@ -191,3 +191,31 @@ def check(keys, values, offsets, k, key_type, largest=True, determinism="gpu_to_
         gv = gv[np.asarray(rows)] if gv is not None else None
     compare(gk, gv, ok, ov, sub_off, k, key_type, determinism, ordering, kb, values_are)
     return gk, gv
+
+
+def check_all_rows(keys, values, offsets, k, key_type, largest=True, determinism="gpu_to_gpu",
+                   tie_break="prefer_smaller_index", ordering="stable_sorted", chunk_rows=1024,
+                   say=None):
+    """One GPU call over the whole batch, then EVERY row compared with the
+    oracle, in blocks of ``chunk_rows`` consecutive rows so that host memory
+    stays bounded (segments must be laid out in order, as every workload's
+    are).  Returns the number of rows compared."""
+    gk, gv = run_gpu(keys, values, offsets, k, key_type, largest, determinism, tie_break,
+                     ordering)
+    off = offsets.cpu().numpy()
+    s = off.shape[0] - 1
+    for r0 in range(0, s, chunk_rows):
+        r1 = min(s, r0 + chunk_rows)
+        b, e = int(off[r0]), int(off[r1])
+        assert np.all(np.diff(off[r0:r1 + 1]) >= 0), "check_all_rows needs ordered offsets"
+        kb = key_bits_np(keys[b:e])
+        vb = values[b:e].cpu().numpy().view(np.uint32) if values is not None else None
+        sub_off = off[r0:r1 + 1] - b
+        ok, ov = run_oracle(kb, vb, sub_off, k, key_type, largest,
+                            tie_break == "prefer_larger_index")
+        compare(gk[r0:r1], gv[r0:r1] if gv is not None else None, ok, ov, sub_off, k,
+                key_type, determinism, ordering, kb)
+        if say is not None and (r1 == s or (r0 // chunk_rows) % 4 == 0):
+            say(f"  rows [{r0}, {r1}) of {s} equal the oracle")
+        del kb, vb, ok, ov
+    return s

@@ -13,7 +13,7 @@ import pytest
 import torch
 
 import workloads
-from parity import check, key_bits_np, run_gpu, KEY_CANARY
+from parity import check, check_all_rows, key_bits_np, run_gpu, KEY_CANARY
 
 pytestmark = pytest.mark.gpu
 
@@ -92,8 +92,8 @@ def test_worked_example(key_type):
 
 
 # ---------------------------------------------------------------------------
-# The benchmark workloads (full size where the oracle keeps up, else sampled
-# rows), each in its own request mode.
+# The benchmark workloads, each in its own request mode: every row at full
+# size, plus reduced shapes that take the other plans.
 # ---------------------------------------------------------------------------
 def _workload(name, **shape):
     w = workloads.WORKLOADS[name]
@@ -129,15 +129,12 @@ def test_quantized_reduced_multi_workgroup():
     _run_workload("quantized_f32_1024xU65536_k256", num_segments=96)
 
 
-def test_quantized_full_sampled():
+def test_quantized_full_every_row():
     w, keys, vals, off = _workload("quantized_f32_1024xU65536_k256")
-    sizes = (off[1:] - off[:-1]).cpu().numpy()
-    rng = np.random.default_rng(0)
-    rows = sorted(set(rng.choice(len(sizes), 48, replace=False).tolist()
-                      + np.argsort(sizes)[-4:].tolist() + np.argsort(sizes)[:4].tolist()))
-    say(f"[quantized full] rows {rows[:8]}...")
-    check(keys, vals, off, w["k"], w["key_type"], w["largest"], w["determinism"],
-          w["tie_break"], w["ordering"], rows=rows)
+    say(f"[quantized full] segments={off.numel() - 1} keys={keys.numel()}")
+    n = check_all_rows(keys, vals, off, w["k"], w["key_type"], w["largest"], w["determinism"],
+                       w["tie_break"], w["ordering"], say=say)
+    assert n == 1024
 
 
 @pytest.mark.parametrize("name", ["uniform_u32_32x4Mi_k2048", "normal10_f32_32x4Mi_k2048"])
@@ -146,17 +143,55 @@ def test_large_segments_reduced(name):
 
 
 @pytest.mark.parametrize("name", ["uniform_u32_32x4Mi_k2048", "normal10_f32_32x4Mi_k2048"])
-def test_large_segments_full_sampled(name):
-    _run_workload(name, rows=[0, 13, 31])
+def test_large_segments_full_every_row(name):
+    w, keys, vals, off = _workload(name)
+    say(f"[{name}] full size, every row")
+    n = check_all_rows(keys, vals, off, w["k"], w["key_type"], w["largest"], w["determinism"],
+                       w["tie_break"], w["ordering"], chunk_rows=8, say=say)
+    assert n == 32
+    del keys, vals, off
+    torch.cuda.empty_cache()
 
 
 def test_logits_bf16_reduced():
     _run_workload("logits_bf16_16384x128Ki_k50", num_segments=256)
 
 
-def test_logits_bf16_full_sampled():
-    rows = [0, 1, 777, 8191, 12345, 16383]
-    _run_workload("logits_bf16_16384x128Ki_k50", rows=rows)
+def test_logits_bf16_full_every_row():
+    """All 16384 rows of the full-size vocabulary-logit workload (2^31 keys),
+    compared in blocks of 1024 rows (multiset of key values plus validity of
+    every returned index, the not_guaranteed contract)."""
+    w, keys, vals, off = _workload("logits_bf16_16384x128Ki_k50")
+    say("[logits bf16] full size, every row")
+    n = check_all_rows(keys, vals, off, w["k"], w["key_type"], w["largest"], w["determinism"],
+                       w["tie_break"], w["ordering"], chunk_rows=1024, say=say)
+    assert n == 16384
+    del keys, vals, off
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("variant", ["normal", "tied"])
+def test_logits_bf16_2048x128Ki_every_row_all_modes(variant):
+    """2048 segments of 131072 bf16 keys (the one-workgroup-per-segment plan
+    with 16-byte loads, 4 per lane, as the full-size logit workload runs it),
+    every row compared, in every determinism mode.  "tied" draws the keys from
+    a coarse grid, so that the k-th key has many copies."""
+    g = torch.Generator(device=DEV)
+    g.manual_seed(2048 if variant == "normal" else 2049)
+    S, n = 2048, 131072
+    if variant == "normal":
+        keys = (torch.randn(S * n, generator=g, device=DEV) * 3).to(torch.bfloat16)
+    else:
+        keys = (torch.randint(-40, 41, (S * n,), generator=g, device=DEV).float() / 4).to(
+            torch.bfloat16)
+    off = torch.arange(S + 1, dtype=torch.int64, device=DEV) * n
+    vals = torch.arange(n, dtype=torch.int32, device=DEV).repeat(S)
+    for det, tb in MODES:
+        say(f"[bf16 2048x128Ki {variant}] {det}/{tb}")
+        check_all_rows(keys, vals, off, 50, "bf16", True, det, tb, "unsorted", chunk_rows=512)
+    check_all_rows(keys, vals, off, 64, "bf16", False, "gpu_to_gpu", "prefer_larger_index",
+                   "stable_sorted", chunk_rows=512)
+    del keys, vals, off
     torch.cuda.empty_cache()
 
 
