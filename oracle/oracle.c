@@ -46,9 +46,19 @@
  *
  * Key types (the caller's raw bit patterns):
  *   0 = binary32 float, 1 = bfloat16 (16 bits), 2 = uint32, 3 = int32,
- *   4 = binary16 float (16 bits).
- * Every key of these types is exactly representable as a C double, so the
- * comparisons below are exact.
+ *   4 = binary16 float (16 bits), 5 = uint16, 6 = int16, 7 = uint64,
+ *   8 = int64, 9 = binary64 float.
+ * Floating-point keys are compared as C doubles (every binary16, bfloat16,
+ * binary32 and binary64 value is one exactly); integer keys are compared as
+ * integers (int64_t, and uint64_t for uint64 keys, which a double cannot
+ * hold exactly), so every comparison below is exact.
+ *
+ * Per-segment k (the extended entry point): when a k_per_segment array is
+ * given, segment i keeps min(max(k_per_segment[i], 0), k, n_i) items, where k
+ * stays the fixed row stride of the outputs.
+ *   [PR "Implement Segmented TopK ...", the review comment on deferred /
+ *    per-segment k, and §3.4 Single-CTA path and the runtime collapse]
+ * Values are an opaque payload of 4 or 8 bytes per item, copied bit for bit.
  */
 #include <math.h>
 #include <stdint.h>
@@ -59,10 +69,18 @@
 #include <omp.h>
 #endif
 
-enum { OR_F32 = 0, OR_BF16 = 1, OR_U32 = 2, OR_I32 = 3, OR_F16 = 4 };
+enum { OR_F32 = 0, OR_BF16 = 1, OR_U32 = 2, OR_I32 = 3, OR_F16 = 4, OR_U16 = 5, OR_I16 = 6,
+       OR_U64 = 7, OR_I64 = 8, OR_F64 = 9 };
 
+/* One item of a segment.  The key is held exactly in one of three fields
+ * (the other two are zero): f for floating-point keys, s for signed and
+ * narrow unsigned integers, u for uint64.  dir is +1 for a MIN request and -1
+ * for a MAX request, so that "ascending under dir" means "better first". */
 typedef struct {
-    double v;     /* key value, negated for MAX so that "ascending" = "better first" */
+    double f;
+    int64_t s;
+    uint64_t u;
+    int dir;
     int64_t tie;  /* index, negated for prefer_larger_index */
     int64_t idx;  /* source index inside the segment */
 } item_t;
@@ -113,22 +131,79 @@ static double decode_key(const void *keys, int type, int64_t pos)
             mag = ldexp((double)(m | 0x400), e - 25); /* 1.m * 2^(e-15) */
         return sign ? -mag : mag;
     }
+    case OR_F64: {
+        double d;
+        memcpy(&d, (const char *)keys + 8 * pos, 8);
+        return d;
+    }
     default:
         return NAN;
     }
 }
 
+static int is_float_type(int type)
+{
+    return type == OR_F32 || type == OR_BF16 || type == OR_F16 || type == OR_F64;
+}
+
+/* Integer keys other than uint64, widened exactly to int64_t. */
+static int64_t decode_int(const void *keys, int type, int64_t pos)
+{
+    switch (type) {
+    case OR_U32: {
+        uint32_t u;
+        memcpy(&u, (const char *)keys + 4 * pos, 4);
+        return (int64_t)u;
+    }
+    case OR_I32: {
+        int32_t v;
+        memcpy(&v, (const char *)keys + 4 * pos, 4);
+        return (int64_t)v;
+    }
+    case OR_U16: {
+        uint16_t v;
+        memcpy(&v, (const char *)keys + 2 * pos, 2);
+        return (int64_t)v;
+    }
+    case OR_I16: {
+        int16_t v;
+        memcpy(&v, (const char *)keys + 2 * pos, 2);
+        return (int64_t)v;
+    }
+    case OR_I64: {
+        int64_t v;
+        memcpy(&v, (const char *)keys + 8 * pos, 8);
+        return v;
+    }
+    default:
+        return 0;
+    }
+}
+
 static int key_bytes(int type)
 {
-    return (type == OR_BF16 || type == OR_F16) ? 2 : 4;
+    switch (type) {
+    case OR_BF16: case OR_F16: case OR_U16: case OR_I16: return 2;
+    case OR_U64: case OR_I64: case OR_F64: return 8;
+    default: return 4;
+    }
+}
+
+/* Key order under the request's direction: <0 when a is better than b. */
+static int cmp_key(const item_t *a, const item_t *b)
+{
+    if (a->f != b->f) return (a->f < b->f ? -1 : 1) * a->dir;
+    if (a->s != b->s) return (a->s < b->s ? -1 : 1) * a->dir;
+    if (a->u != b->u) return (a->u < b->u ? -1 : 1) * a->dir;
+    return 0;
 }
 
 /* Selection order: better key first, then the tie-break order of indices. */
 static int cmp_select(const void *pa, const void *pb)
 {
     const item_t *a = (const item_t *)pa, *b = (const item_t *)pb;
-    if (a->v < b->v) return -1;
-    if (a->v > b->v) return 1;
+    int c = cmp_key(a, b);
+    if (c) return c;
     if (a->tie < b->tie) return -1;
     if (a->tie > b->tie) return 1;
     return 0;
@@ -138,31 +213,40 @@ static int cmp_select(const void *pa, const void *pb)
 static int cmp_output(const void *pa, const void *pb)
 {
     const item_t *a = (const item_t *)pa, *b = (const item_t *)pb;
-    if (a->v < b->v) return -1;
-    if (a->v > b->v) return 1;
+    int c = cmp_key(a, b);
+    if (c) return c;
     if (a->idx < b->idx) return -1;
     if (a->idx > b->idx) return 1;
     return 0;
 }
 
 /* One segment: sort-and-take.  Returns 0, or -1 when memory runs out. */
-static int one_segment(const void *keys_in, int type, const uint32_t *values_in,
-                       int64_t begin, int64_t n, int64_t k, int largest, int prefer_larger,
-                       void *keys_out, uint32_t *values_out, int64_t row)
+static int one_segment(const void *keys_in, int type, const void *values_in, int value_bytes,
+                       int64_t begin, int64_t n, int64_t k_i, int64_t stride, int largest,
+                       int prefer_larger, void *keys_out, void *values_out, int64_t row)
 {
-    int64_t j, k_i;
+    int64_t j;
     int kb = key_bytes(type);
     item_t *items;
 
-    if (n <= 0 || k <= 0)
+    if (n <= 0 || k_i <= 0)
         return 0;
-    k_i = k < n ? k : n;
+    if (k_i > n)
+        k_i = n;
     items = (item_t *)malloc((size_t)n * sizeof(item_t));
     if (!items)
         return -1;
     for (j = 0; j < n; ++j) {
-        double v = decode_key(keys_in, type, begin + j);
-        items[j].v = largest ? -v : v;
+        items[j].f = 0.0;
+        items[j].s = 0;
+        items[j].u = 0;
+        if (is_float_type(type))
+            items[j].f = decode_key(keys_in, type, begin + j);
+        else if (type == OR_U64)
+            memcpy(&items[j].u, (const char *)keys_in + 8 * (begin + j), 8);
+        else
+            items[j].s = decode_int(keys_in, type, begin + j);
+        items[j].dir = largest ? -1 : 1;
         items[j].tie = prefer_larger ? -j : j;
         items[j].idx = j;
     }
@@ -172,10 +256,11 @@ static int one_segment(const void *keys_in, int type, const uint32_t *values_in,
     qsort(items, (size_t)k_i, sizeof(item_t), cmp_output);
     for (j = 0; j < k_i; ++j) {
         int64_t src = begin + items[j].idx;
-        int64_t dst = row * k + j;
+        int64_t dst = row * stride + j;
         memcpy((char *)keys_out + kb * dst, (const char *)keys_in + kb * src, (size_t)kb);
         if (values_in)
-            values_out[dst] = values_in[src];
+            memcpy((char *)values_out + (int64_t)value_bytes * dst,
+                   (const char *)values_in + (int64_t)value_bytes * src, (size_t)value_bytes);
     }
     free(items);
     return 0;
@@ -183,25 +268,32 @@ static int one_segment(const void *keys_in, int type, const uint32_t *values_in,
 
 /*
  * Batched top-k over num_segments segments.
- *   keys_in      raw key patterns, type `key_type` (see the list above)
- *   values_in    32-bit payload aligned with keys_in, or NULL (keys only)
- *   offsets      num_segments + 1 int64 offsets into keys_in / values_in
- *   k            number of items kept per segment (fixed output stride)
- *   largest      1 = MAX request, 0 = MIN request
+ *   keys_in       raw key patterns, type `key_type` (see the list above)
+ *   values_in     payload of value_bytes (4 or 8) per key, aligned with
+ *                 keys_in, or NULL (keys only)
+ *   offsets       num_segments + 1 int64 offsets into keys_in / values_in
+ *   k             largest number of items kept per segment, and the fixed
+ *                 row stride of the outputs
+ *   k_per_segment NULL (every segment keeps up to k), or num_segments int32
+ *                 counts, each clamped to [0, k]
+ *   largest       1 = MAX request, 0 = MIN request
  *   prefer_larger 1 = ties at the boundary resolved toward larger indices
- *   keys_out     num_segments * k keys; values_out likewise (when values_in)
- *   num_threads  worker threads over segments (<= 0: the runtime default)
+ *   keys_out      num_segments * k keys; values_out likewise (when values_in)
+ *   num_threads   worker threads over segments (<= 0: the runtime default)
  * Returns 0 on success, 1 on a bad argument, 2 when memory runs out.
  */
-int oracle_batched_topk(const void *keys_in, int key_type, const uint32_t *values_in,
-                        const int64_t *offsets, int64_t num_segments, int64_t k,
-                        int largest, int prefer_larger, void *keys_out, uint32_t *values_out,
-                        int num_threads)
+int oracle_batched_topk_ex(const void *keys_in, int key_type, const void *values_in,
+                           int value_bytes, const int64_t *offsets, int64_t num_segments,
+                           int64_t k, const int32_t *k_per_segment, int largest,
+                           int prefer_larger, void *keys_out, void *values_out,
+                           int num_threads)
 {
     int64_t i;
     int failed = 0;
 
-    if (num_segments < 0 || k < 0 || key_type < OR_F32 || key_type > OR_F16)
+    if (num_segments < 0 || k < 0 || key_type < OR_F32 || key_type > OR_F64)
+        return 1;
+    if (values_in && value_bytes != 4 && value_bytes != 8)
         return 1;
     if (num_segments == 0 || k == 0)
         return 0;
@@ -216,12 +308,29 @@ int oracle_batched_topk(const void *keys_in, int key_type, const uint32_t *value
     for (i = 0; i < num_segments; ++i) {
         int64_t begin = offsets[i];
         int64_t n = offsets[i + 1] - offsets[i];
-        if (one_segment(keys_in, key_type, values_in, begin, n, k, largest, prefer_larger,
-                        keys_out, values_out, i) != 0)
+        int64_t k_i = k;
+        if (k_per_segment) {
+            k_i = k_per_segment[i] < 0 ? 0 : (int64_t)k_per_segment[i];
+            if (k_i > k)
+                k_i = k;
+        }
+        if (one_segment(keys_in, key_type, values_in, value_bytes, begin, n, k_i, k, largest,
+                        prefer_larger, keys_out, values_out, i) != 0)
             failed = 1;
     }
     (void)num_threads;
     return failed ? 2 : 0;
+}
+
+/* The same with one k for every segment and 32-bit values. */
+int oracle_batched_topk(const void *keys_in, int key_type, const uint32_t *values_in,
+                        const int64_t *offsets, int64_t num_segments, int64_t k,
+                        int largest, int prefer_larger, void *keys_out, uint32_t *values_out,
+                        int num_threads)
+{
+    return oracle_batched_topk_ex(keys_in, key_type, values_in, 4, offsets, num_segments, k,
+                                  NULL, largest, prefer_larger, keys_out, values_out,
+                                  num_threads);
 }
 
 /* Threads the runtime would use by default (reported next to timings). */

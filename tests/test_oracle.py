@@ -336,5 +336,183 @@ def test_rejects_bad_arguments():
                             out.ctypes.data, None, 1)
     assert lib.oracle_batched_topk(*args(-1, 1, 0)) == 1
     assert lib.oracle_batched_topk(*args(1, -1, 0)) == 1
-    assert lib.oracle_batched_topk(*args(1, 1, 9)) == 1
+    assert lib.oracle_batched_topk(*args(1, 1, 10)) == 1
+    assert lib.oracle_batched_topk(*args(1, 1, -1)) == 1
     assert lib.oracle_batched_topk(*args(1, 1, 0)) == 0
+
+
+# --------------------------------------------------------------------------
+# 5. More key types (uint16, int16, uint64, int64, float64), per-segment k and
+#    8-byte values.  Integer keys are checked with Python integers (exact at
+#    any width), floats with numpy float64; neither goes through the oracle.
+# --------------------------------------------------------------------------
+WIDE_NUMPY = {"u16": np.uint16, "i16": np.int16, "u64": np.uint64, "i64": np.int64,
+              "f64": np.float64}
+WIDE_ALPHABET = {
+    "u16": [0, 1, 2, 2 ** 15, 2 ** 16 - 2, 2 ** 16 - 1],
+    "i16": [-(2 ** 15), -1, 0, 1, 2 ** 15 - 1],
+    # neighbours a double cannot tell apart
+    "u64": [0, 1, 2 ** 53 + 1, 2 ** 63, 2 ** 63 + 1, 2 ** 64 - 2, 2 ** 64 - 1],
+    "i64": [-(2 ** 63), -(2 ** 63) + 1, -1, 0, 2 ** 53 + 1, 2 ** 63 - 2, 2 ** 63 - 1],
+    "f64": [float("-inf"), -1.5, -0.0, 0.0, 5e-324, 1.5, float("inf")],
+}
+
+
+def wide_keys(vals, key_type):
+    if key_type == "f64":
+        return np.asarray(vals, dtype=np.float64)
+    return np.array([int(v) for v in vals], dtype=WIDE_NUMPY[key_type])
+
+
+def wide_exact(keys, key_type):
+    """Raw keys -> exact Python numbers (ints, or floats for f64)."""
+    if key_type == "f64":
+        return [float(x) for x in keys]
+    return [int(x) for x in keys]
+
+
+@pytest.mark.parametrize("key_type", list(WIDE_ALPHABET))
+def test_brute_force_tiny_wide_types(key_type):
+    rng = np.random.default_rng(17)
+    alpha = WIDE_ALPHABET[key_type]
+    for trial in range(50):
+        n = int(rng.integers(1, 9))
+        vals = [alpha[i] for i in rng.integers(0, len(alpha), n)]
+        keys = wide_keys(vals, key_type)
+        exact = wide_exact(keys, key_type)
+        payload = (rng.permutation(1000)[:n].astype(np.uint64) << np.uint64(32)) | np.uint64(7)
+        off = np.array([0, n], dtype=np.int64)
+        for k in range(1, n + 2):
+            for largest in (True, False):
+                for pl in (False, True):
+                    ok, ov = oracle.batched_topk(keys, off, k, key_type=key_type,
+                                                 values=payload, largest=largest,
+                                                 prefer_larger=pl)
+                    want = brute_force(exact, k, largest, pl)
+                    kk = len(want)
+                    got_idx = sorted(int(np.nonzero(payload == p)[0][0]) for p in ov[0, :kk])
+                    assert tuple(got_idx) == want, (vals, k, largest, pl)
+                    for j in range(kk):
+                        i = int(np.nonzero(payload == ov[0, j])[0][0])
+                        assert ok[0, j].tobytes() == keys[i].tobytes()
+
+
+def test_u64_and_i64_neighbours_are_ordered_exactly():
+    # 2^64-1 > 2^64-2 and 2^63+1 > 2^63 although each pair is one double.
+    keys = np.array([2 ** 64 - 2, 2 ** 63, 2 ** 64 - 1, 2 ** 63 + 1], dtype=np.uint64)
+    off = np.array([0, 4], dtype=np.int64)
+    idx = np.arange(4, dtype=np.uint32)
+    _, ov = oracle.batched_topk(keys, off, 4, key_type="u64", values=idx, largest=True)
+    assert list(ov[0]) == [2, 0, 3, 1]
+    _, ov = oracle.batched_topk(keys, off, 1, key_type="u64", values=idx, largest=False)
+    assert list(ov[0]) == [1]
+    keys = np.array([2 ** 63 - 2, -(2 ** 63) + 1, 2 ** 63 - 1, -(2 ** 63)], dtype=np.int64)
+    _, ov = oracle.batched_topk(keys, off, 4, key_type="i64", values=idx, largest=True)
+    assert list(ov[0]) == [2, 0, 1, 3]
+    _, ov = oracle.batched_topk(keys, off, 2, key_type="i64", values=idx, largest=False,
+                                prefer_larger=True)
+    assert list(ov[0]) == [3, 1]
+
+
+def test_f64_signed_zero_denormal_and_infinities():
+    keys = np.array([-0.0, 5e-324, 0.0, -5e-324, np.inf, -np.inf], dtype=np.float64)
+    off = np.array([0, 6], dtype=np.int64)
+    idx = np.arange(6, dtype=np.uint32)
+    ok, ov = oracle.batched_topk(keys, off, 6, key_type="f64", values=idx, largest=True)
+    assert list(ov[0]) == [4, 1, 0, 2, 3, 5]
+    assert ok[0, 2].tobytes() == np.float64(-0.0).tobytes()
+    _, ov = oracle.batched_topk(keys, off, 2, key_type="f64", values=idx, largest=True,
+                                prefer_larger=True)
+    assert list(ov[0]) == [4, 1]
+
+
+def _python_topk(exact, k, largest, prefer_larger):
+    """Indices of the top-k by Python's sort on exact numbers, in stable order."""
+    n = len(exact)
+    order = sorted(range(n), key=lambda i: ((-exact[i]) if largest else exact[i],
+                                            -i if prefer_larger else i))
+    chosen = order[:min(k, n)]
+    return sorted(chosen, key=lambda i: ((-exact[i]) if largest else exact[i], i))
+
+
+@pytest.mark.parametrize("key_type", list(WIDE_ALPHABET))
+@pytest.mark.parametrize("largest", [True, False])
+@pytest.mark.parametrize("prefer_larger", [False, True])
+def test_wide_types_against_python_sort_with_per_segment_k(key_type, largest, prefer_larger):
+    rng = np.random.default_rng(23)
+    S = 30
+    sizes = rng.integers(-2, 300, S)
+    off = np.concatenate([[3], 3 + np.cumsum(sizes)]).astype(np.int64)
+    total = int(off.max()) + 5
+    alpha = WIDE_ALPHABET[key_type]
+    if key_type == "f64":
+        pool = np.array(alpha + list(rng.normal(0, 1e3, 40)), dtype=np.float64)
+    elif key_type in ("u64", "i64"):
+        lo, hi = (0, 2 ** 64) if key_type == "u64" else (-(2 ** 63), 2 ** 63)
+        pool = alpha + [int(x) for x in rng.integers(0, 2 ** 62, 40)] + [hi - 1 - j for j in range(5)]
+        pool = [v for v in pool if lo <= v < hi]
+    else:
+        pool = alpha + [int(x) for x in rng.integers(0 if key_type == "u16" else -(2 ** 15),
+                                                      2 ** 15, 40)]
+    keys = wide_keys([pool[i] for i in rng.integers(0, len(pool), total)], key_type)
+    exact = wide_exact(keys, key_type)
+    payload = rng.integers(0, 2 ** 63, total, dtype=np.int64).view(np.uint64) | np.uint64(1 << 63)
+    k = 40
+    kseg = rng.integers(-3, 60, S).astype(np.int32)
+    kseg[0], kseg[1], kseg[2] = 0, 1000, k
+    canary = np.full((S, k), 0xFEEDFACECAFEBEEF, np.uint64)
+    ok, ov = oracle.batched_topk(keys, off, k, key_type=key_type, values=payload,
+                                 largest=largest, prefer_larger=prefer_larger,
+                                 out_values=canary, k_per_segment=kseg)
+    for i in range(S):
+        b, e = int(off[i]), int(off[i + 1])
+        n = max(0, e - b)
+        kk = min(max(int(kseg[i]), 0), k, n)
+        want = _python_topk(exact[b:b + n], kk, largest, prefer_larger) if kk else []
+        assert [int(v) for v in ov[i, :kk]] == [int(payload[b + j]) for j in want], i
+        assert ok[i, :kk].tobytes() == keys[b + np.array(want, dtype=np.int64)].tobytes()
+        assert np.all(ov[i, kk:] == np.uint64(0xFEEDFACECAFEBEEF)), i
+
+
+@pytest.mark.parametrize("key_type", ALL_TYPES)
+def test_per_segment_k_against_brute_force(key_type):
+    """Each segment with its own k (0, 1, n, above n, above the row stride)
+    against the exhaustive search, every direction and tie-break."""
+    rng = np.random.default_rng(29)
+    alpha = ALPHABET[key_type]
+    S, k = 12, 5
+    sizes = rng.integers(0, 8, S)
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    total = int(off[-1])
+    vals = [alpha[i] for i in rng.integers(0, len(alpha), total)]
+    keys = as_keys(vals, key_type)
+    num = numeric(keys, key_type)
+    payload = np.arange(total, dtype=np.uint32) + 100
+    kseg = np.array([0, 1, 2, 3, 4, 5, 6, 9, -1, 5, 2, 100], dtype=np.int32)
+    for largest in (True, False):
+        for pl in (False, True):
+            _, ov = oracle.batched_topk(keys, off, k, key_type=key_type, values=payload,
+                                        largest=largest, prefer_larger=pl,
+                                        out_values=np.full((S, k), 1, np.uint32),
+                                        k_per_segment=kseg)
+            for i in range(S):
+                b, n = int(off[i]), int(sizes[i])
+                kk = min(max(int(kseg[i]), 0), k, n)
+                if kk == 0:
+                    assert np.all(ov[i] == 1)
+                    continue
+                want = brute_force(list(num[b:b + n]), kk, largest, pl)
+                got = tuple(sorted(int(v) - 100 - b for v in ov[i, :kk]))
+                assert got == want, (i, largest, pl)
+                assert np.all(ov[i, kk:] == 1)
+
+
+def test_per_segment_k_equal_to_k_matches_uniform_call():
+    rng = np.random.default_rng(31)
+    keys = rng.normal(size=5000).astype(np.float32)
+    off = np.array([0, 100, 2000, 2001, 5000], dtype=np.int64)
+    vals = np.arange(5000, dtype=np.uint32)
+    a = oracle.batched_topk(keys, off, 64, values=vals)
+    b = oracle.batched_topk(keys, off, 64, values=vals,
+                            k_per_segment=np.full(4, 64, np.int32))
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
