@@ -1,10 +1,17 @@
-"""The kernels' raw-bit bound test, checked on the host (no GPU needed).
+"""The kernels' key transform and raw-bit bound test, checked on the host (no
+GPU needed).
 
 tests/prefilter_exact.hip includes the kernel header, builds host-only with
-hipcc and checks, for every key type and direction, that the test built for
-each pass-0 bucket bound passes exactly the keys whose order-preserving bits
-are within the bound (every 16-bit pattern; boundary and seeded random 32-bit
-patterns), and that the per-lane chunk reduction agrees with the per-key test.
+hipcc and checks, for every key type:
+  * the order-preserving transform against numeric comparison of the keys as
+    the compiler decodes them: a < b exactly when ord(a) < ord(b), a == b
+    exactly when ord(a) == ord(b) (so -0.0 and +0.0 meet), over every 16-bit
+    pattern and over boundary and a million seeded random 32-bit patterns;
+  * for every direction, that the test built for each pass-0 bucket bound
+    passes exactly the keys whose order-preserving bits are within the bound,
+    and that the per-lane chunk reduction agrees with the per-key test.
+Run with --perturbed, the same binary swaps in a transform with a planted
+mistake and must catch it for every key type.
 """
 import os
 import shutil
@@ -28,3 +35,7 @@ def test_raw_bit_bound_test_is_exact(tmp_path):
     print(r.stdout)
     assert r.returncode == 0, r.stdout
     assert "total mismatches: 0" in r.stdout
+    assert r.stdout.count("ordered bits vs numeric order") == 5
+    p = subprocess.run([str(exe), "--perturbed"], capture_output=True, text=True, timeout=300)
+    print(p.stdout)
+    assert p.returncode == 0 and "caught for 5 of 5" in p.stdout, p.stdout
