@@ -48,7 +48,9 @@ typedef enum segtopk_key_type {
     SEGTOPK_KEY_BF16 = 1, /* bfloat16 (upper half of a binary32)    */
     SEGTOPK_KEY_U32 = 2,  /* unsigned 32-bit integer                */
     SEGTOPK_KEY_I32 = 3,  /* signed 32-bit integer                  */
-    SEGTOPK_KEY_F16 = 4   /* IEEE binary16                          */
+    SEGTOPK_KEY_F16 = 4,  /* IEEE binary16                          */
+    SEGTOPK_KEY_U16 = 5,  /* unsigned 16-bit integer                */
+    SEGTOPK_KEY_I16 = 6   /* signed 16-bit integer                  */
 } segtopk_key_type;
 
 /* ---- request --------------------------------------------------------- */
@@ -102,9 +104,10 @@ typedef struct segtopk_keys {
     int32_t type; /* a segtopk_key_type */
 } segtopk_keys;
 
-/* Values: any 32-bit payload aligned with keys.in, copied bit for bit;
- * `out` has the same num_segments x k shape as the key output.  Pass NULL
- * (or in == NULL) for a keys-only request. */
+/* Values: any 32-bit payload aligned with keys.in (batched_topk_ex also takes
+ * 64-bit payloads), copied bit for bit; `out` has the same num_segments x k
+ * shape as the key output.  Pass NULL (or in == NULL) for a keys-only
+ * request. */
 typedef struct segtopk_values {
     const void *in;
     void *out;
@@ -134,12 +137,15 @@ typedef struct segtopk_values {
  * The call is asynchronous: it validates the request, queues kernels on
  * `stream` and returns without waiting.  It never copies data to the host.
  * Internal scratch (only for batches of fewer than 2048 segments) is one
- * buffer per (device, stream), taken from the device's stream-ordered memory
- * pool on `stream` the first time a call on that stream needs it and grown
- * (the old buffer freed on `stream`) when a later call needs more.  Calls on
- * one stream reuse it in stream order; it is held until the process ends.
- * A stream handle that is destroyed and created again may inherit the buffer
- * of its predecessor, which is safe because the old stream has no work left.
+ * buffer per (device, stream), taken from a memory pool the library creates
+ * for the device (the device's default pool is not touched) on `stream` the
+ * first time a call on that stream needs it, and grown (the old buffer freed
+ * on `stream`) when a later call needs more.  Calls on one stream reuse it in
+ * stream order.  The library keeps such buffers for at most 16 (device,
+ * stream) pairs; the least recently used one is freed, in stream order, when
+ * a seventeenth pair needs one.  A stream handle that is destroyed and
+ * created again may inherit the buffer of its predecessor, which is safe
+ * because every call first waits for the buffer's previous use.
  * Outputs must not overlap the inputs.  Calls on different streams are
  * independent.
  *
@@ -154,6 +160,52 @@ int batched_topk(const segtopk_keys *keys, const segtopk_values *values,
                  const int64_t *segment_offsets, int64_t num_segments, int64_t k,
                  int direction, int determinism, int tie_break, int ordering,
                  hipStream_t stream);
+
+/*
+ * batched_topk_ex -- batched_topk with per-segment k, a segment-size hint and
+ * 64-bit payloads.   [PR "Implement Segmented TopK using
+ * Thread-Block-Clusters", the review comment asking for deferred (per-segment)
+ * k and for k and num_segments to be validated beyond their wrapper form;
+ * §3.4 Single-CTA path and the runtime collapse; the static segment-size
+ * bounds of the tuning discussion]
+ *
+ *   value_bytes       size of one payload item: 4 or 8 (ignored for a
+ *                     keys-only request).  values.in / values.out must be
+ *                     aligned to it.
+ *   k                 output row stride and the largest k of any segment,
+ *                     0 <= k <= 2^31 - 1
+ *   k_per_segment     NULL (every segment uses k), or a DEVICE array of
+ *                     num_segments int32 counts, aligned to 4 bytes: segment i
+ *                     keeps k_i = min(max(k_per_segment[i], 0), k, n_i) items.
+ *                     Slots k_i .. k-1 of row i are left untouched.  Read on
+ *                     the device, in stream order, so it may be written by
+ *                     earlier work on `stream`.
+ *   max_segment_size  host-side hint: no segment holds more keys than this;
+ *                     <= 0 means unknown.  It only steers the launch plan
+ *                     (whether segments are split over several workgroups,
+ *                     scratch and stash sizes); a segment larger than the hint
+ *                     is still served correctly, at the cost of a less suited
+ *                     plan.
+ *   the other arguments are batched_topk's.
+ *
+ * With value_bytes == 8 the selection writes each winner's source index into
+ * its output slot and a second kernel on `stream` replaces it with the
+ * payload; no scratch is taken for that.
+ * Returns what batched_topk returns; value_bytes other than 4 or 8, or a
+ * misaligned k_per_segment, is SEGTOPK_INVALID_ARGUMENT.
+ *
+ * batched_topk(keys, values, off, S, k, ...) is
+ * batched_topk_ex(keys, values, 4, off, S, k, NULL, 0, ...).
+ *
+ * Graph capture: a request whose plan needs internal scratch (fewer than
+ * 2048 segments, unless max_segment_size shows that no segment needs more
+ * than one workgroup) returns SEGTOPK_NOT_SUPPORTED while `stream` is being
+ * captured; the other plans queue only kernel launches and may be captured.
+ */
+int batched_topk_ex(const segtopk_keys *keys, const segtopk_values *values, int32_t value_bytes,
+                    const int64_t *segment_offsets, int64_t num_segments, int64_t k,
+                    const int32_t *k_per_segment, int64_t max_segment_size, int direction,
+                    int determinism, int tie_break, int ordering, hipStream_t stream);
 
 /* Human-readable name of a status code (static storage). */
 const char *segtopk_status_string(int status);

@@ -20,7 +20,8 @@ LIB_PATH = os.path.join(_HERE, "libsegtopk.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "segtopk.h")
 
 # Values of the enums in include/segtopk.h.
-KEY_TYPES = {"f32": 0, "bf16": 1, "u32": 2, "i32": 3, "f16": 4}
+KEY_TYPES = {"f32": 0, "bf16": 1, "u32": 2, "i32": 3, "f16": 4, "u16": 5, "i16": 6}
+KEY_BYTES = {"f32": 4, "bf16": 2, "u32": 4, "i32": 4, "f16": 2, "u16": 2, "i16": 2}
 DIRECTIONS = {"max": 0, "min": 1}
 DETERMINISM = {"not_guaranteed": 0, "run_to_run": 1, "gpu_to_gpu": 2}
 TIE_BREAK = {"unspecified": 0, "prefer_smaller_index": 1, "prefer_larger_index": 2}
@@ -29,9 +30,11 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "not supported", 3: "HIP error"}
 MAX_SORTED_K = 4096
 
 _DTYPE_KEY = {torch.float32: "f32", torch.bfloat16: "bf16", torch.float16: "f16",
-              torch.int32: "i32"}
+              torch.int32: "i32", torch.int16: "i16"}
 if hasattr(torch, "uint32"):
     _DTYPE_KEY[torch.uint32] = "u32"
+if hasattr(torch, "uint16"):
+    _DTYPE_KEY[torch.uint16] = "u16"
 
 
 class SegTopKError(RuntimeError):
@@ -65,6 +68,11 @@ def library() -> ctypes.CDLL:
             ctypes.POINTER(_Keys), ctypes.POINTER(_Values), ctypes.c_void_p,
             ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
             ctypes.c_int, ctypes.c_void_p]
+        lib.batched_topk_ex.restype = ctypes.c_int
+        lib.batched_topk_ex.argtypes = [
+            ctypes.POINTER(_Keys), ctypes.POINTER(_Values), ctypes.c_int32, ctypes.c_void_p,
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
         lib.segtopk_status_string.restype = ctypes.c_char_p
         lib.segtopk_status_string.argtypes = [ctypes.c_int]
         lib.segtopk_version.restype = ctypes.c_int
@@ -83,7 +91,7 @@ def header_functions() -> list:
 
 def raw_call(keys_in, keys_out, key_type, values_in, values_out, offsets, num_segments, k,
              direction, determinism, tie_break, ordering, stream=None) -> int:
-    """Calls the C entry point with integer pointers; returns its status."""
+    """Calls batched_topk with integer pointers; returns its status."""
     kd = _Keys(keys_in, keys_out, key_type)
     vd = _Values(values_in, values_out)
     return library().batched_topk(ctypes.byref(kd), ctypes.byref(vd) if values_in else None,
@@ -91,53 +99,127 @@ def raw_call(keys_in, keys_out, key_type, values_in, values_out, offsets, num_se
                                   ordering, stream)
 
 
+def raw_call_ex(keys_in, keys_out, key_type, values_in, values_out, value_bytes, offsets,
+                num_segments, k, k_per_segment, max_segment_size, direction, determinism,
+                tie_break, ordering, stream=None) -> int:
+    """Calls batched_topk_ex with integer pointers; returns its status."""
+    kd = _Keys(keys_in, keys_out, key_type)
+    vd = _Values(values_in, values_out)
+    return library().batched_topk_ex(ctypes.byref(kd), ctypes.byref(vd) if values_in else None,
+                                     value_bytes, offsets, num_segments, k, k_per_segment,
+                                     max_segment_size, direction, determinism, tie_break,
+                                     ordering, stream)
+
+
+def _device_tensor(name, t, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must be a device tensor on {device} (got {t.device})")
+
+
+def _output_tensor(name, t, device, elem_bytes, need):
+    _device_tensor(name, t, device)
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.element_size() != elem_bytes:
+        raise TypeError(f"{name} must have {elem_bytes}-byte elements "
+                        f"(got {t.element_size()})")
+    if t.numel() < need:
+        raise ValueError(f"{name} holds {t.numel()} elements; num_segments * k = {need} needed")
+
+
 def batched_topk(keys: torch.Tensor, segment_offsets: torch.Tensor, k: int, *,
                  values: torch.Tensor | None = None, largest: bool = True,
                  determinism: str = "gpu_to_gpu", tie_break: str = "prefer_smaller_index",
                  ordering: str = "stable_sorted", key_type: str | None = None,
                  out_keys: torch.Tensor | None = None, out_values: torch.Tensor | None = None,
-                 stream: torch.cuda.Stream | None = None):
+                 stream: torch.cuda.Stream | None = None,
+                 k_per_segment: torch.Tensor | None = None,
+                 max_segment_size: int | None = None):
     """Top-k of every segment of ``keys`` on the GPU.
 
-    keys             1-D device tensor (float32, bfloat16, float16, int32; for
-                     uint32 keys pass their bits as int32 with key_type="u32")
+    keys             1-D device tensor (float32, bfloat16, float16, int32,
+                     int16; for uint32 / uint16 keys pass their bits as int32 /
+                     int16 with key_type="u32" / "u16")
     segment_offsets  int64 device tensor of num_segments + 1 offsets
-    values           optional 1-D 32-bit payload (int32/uint32/float32), same
-                     length as keys
+    values           optional 1-D payload of 4- or 8-byte items (any dtype),
+                     same length as keys
+    k_per_segment    optional int32 device tensor: segment i keeps
+                     min(max(k_per_segment[i], 0), k, n_i) items; k stays the
+                     row stride of the outputs
+    max_segment_size optional host-side hint: no segment is longer (it steers
+                     the launch plan only)
     Defaults follow the requirements page: gpu_to_gpu determinism,
     prefer_smaller_index ties, stable_sorted output.
     Returns (out_keys, out_values) of shape (num_segments, k); out_values is
-    None for keys-only calls.  Row i holds min(k, n_i) results; the rest of the
-    row is left as the caller's tensor had it (uninitialised when allocated
-    here).
+    None for keys-only calls.  Row i holds its k_i results; the rest of the row
+    is left as the caller's tensor had it (uninitialised when allocated here).
+    Bad tensors (host memory, another device, wrong element size, outputs too
+    small or not contiguous) raise before anything is queued.
     """
+    if not isinstance(keys, torch.Tensor):
+        raise TypeError("keys must be a torch tensor")
     if key_type is None:
         if keys.dtype not in _DTYPE_KEY:
             raise TypeError(f"unsupported key dtype {keys.dtype}")
         key_type = _DTYPE_KEY[keys.dtype]
-    if not keys.is_cuda or not segment_offsets.is_cuda:
-        raise ValueError("keys and segment_offsets must be device tensors")
+    if key_type not in KEY_TYPES:
+        raise ValueError(f"unknown key_type {key_type!r}")
+    if not keys.is_cuda:
+        raise ValueError("keys must be a device tensor")
+    dev = keys.device
+    if keys.element_size() != KEY_BYTES[key_type]:
+        raise TypeError(f"key_type {key_type} needs {KEY_BYTES[key_type]}-byte keys "
+                        f"(got {keys.dtype})")
+    _device_tensor("segment_offsets", segment_offsets, dev)
     if segment_offsets.dtype != torch.int64:
         raise TypeError("segment_offsets must be int64")
-    keys = keys.contiguous()
+    if segment_offsets.dim() != 1 or segment_offsets.numel() < 1:
+        raise ValueError("segment_offsets must be 1-D with num_segments + 1 entries")
+    k = int(k)
+    if k < 0:
+        raise ValueError("k must be >= 0")
+    keys = keys.reshape(-1).contiguous()
     segment_offsets = segment_offsets.contiguous()
     s = segment_offsets.numel() - 1
     if out_keys is None:
-        out_keys = torch.empty((max(s, 0), k), dtype=keys.dtype, device=keys.device)
+        out_keys = torch.empty((s, k), dtype=keys.dtype, device=dev)
+    _output_tensor("out_keys", out_keys, dev, keys.element_size(), s * k)
     vin = vout = None
+    vbytes = 4
     if values is not None:
-        if values.element_size() != 4:
-            raise TypeError("values must be a 32-bit payload")
-        values = values.contiguous()
+        _device_tensor("values", values, dev)
+        vbytes = values.element_size()
+        if vbytes not in (4, 8):
+            raise TypeError("values must be a 4- or 8-byte payload")
+        values = values.reshape(-1).contiguous()
+        if values.numel() < keys.numel():
+            raise ValueError("values must hold one item per key")
         if out_values is None:
-            out_values = torch.empty((max(s, 0), k), dtype=values.dtype, device=keys.device)
+            out_values = torch.empty((s, k), dtype=values.dtype, device=dev)
+        _output_tensor("out_values", out_values, dev, vbytes, s * k)
         vin, vout = values.data_ptr(), out_values.data_ptr()
+    kseg_ptr = None
+    if k_per_segment is not None:
+        _device_tensor("k_per_segment", k_per_segment, dev)
+        if k_per_segment.dtype != torch.int32:
+            raise TypeError("k_per_segment must be int32")
+        k_per_segment = k_per_segment.reshape(-1).contiguous()
+        if k_per_segment.numel() < s:
+            raise ValueError("k_per_segment needs one entry per segment")
+        kseg_ptr = k_per_segment.data_ptr()
     if stream is None:
-        stream = torch.cuda.current_stream(keys.device)
-    rc = raw_call(keys.data_ptr(), out_keys.data_ptr(), KEY_TYPES[key_type], vin, vout,
-                  segment_offsets.data_ptr(), s, k, DIRECTIONS["max" if largest else "min"],
-                  DETERMINISM[determinism], TIE_BREAK[tie_break], ORDERING[ordering],
-                  stream.cuda_stream)
+        stream = torch.cuda.current_stream(dev)
+    args = (DIRECTIONS["max" if largest else "min"], DETERMINISM[determinism],
+            TIE_BREAK[tie_break], ORDERING[ordering], stream.cuda_stream)
+    if kseg_ptr is None and max_segment_size is None and vbytes == 4:
+        rc = raw_call(keys.data_ptr(), out_keys.data_ptr(), KEY_TYPES[key_type], vin, vout,
+                      segment_offsets.data_ptr(), s, k, *args)
+    else:
+        rc = raw_call_ex(keys.data_ptr(), out_keys.data_ptr(), KEY_TYPES[key_type], vin, vout,
+                         vbytes, segment_offsets.data_ptr(), s, k, kseg_ptr,
+                         int(max_segment_size or 0), *args)
     if rc != 0:
         raise SegTopKError(rc)
     return out_keys, (out_values if values is not None else None)

@@ -61,48 +61,89 @@ __global__ __launch_bounds__(1024) void order_kernel(const int64_t *off, int64_t
     }
 }
 
+// 8-byte payloads: the selection left each winner's source index in the low
+// half of its 8-byte output slot; replace it by the payload.  Slots past k_i
+// are not touched.  One thread per slot of the S x k output.
+__global__ void gather64_kernel(const int64_t *off, const int32_t *kseg, int64_t num_segments,
+                                uint32_t k, const uint64_t *vals_in, uint64_t *vals_out) {
+    const uint64_t total = (uint64_t)num_segments * k;
+    for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+         i += (uint64_t)gridDim.x * blockDim.x) {
+        const uint64_t row = i / k;
+        const uint32_t j = (uint32_t)(i - row * k);
+        const int64_t b = off[row], e = off[row + 1];
+        const uint64_t n = e > b ? (uint64_t)(e - b) : 0u;
+        uint64_t k_i = n < k ? n : k;
+        if (kseg) {
+            const int32_t ks = kseg[row];
+            const uint64_t ku = ks > 0 ? (uint64_t)ks : 0u;
+            k_i = ku < k_i ? ku : k_i;
+        }
+        if (j >= k_i) continue;
+        const uint32_t idx = (uint32_t)vals_out[i];
+        if (idx < n) vals_out[i] = vals_in[b + idx];
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Host side.
 // ---------------------------------------------------------------------------
 constexpr uint32_t kTargetWorkgroups = 2048;  // enough to fill 256 CUs several times
-constexpr uint32_t kMaxWgPerSeg = 256;
 constexpr uint32_t kMinSlice = 16384;
 constexpr int64_t kOrderMinSegments = 256;  // fewer segments: no processing order
+constexpr size_t kMaxCachedStreams = 16;    // scratch buffers kept (LRU beyond that)
 
-int key_bytes(int type) { return (type == SEGTOPK_KEY_BF16 || type == SEGTOPK_KEY_F16) ? 2 : 4; }
+int key_bytes(int type) {
+    return (type == SEGTOPK_KEY_BF16 || type == SEGTOPK_KEY_F16 || type == SEGTOPK_KEY_U16 ||
+            type == SEGTOPK_KEY_I16)
+               ? 2
+               : 4;
+}
 
-uint32_t next_pow2(uint32_t x) {
-    uint32_t p = 1;
+// Smallest power of two >= x, for 1 <= x <= 2^62.
+uint64_t next_pow2(uint64_t x) {
+    uint64_t p = 1;
     while (p < x) p <<= 1;
     return p;
 }
 
+// The library's own stream-ordered pool per device (freed scratch stays
+// cached in it; the device's default pool is left as the process set it).
 std::mutex g_pool_mu;
-bool g_pool_ready[64];
+hipMemPool_t g_pool[64];
 
-// Keep freed scratch in the device's stream-ordered pool between calls.
-void prepare_pool(int dev) {
+hipError_t pool_for(int dev, hipMemPool_t *out) {
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
     std::lock_guard<std::mutex> lk(g_pool_mu);
-    if (dev < 0 || dev >= 64 || g_pool_ready[dev]) return;
-    hipMemPool_t pool;
-    if (hipDeviceGetDefaultMemPool(&pool, dev) == hipSuccess) {
+    if (!g_pool[dev]) {
+        hipMemPoolProps props = {};
+        props.allocType = hipMemAllocationTypePinned;
+        props.location.type = hipMemLocationTypeDevice;
+        props.location.id = dev;
+        hipMemPool_t pool = nullptr;
+        hipError_t e = hipMemPoolCreate(&pool, &props);
+        if (e != hipSuccess) return e;
         uint64_t thr = UINT64_MAX;
         (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &thr);
+        g_pool[dev] = pool;
     }
-    g_pool_ready[dev] = true;
+    *out = g_pool[dev];
+    return hipSuccess;
 }
 
 // Scratch reused across the calls on one stream.  Stream order keeps the
 // calls on a stream from overlapping, so one buffer per (device, stream)
 // suffices; a stream-ordered malloc/free pair in every call made the host
 // wait for the device each time.  A call that needs more grows the buffer
-// (the old one is freed in stream order); buffers are held until the process
-// ends.  The per-thread default stream is one handle for many streams, so
-// that key also holds the calling thread.  Each buffer carries an event
-// recorded after its last use: a call first makes its stream wait for it,
-// so that a stream created with the handle of a destroyed one that still
-// has work queued cannot overlap that work.  The caller holds g_ws_mu from
-// stream_scratch until it has queued its kernels and recorded the event.
+// (the old one is freed in stream order).  The per-thread default stream is
+// one handle for many streams, so that key also holds the calling thread.
+// Each buffer carries an event recorded after its last use: a call first
+// makes its stream wait for it, so that a stream created with the handle of a
+// destroyed one that still has work queued cannot overlap that work.  At most
+// kMaxCachedStreams buffers are kept; the least recently used one is freed
+// in the order of the stream that evicts it, after its own last use.  The
+// caller holds g_ws_mu from stream_scratch until it has queued its kernels
+// and recorded the event.
 struct WsKey {
     int dev;
     hipStream_t stream;
@@ -120,36 +161,66 @@ struct WsBuf {
     // Leading 32-bit words that are zero once the stream's queued work is
     // done: slice mode leaves its histograms and tickets cleared again.
     size_t clean_words = 0;
+    uint64_t last_use = 0;
 };
 std::mutex g_ws_mu;
 std::map<WsKey, WsBuf> g_ws;
+uint64_t g_ws_tick = 0;
+
+hipError_t evict_lru(const WsKey &keep, hipStream_t stream) {
+    auto victim = g_ws.end();
+    for (auto it = g_ws.begin(); it != g_ws.end(); ++it)
+        if (!(it->first.dev == keep.dev && it->first.stream == keep.stream &&
+              it->first.thread == keep.thread) &&
+            (victim == g_ws.end() || it->second.last_use < victim->second.last_use))
+            victim = it;
+    if (victim == g_ws.end()) return hipSuccess;
+    WsBuf &v = victim->second;
+    if (v.done) {
+        const hipError_t e = hipStreamWaitEvent(stream, v.done, 0);
+        if (e != hipSuccess) return e;
+    }
+    if (v.ptr) {
+        const hipError_t e = hipFreeAsync(v.ptr, stream);
+        if (e != hipSuccess) return e;
+    }
+    if (v.done) (void)hipEventDestroy(v.done);
+    g_ws.erase(victim);
+    return hipSuccess;
+}
 
 hipError_t stream_scratch(int dev, hipStream_t stream, size_t bytes, WsBuf **out) {
     const WsKey key{dev, stream,
                     stream == hipStreamPerThread ? std::this_thread::get_id() : std::thread::id()};
+    hipMemPool_t pool;
+    hipError_t e = pool_for(dev, &pool);
+    if (e != hipSuccess) return e;
     WsBuf &b = g_ws[key];
+    b.last_use = ++g_ws_tick;
     if (!b.done) {
-        const hipError_t e = hipEventCreateWithFlags(&b.done, hipEventDisableTiming);
+        e = hipEventCreateWithFlags(&b.done, hipEventDisableTiming);
         if (e != hipSuccess) {
             b.done = nullptr;
             return e;
         }
     } else {
-        const hipError_t e = hipStreamWaitEvent(stream, b.done, 0);
+        e = hipStreamWaitEvent(stream, b.done, 0);
         if (e != hipSuccess) return e;
     }
-    if (b.bytes < bytes) {
+    if (g_ws.size() > kMaxCachedStreams && (e = evict_lru(key, stream)) != hipSuccess) return e;
+    WsBuf &bb = g_ws[key];
+    if (bb.bytes < bytes) {
         size_t want = bytes + (bytes >> 2);
         want = (want + ((size_t)1 << 20) - 1) & ~(((size_t)1 << 20) - 1);
         void *np = nullptr;
-        const hipError_t e = hipMallocAsync(&np, want, stream);
+        e = hipMallocFromPoolAsync(&np, want, pool, stream);
         if (e != hipSuccess) return e;
-        if (b.ptr) (void)hipFreeAsync(b.ptr, stream);
-        b.ptr = np;
-        b.bytes = want;
-        b.clean_words = 0;
+        if (bb.ptr) (void)hipFreeAsync(bb.ptr, stream);
+        bb.ptr = np;
+        bb.bytes = want;
+        bb.clean_words = 0;
     }
-    *out = &b;
+    *out = &bb;
     return hipSuccess;
 }
 
@@ -170,6 +241,8 @@ int per_cu_for(int type, bool largest, size_t lds) {
     case SEGTOPK_KEY_BF16: return topk_per_cu<SEGTOPK_KEY_BF16>(largest, lds);
     case SEGTOPK_KEY_U32: return topk_per_cu<SEGTOPK_KEY_U32>(largest, lds);
     case SEGTOPK_KEY_I32: return topk_per_cu<SEGTOPK_KEY_I32>(largest, lds);
+    case SEGTOPK_KEY_U16: return topk_per_cu<SEGTOPK_KEY_U16>(largest, lds);
+    case SEGTOPK_KEY_I16: return topk_per_cu<SEGTOPK_KEY_I16>(largest, lds);
     default: return topk_per_cu<SEGTOPK_KEY_F16>(largest, lds);
     }
 }
@@ -200,8 +273,261 @@ hipError_t launch(int type, const Params &p, bool largest, int variant, uint32_t
     case SEGTOPK_KEY_BF16: return launch_topk<SEGTOPK_KEY_BF16>(p, largest, variant, grid, lds, st);
     case SEGTOPK_KEY_U32: return launch_topk<SEGTOPK_KEY_U32>(p, largest, variant, grid, lds, st);
     case SEGTOPK_KEY_I32: return launch_topk<SEGTOPK_KEY_I32>(p, largest, variant, grid, lds, st);
+    case SEGTOPK_KEY_U16: return launch_topk<SEGTOPK_KEY_U16>(p, largest, variant, grid, lds, st);
+    case SEGTOPK_KEY_I16: return launch_topk<SEGTOPK_KEY_I16>(p, largest, variant, grid, lds, st);
     default: return launch_topk<SEGTOPK_KEY_F16>(p, largest, variant, grid, lds, st);
     }
+}
+
+struct Request {
+    const segtopk_keys *keys;
+    const segtopk_values *values;
+    int32_t value_bytes;
+    const int64_t *offsets;
+    int64_t num_segments, k;
+    const int32_t *kseg;
+    int64_t max_seg;
+    int direction, determinism, tie_break, ordering;
+    hipStream_t stream;
+};
+
+// Everything the call queues, decided on the host from the request alone.
+struct Plan {
+    Params p;
+    int type;
+    bool largest;
+    int variant;
+    uint32_t grid;
+    size_t lds;
+    bool pairs, wide_values;
+    // scratch: the order array (order), or the slice-mode layout (sliced)
+    bool order, sliced;
+    size_t scratch_bytes, zero_words, data_off, n_hist, info_words;
+};
+
+int validate(const Request &r) {
+    if (!r.keys) return SEGTOPK_INVALID_ARGUMENT;
+    const int type = r.keys->type;
+    if (type < SEGTOPK_KEY_F32 || type > SEGTOPK_KEY_I16) return SEGTOPK_INVALID_ARGUMENT;
+    if (r.direction != SEGTOPK_MAX && r.direction != SEGTOPK_MIN) return SEGTOPK_INVALID_ARGUMENT;
+    if (r.determinism < SEGTOPK_NOT_GUARANTEED || r.determinism > SEGTOPK_GPU_TO_GPU)
+        return SEGTOPK_INVALID_ARGUMENT;
+    if (r.tie_break < SEGTOPK_TIE_UNSPECIFIED || r.tie_break > SEGTOPK_PREFER_LARGER_INDEX)
+        return SEGTOPK_INVALID_ARGUMENT;
+    if (r.ordering < SEGTOPK_UNSORTED || r.ordering > SEGTOPK_STABLE_SORTED)
+        return SEGTOPK_INVALID_ARGUMENT;
+    // An explicit index tie-break pins the set across GPUs, so it must come
+    // with gpu_to_gpu.   [docs "Top-K: Determinism ...", "Which items are selected?"]
+    if (r.tie_break != SEGTOPK_TIE_UNSPECIFIED && r.determinism != SEGTOPK_GPU_TO_GPU)
+        return SEGTOPK_INVALID_ARGUMENT;
+    if (r.k < 0 || r.k > INT32_MAX || r.num_segments < 0 || r.num_segments > INT32_MAX)
+        return SEGTOPK_INVALID_ARGUMENT;
+    if (r.value_bytes != 4 && r.value_bytes != 8) return SEGTOPK_INVALID_ARGUMENT;
+    if (r.num_segments == 0 || r.k == 0) return SEGTOPK_OK;
+    if (!r.keys->in || !r.keys->out || !r.offsets) return SEGTOPK_INVALID_ARGUMENT;
+    const bool pairs = r.values && r.values->in;
+    if (pairs && !r.values->out) return SEGTOPK_INVALID_ARGUMENT;
+    const uintptr_t kb = (uintptr_t)key_bytes(type);
+    if ((reinterpret_cast<uintptr_t>(r.keys->in) % kb) ||
+        (reinterpret_cast<uintptr_t>(r.keys->out) % kb))
+        return SEGTOPK_INVALID_ARGUMENT;
+    const uintptr_t vb = (uintptr_t)r.value_bytes;
+    if (pairs && ((reinterpret_cast<uintptr_t>(r.values->in) % vb) ||
+                  (reinterpret_cast<uintptr_t>(r.values->out) % vb)))
+        return SEGTOPK_INVALID_ARGUMENT;
+    if ((reinterpret_cast<uintptr_t>(r.offsets) & 7)) return SEGTOPK_INVALID_ARGUMENT;
+    if (r.kseg && (reinterpret_cast<uintptr_t>(r.kseg) & 3)) return SEGTOPK_INVALID_ARGUMENT;
+    if (r.ordering != SEGTOPK_UNSORTED && r.k > SEGTOPK_MAX_SORTED_K) return SEGTOPK_NOT_SUPPORTED;
+    return -1;  // valid, with work to do
+}
+
+// The launch plan.  Only host arithmetic and (for fewer than 2048 segments)
+// the cached occupancy query of the sliced kernel.
+int make_plan(const Request &r, int dev, Plan &pl) {
+    const int type = r.keys->type;
+    const bool pairs = r.values && r.values->in;
+    const bool sorted = r.ordering != SEGTOPK_UNSORTED;
+    const uint64_t k = (uint64_t)r.k;
+    const uint64_t S = (uint64_t)r.num_segments;
+    // The hint only sizes the plan, never a bound the kernels rely on.
+    const uint64_t hint = r.max_seg > 0 ? (uint64_t)r.max_seg : 0u;
+    const uint64_t k_eff = (hint && hint < k) ? hint : k;
+
+    Params &p = pl.p;
+    p = Params{};
+    p.keys_in = r.keys->in;
+    p.keys_out = r.keys->out;
+    p.vals_in = pairs ? static_cast<const uint32_t *>(r.values->in) : nullptr;
+    p.vals_out = pairs ? static_cast<uint32_t *>(r.values->out) : nullptr;
+    p.offsets = r.offsets;
+    p.num_segments = r.num_segments;
+    p.kseg = r.kseg;
+    p.k = (uint32_t)k;
+    p.det = r.determinism != SEGTOPK_NOT_GUARANTEED;
+    p.prefer_larger = r.tie_break == SEGTOPK_PREFER_LARGER_INDEX;
+    p.sorted = sorted;
+    pl.wide_values = pairs && r.value_bytes == 8;
+    p.vindex = pl.wide_values ? 1u : 0u;
+    p.vshift = pl.wide_values ? 1u : 0u;
+
+    // Output staging: sorted output is staged and sorted in LDS (k is at most
+    // SEGTOPK_MAX_SORTED_K then); unsorted output only for small k (coalesced
+    // row writes), else written in place.  Sized by k, never by the hint: a
+    // segment may exceed the hint.
+    uint64_t out_cap = next_pow2(k < 2 ? 2 : (k > 8192 ? 8192 : k));
+    if (!sorted && out_cap > 256) out_cap = 0;
+    // Several workgroups per segment when the segments alone cannot fill the
+    // device, unless the hint says no segment is long enough to be split.
+    const bool many = S >= kTargetWorkgroups;
+    uint64_t min_slice = kMinSlice;
+    if (8 * k > min_slice) min_slice = 8 * k > (1ull << 30) ? (1ull << 30) : 8 * k;
+    const bool split = !many && !(hint && hint <= min_slice);
+    // Stash: with one workgroup per segment, room for about eight times k
+    // candidates in four wave regions; with several, the segment-wide bound
+    // keeps each slice's candidates few, and the stash only has to hold
+    // bucket b* of the last arriver (about 2k at most).
+    uint64_t stash = (split ? 2 : 8) * k_eff;
+    if (stash > 8192) stash = 8192;
+    uint64_t stash_cap = next_pow2(stash < 1 ? 1 : stash);
+    if (stash_cap < (split ? 2048u : 1024u)) stash_cap = split ? 2048u : 1024u;
+    while (stash_cap > 1024 && 8 * (stash_cap + out_cap) > kMaxDynLds) stash_cap >>= 1;
+    if (8 * (stash_cap + out_cap) > kMaxDynLds) return SEGTOPK_NOT_SUPPORTED;
+    p.stash_cap = (uint32_t)stash_cap;
+    p.out_cap = (uint32_t)out_cap;
+    pl.lds = 8 * (size_t)(stash_cap + out_cap);
+    pl.largest = r.direction == SEGTOPK_MAX;
+    pl.type = type;
+    pl.pairs = pairs;
+
+    uint64_t P = 1;
+    if (split) {
+        // As many workgroups as the device holds at once, so that all the
+        // slices of a segment run together and share their bound.
+        const uint64_t target = resident_wgs_for(type, dev, pl.largest, pl.lds);
+        if (S < 8) {
+            P = target / S;  // every slice of every segment resident at once
+        } else {
+            P = (target + S - 1) / S;
+        }
+        if (P > kMaxWgPerSeg) P = kMaxWgPerSeg;
+        if (P < 1) P = 1;
+        if (2 * k > stash_cap) P = 1;  // slices could not hold their local candidates
+    }
+    p.wg_per_seg = (uint32_t)P;
+    p.min_slice = (uint32_t)min_slice;
+    p.spread = (split && S < 8 && P > 1) ? 1u : 0u;
+    // With one workgroup per segment workgroup b serves segment b; with
+    // several, the XCD-local mapping rounds the batch up to a multiple of 8.
+    const uint64_t grid = P == 1 ? S : (p.spread ? S * P : (S + 7) / 8 * 8 * P);
+    if (grid > 0x7FFFFFFFull) return SEGTOPK_NOT_SUPPORTED;
+    pl.grid = (uint32_t)grid;
+    pl.variant = many ? kVariantOne : (P > 1 ? kVariantSliced : kVariantSplit);
+
+    // Scratch.  One workgroup per segment for many segments of unknown sizes
+    // (not all within one chunk by the hint): process the largest first.
+    pl.order = split && P == 1 && S >= (uint64_t)kOrderMinSegments && !(hint && hint <= 8192);
+    pl.sliced = P > 1;
+    pl.scratch_bytes = pl.zero_words = pl.data_off = pl.n_hist = pl.info_words = 0;
+    if (pl.order) {
+        pl.scratch_bytes = S * sizeof(uint32_t);
+    } else if (pl.sliced) {
+        pl.n_hist = S * kBuckets;
+        pl.zero_words = 2 * pl.n_hist + S;  // merged and shared histograms, tickets
+        pl.info_words = S * P * 4;
+        const size_t cum_words = S * P * kBuckets;
+        size_t bytes = (pl.zero_words + pl.info_words + cum_words) * 4;
+        bytes = (bytes + 255) & ~(size_t)255;
+        pl.data_off = bytes;
+        pl.scratch_bytes = bytes + S * P * (size_t)stash_cap * sizeof(uint2);
+    }
+    return SEGTOPK_OK;
+}
+
+// Points the plan's scratch fields into `ws`.
+void bind_scratch(Plan &pl, void *ws) {
+    Params &p = pl.p;
+    uint32_t *wsw = static_cast<uint32_t *>(ws);
+    if (pl.order) {
+        p.order = wsw;
+    } else if (pl.sliced) {
+        p.ws_hist = wsw;
+        p.ws_early = wsw + pl.n_hist;
+        p.ws_ticket = wsw + 2 * pl.n_hist;
+        p.ws_slot_info = wsw + pl.zero_words;
+        p.ws_slot_cum = wsw + pl.zero_words + pl.info_words;
+        p.ws_slot_data = reinterpret_cast<uint2 *>(static_cast<char *>(ws) + pl.data_off);
+    }
+}
+
+// Queues the plan's kernels on `stream`: the clearing kernel when asked, the
+// order kernel, the selection, and the 8-byte value gather.
+hipError_t queue(const Request &r, const Plan &pl, bool clear, hipStream_t stream) {
+    hipError_t err = hipSuccess;
+    if (clear) {
+        size_t zb = (pl.zero_words + 255) / 256;
+        if (zb > 1024) zb = 1024;
+        if (zb < 1) zb = 1;
+        hipLaunchKernelGGL(zero_kernel, dim3((unsigned)zb), dim3(256), 0, stream,
+                           const_cast<uint32_t *>(pl.p.ws_hist), pl.zero_words);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
+    if (pl.order) {
+        hipLaunchKernelGGL(order_kernel, dim3(1), dim3(1024), 0, stream, r.offsets,
+                           r.num_segments, const_cast<uint32_t *>(pl.p.order));
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
+    err = launch(pl.type, pl.p, pl.largest, pl.variant, pl.grid, pl.lds, stream);
+    if (err != hipSuccess) return err;
+    if (pl.wide_values) {
+        const uint64_t total = (uint64_t)r.num_segments * (uint64_t)r.k;
+        uint64_t blocks = (total + 255) / 256;
+        if (blocks > 4096) blocks = 4096;
+        hipLaunchKernelGGL(gather64_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                           r.offsets, r.kseg, r.num_segments, (uint32_t)r.k,
+                           static_cast<const uint64_t *>(r.values->in),
+                           static_cast<uint64_t *>(r.values->out));
+        err = hipGetLastError();
+    }
+    return err;
+}
+
+int run(const Request &r) {
+    const int v = validate(r);
+    if (v >= 0) return v;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return SEGTOPK_HIP_ERROR;
+    Plan pl;
+    const int ps = make_plan(r, dev, pl);
+    if (ps != SEGTOPK_OK) return ps;
+    const hipStream_t stream = r.stream;
+    if (pl.scratch_bytes == 0)
+        return queue(r, pl, false, stream) == hipSuccess ? SEGTOPK_OK : SEGTOPK_HIP_ERROR;
+
+    // The scratch cache decides on the host what the stream's buffer holds;
+    // a captured graph would replay those decisions against a buffer that
+    // may have been regrown or dirtied since.
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cs) != hipSuccess) return SEGTOPK_HIP_ERROR;
+    if (cs != hipStreamCaptureStatusNone) return SEGTOPK_NOT_SUPPORTED;
+
+    std::lock_guard<std::mutex> lk(g_ws_mu);
+    WsBuf *wsb = nullptr;
+    if (stream_scratch(dev, stream, pl.scratch_bytes, &wsb) != hipSuccess) return SEGTOPK_HIP_ERROR;
+    bind_scratch(pl, wsb->ptr);
+    bool clear = false;
+    if (pl.order) {
+        wsb->clean_words = 0;  // the order overwrites the front
+    } else {
+        clear = wsb->clean_words < pl.zero_words;
+        // The slots (after the cleared words) are written by this call; the
+        // sliced kernel clears the histograms and tickets it used.
+        wsb->clean_words = 0;
+    }
+    hipError_t err = queue(r, pl, clear, stream);
+    if (err == hipSuccess && pl.sliced) wsb->clean_words = pl.zero_words;
+    const hipError_t e = hipEventRecord(wsb->done, stream);
+    if (err == hipSuccess) err = e;
+    return err == hipSuccess ? SEGTOPK_OK : SEGTOPK_HIP_ERROR;
 }
 
 }  // namespace
@@ -210,153 +536,19 @@ extern "C" int batched_topk(const segtopk_keys *keys, const segtopk_values *valu
                             const int64_t *segment_offsets, int64_t num_segments, int64_t k,
                             int direction, int determinism, int tie_break, int ordering,
                             hipStream_t stream) {
-    // ---- validation (no HIP call before it passes) ----
-    if (!keys) return SEGTOPK_INVALID_ARGUMENT;
-    const int type = keys->type;
-    if (type < SEGTOPK_KEY_F32 || type > SEGTOPK_KEY_F16) return SEGTOPK_INVALID_ARGUMENT;
-    if (direction != SEGTOPK_MAX && direction != SEGTOPK_MIN) return SEGTOPK_INVALID_ARGUMENT;
-    if (determinism < SEGTOPK_NOT_GUARANTEED || determinism > SEGTOPK_GPU_TO_GPU)
-        return SEGTOPK_INVALID_ARGUMENT;
-    if (tie_break < SEGTOPK_TIE_UNSPECIFIED || tie_break > SEGTOPK_PREFER_LARGER_INDEX)
-        return SEGTOPK_INVALID_ARGUMENT;
-    if (ordering < SEGTOPK_UNSORTED || ordering > SEGTOPK_STABLE_SORTED)
-        return SEGTOPK_INVALID_ARGUMENT;
-    // An explicit index tie-break pins the set across GPUs, so it must come
-    // with gpu_to_gpu.   [docs "Top-K: Determinism ...", "Which items are selected?"]
-    if (tie_break != SEGTOPK_TIE_UNSPECIFIED && determinism != SEGTOPK_GPU_TO_GPU)
-        return SEGTOPK_INVALID_ARGUMENT;
-    if (k < 0 || k > INT32_MAX || num_segments < 0 || num_segments > INT32_MAX)
-        return SEGTOPK_INVALID_ARGUMENT;
-    if (num_segments == 0 || k == 0) return SEGTOPK_OK;
-    if (!keys->in || !keys->out || !segment_offsets) return SEGTOPK_INVALID_ARGUMENT;
-    const bool pairs = values && values->in;
-    if (pairs && !values->out) return SEGTOPK_INVALID_ARGUMENT;
-    const int kb = key_bytes(type);
-    if ((reinterpret_cast<uintptr_t>(keys->in) % kb) || (reinterpret_cast<uintptr_t>(keys->out) % kb))
-        return SEGTOPK_INVALID_ARGUMENT;
-    if (pairs && ((reinterpret_cast<uintptr_t>(values->in) & 3) ||
-                  (reinterpret_cast<uintptr_t>(values->out) & 3)))
-        return SEGTOPK_INVALID_ARGUMENT;
-    if ((reinterpret_cast<uintptr_t>(segment_offsets) & 7)) return SEGTOPK_INVALID_ARGUMENT;
-    const bool sorted = ordering != SEGTOPK_UNSORTED;
-    if (sorted && k > SEGTOPK_MAX_SORTED_K) return SEGTOPK_NOT_SUPPORTED;
+    const Request r{keys, values, 4, segment_offsets, num_segments, k, nullptr, 0,
+                    direction, determinism, tie_break, ordering, stream};
+    return run(r);
+}
 
-    // ---- plan ----
-    Params p = {};
-    p.keys_in = keys->in;
-    p.keys_out = keys->out;
-    p.vals_in = pairs ? static_cast<const uint32_t *>(values->in) : nullptr;
-    p.vals_out = pairs ? static_cast<uint32_t *>(values->out) : nullptr;
-    p.offsets = segment_offsets;
-    p.num_segments = num_segments;
-    p.k = (uint32_t)k;
-    p.det = determinism != SEGTOPK_NOT_GUARANTEED;
-    p.prefer_larger = tie_break == SEGTOPK_PREFER_LARGER_INDEX;
-    p.sorted = sorted;
-
-    const uint32_t k32 = (uint32_t)k;
-    // Output staging: sorted output is staged and sorted in LDS; unsorted
-    // output only for small k (coalesced row writes), else written in place.
-    uint32_t out_cap = next_pow2(k32 < 2 ? 2 : k32);
-    if (!sorted && out_cap > 256) out_cap = 0;
-    // Several workgroups per segment when the segments alone cannot fill the
-    // device.  Stash: with one workgroup per segment, room for about eight
-    // times k candidates in four wave regions; with several, the
-    // segment-wide bound keeps each slice's candidates few, and the stash
-    // only has to hold bucket b* of the last arriver (about 2k at most).
-    const bool split = (uint64_t)num_segments < kTargetWorkgroups;
-    uint32_t stash_cap = next_pow2((split ? 2 : 8) * k32);
-    if (stash_cap < (split ? 2048u : 1024u)) stash_cap = split ? 2048u : 1024u;
-    if (stash_cap > 8192) stash_cap = 8192;
-    while (stash_cap > 1024 && 8 * (size_t)(stash_cap + out_cap) > kMaxDynLds) stash_cap >>= 1;
-    if (8 * (size_t)(stash_cap + out_cap) > kMaxDynLds) return SEGTOPK_NOT_SUPPORTED;
-    p.stash_cap = stash_cap;
-    p.out_cap = out_cap;
-    const size_t lds = 8 * (size_t)(stash_cap + out_cap);
-
-    int dev = 0;
-    uint32_t P = 1;
-    if (split) {
-        // As many workgroups as the device holds at once, so that all the
-        // slices of a segment run together and share their bound.
-        if (hipGetDevice(&dev) != hipSuccess) return SEGTOPK_HIP_ERROR;
-        const uint32_t target = resident_wgs_for(type, dev, direction == SEGTOPK_MAX, lds);
-        P = (uint32_t)((target + num_segments - 1) / num_segments);
-        if (P > kMaxWgPerSeg) P = kMaxWgPerSeg;
-        if (P < 1) P = 1;
-    }
-    uint32_t min_slice = kMinSlice;
-    if ((uint64_t)8 * k32 > min_slice) min_slice = 8 * k32 > (1u << 30) ? (1u << 30) : 8 * k32;
-    if (k32 * 2 > stash_cap) P = 1;  // slices could not hold their local candidates
-    p.wg_per_seg = P;
-    p.min_slice = min_slice;
-
-    const uint64_t S8 = ((uint64_t)num_segments + 7) / 8 * 8;
-    const uint64_t grid = S8 * P;
-    if (grid > 0x7FFFFFFFull) return SEGTOPK_NOT_SUPPORTED;
-
-    void *ws = nullptr;
-    WsBuf *wsb = nullptr;
-    size_t zero_words_used = 0;
-    std::unique_lock<std::mutex> ws_lock(g_ws_mu, std::defer_lock);
-    hipError_t err = hipSuccess;
-    if (split && P == 1 && num_segments >= kOrderMinSegments) {
-        // One workgroup per segment for many segments of unknown sizes:
-        // process the largest first.
-        if (hipGetDevice(&dev) != hipSuccess) return SEGTOPK_HIP_ERROR;
-        prepare_pool(dev);
-        ws_lock.lock();
-        if (stream_scratch(dev, stream, (size_t)num_segments * sizeof(uint32_t), &wsb) != hipSuccess)
-            return SEGTOPK_HIP_ERROR;
-        ws = wsb->ptr;
-        wsb->clean_words = 0;  // the order overwrites the front
-        p.order = static_cast<const uint32_t *>(ws);
-        hipLaunchKernelGGL(order_kernel, dim3(1), dim3(1024), 0, stream, segment_offsets,
-                           num_segments, static_cast<uint32_t *>(ws));
-        err = hipGetLastError();
-    } else if (P > 1) {
-        prepare_pool(dev);
-        const size_t S = (size_t)num_segments;
-        const size_t n_hist = S * kBuckets, n_ticket = S;
-        const size_t zero_words = 2 * n_hist + n_ticket;
-        zero_words_used = zero_words;
-        const size_t info_words = S * P * 4;
-        const size_t cum_words = S * P * kBuckets;
-        size_t bytes = (zero_words + info_words + cum_words) * 4;
-        bytes = (bytes + 255) & ~(size_t)255;
-        const size_t data_off = bytes;
-        bytes += S * P * (size_t)stash_cap * sizeof(uint2);
-        ws_lock.lock();
-        if (stream_scratch(dev, stream, bytes, &wsb) != hipSuccess) return SEGTOPK_HIP_ERROR;
-        ws = wsb->ptr;
-        uint32_t *wsw = static_cast<uint32_t *>(ws);
-        p.ws_hist = wsw;
-        p.ws_early = wsw + n_hist;
-        p.ws_ticket = wsw + 2 * n_hist;
-        p.ws_slot_info = wsw + zero_words;
-        p.ws_slot_cum = wsw + zero_words + info_words;
-        p.ws_slot_data = reinterpret_cast<uint2 *>(static_cast<char *>(ws) + data_off);
-        if (wsb->clean_words < zero_words) {
-            size_t zb = (zero_words + 255) / 256;
-            if (zb > 1024) zb = 1024;
-            hipLaunchKernelGGL(zero_kernel, dim3((unsigned)zb), dim3(256), 0, stream, wsw, zero_words);
-            err = hipGetLastError();
-        }
-        // The slots (after the cleared words) are written by this call; the
-        // sliced kernel clears the histograms and tickets it used.
-        wsb->clean_words = 0;
-    }
-    if (err == hipSuccess) {
-        const bool largest = direction == SEGTOPK_MAX;
-        const int variant = !split ? kVariantOne : (P > 1 ? kVariantSliced : kVariantSplit);
-        err = launch(type, p, largest, variant, (uint32_t)grid, lds, stream);
-        if (err == hipSuccess && variant == kVariantSliced) wsb->clean_words = zero_words_used;
-    }
-    if (wsb) {
-        const hipError_t e = hipEventRecord(wsb->done, stream);
-        if (err == hipSuccess) err = e;
-    }
-    return err == hipSuccess ? SEGTOPK_OK : SEGTOPK_HIP_ERROR;
+extern "C" int batched_topk_ex(const segtopk_keys *keys, const segtopk_values *values,
+                               int32_t value_bytes, const int64_t *segment_offsets,
+                               int64_t num_segments, int64_t k, const int32_t *k_per_segment,
+                               int64_t max_segment_size, int direction, int determinism,
+                               int tie_break, int ordering, hipStream_t stream) {
+    const Request r{keys, values, value_bytes, segment_offsets, num_segments, k, k_per_segment,
+                    max_segment_size, direction, determinism, tie_break, ordering, stream};
+    return run(r);
 }
 
 extern "C" const char *segtopk_status_string(int status) {
@@ -369,4 +561,4 @@ extern "C" const char *segtopk_status_string(int status) {
     }
 }
 
-extern "C" int segtopk_version(void) { return 200; }
+extern "C" int segtopk_version(void) { return 300; }

@@ -22,6 +22,7 @@ constexpr uint32_t kBlockFinishMin = 512;  // longer candidate lists are finishe
 constexpr uint32_t kNone = 0xFFFFFFFFu; // "no element" / sort padding
 constexpr int kSplitU = 8;               // loads per lane per chunk when segments are split
 constexpr size_t kMaxDynLds = 120 * 1024;
+constexpr uint32_t kMaxWgPerSeg = 1024;  // slices of one segment (the last arriver's prefix table fits LDS)
 
 // ---------------------------------------------------------------------------
 // Kernel arguments.
@@ -33,7 +34,8 @@ struct Params {
     uint32_t *vals_out;
     const int64_t *offsets;
     int64_t num_segments;
-    uint32_t k;              // output row stride
+    const int32_t *kseg;     // [segments] per-segment k (clamped to [0, k]), or nullptr
+    uint32_t k;              // output row stride and largest k
     uint32_t det;            // deterministic tie-break requested
     uint32_t prefer_larger;  // ties toward larger source indices
     uint32_t sorted;         // sorted or stable_sorted output
@@ -48,6 +50,10 @@ struct Params {
     uint32_t *ws_slot_cum;   // [segments][P][kBuckets] entries with rank <= r
     uint2 *ws_slot_data;     // [segments][P][stash_cap] candidates sorted by rank
     const uint32_t *order;   // [segments] processing order (one workgroup each), or nullptr
+    uint32_t spread;         // workgroup b serves segment b / P, slice b % P (small batches)
+    uint32_t vindex;         // write the source index as the value (no gather)
+    uint32_t vshift;         // value slot o is vals_out[o << vshift] (1: 8-byte slots)
+    uint32_t pad_;
 };
 
 // Kernel variants: one workgroup per segment for many segments (4 loads per

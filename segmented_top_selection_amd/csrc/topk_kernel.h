@@ -47,6 +47,8 @@
 //     ordering]
 #pragma once
 
+#include <atomic>
+
 #include "topk_common.h"
 
 namespace segtopk_impl {
@@ -104,6 +106,18 @@ template <> struct Key<SEGTOPK_KEY_U32> {
     __host__ __device__ __forceinline__ static uint32_t ord(uint32_t r) { return r; }
     __host__ __device__ __forceinline__ static uint32_t inv_ord(uint32_t o) { return o; }
 };
+template <> struct Key<SEGTOPK_KEY_U16> {
+    static constexpr int kBits = 16, kBytes = 2;
+    static constexpr bool kSignMag = false;
+    __host__ __device__ __forceinline__ static uint32_t ord(uint32_t r) { return r & 0xFFFFu; }
+    __host__ __device__ __forceinline__ static uint32_t inv_ord(uint32_t o) { return o & 0xFFFFu; }
+};
+template <> struct Key<SEGTOPK_KEY_I16> {
+    static constexpr int kBits = 16, kBytes = 2;
+    static constexpr bool kSignMag = false;
+    __host__ __device__ __forceinline__ static uint32_t ord(uint32_t r) { return (r ^ 0x8000u) & 0xFFFFu; }
+    __host__ __device__ __forceinline__ static uint32_t inv_ord(uint32_t o) { return (o ^ 0x8000u) & 0xFFFFu; }
+};
 template <> struct Key<SEGTOPK_KEY_I32> {
     static constexpr int kBits = 32, kBytes = 4;
     static constexpr bool kSignMag = false;
@@ -155,10 +169,10 @@ __host__ __device__ __forceinline__ Prefilter prefilter_thr(uint32_t thr) {
     constexpr uint32_t H = 1u << (B - 1);
     constexpr uint32_t M = B == 32 ? 0xFFFFFFFFu : 0xFFFFu;
     uint32_t mode, T;
-    if constexpr (KT == SEGTOPK_KEY_U32) {
+    if constexpr (KT == SEGTOPK_KEY_U32 || KT == SEGTOPK_KEY_U16) {
         mode = LARGEST ? kPfMaxU : kPfMinU;
         T = thr;
-    } else if constexpr (KT == SEGTOPK_KEY_I32) {
+    } else if constexpr (KT == SEGTOPK_KEY_I32 || KT == SEGTOPK_KEY_I16) {
         mode = LARGEST ? kPfMaxS : kPfMinS;
         T = thr ^ H;
     } else if (LARGEST) {
@@ -1017,6 +1031,15 @@ template <int KT> struct Cands {
 // ---------------------------------------------------------------------------
 // Output.
 // ---------------------------------------------------------------------------
+// The value of the segment's element idx: the payload, or (index mode, used
+// for 8-byte payloads that a later pass gathers) the index itself.
+__device__ __forceinline__ uint32_t val_load(const Params &p, const Seg &sg, uint32_t idx) {
+    return p.vindex ? idx : p.vals_in[sg.begin + idx];
+}
+__device__ __forceinline__ void val_store(const Params &p, size_t o, uint32_t v) {
+    p.vals_out[o << p.vshift] = v;
+}
+
 template <int KT>
 __device__ __forceinline__ void write_out(const Params &p, const Seg &sg, uint32_t pos,
                                           uint32_t raw, uint32_t idx) {
@@ -1028,7 +1051,7 @@ __device__ __forceinline__ void write_out(const Params &p, const Seg &sg, uint32
         static_cast<uint32_t *>(p.keys_out)[o] = raw;
     else
         static_cast<uint16_t *>(p.keys_out)[o] = (uint16_t)raw;
-    if (p.vals_in) p.vals_out[o] = idx < sg.n ? p.vals_in[sg.begin + idx] : kNone;
+    if (p.vals_in) val_store(p, o, idx < sg.n ? val_load(p, sg, idx) : kNone);
 }
 
 // write_out for B entries per lane: every value load is issued before the
@@ -1039,7 +1062,7 @@ __device__ __forceinline__ void write_batch(const Params &p, const Seg &sg, cons
     uint32_t v[B];
 #pragma unroll
     for (int u = 0; u < B; ++u)
-        v[u] = (p.vals_in && pos[u] < sg.k_i && e[u].y < sg.n) ? p.vals_in[sg.begin + e[u].y] : kNone;
+        v[u] = (p.vals_in && pos[u] < sg.k_i && e[u].y < sg.n) ? val_load(p, sg, e[u].y) : kNone;
 #pragma unroll
     for (int u = 0; u < B; ++u) {
         if (pos[u] >= sg.k_i) continue;
@@ -1048,7 +1071,7 @@ __device__ __forceinline__ void write_batch(const Params &p, const Seg &sg, cons
             static_cast<uint32_t *>(p.keys_out)[o] = e[u].x;
         else
             static_cast<uint16_t *>(p.keys_out)[o] = (uint16_t)e[u].x;
-        if (p.vals_in) p.vals_out[o] = v[u];
+        if (p.vals_in) val_store(p, o, v[u]);
     }
 }
 
@@ -1236,7 +1259,7 @@ __device__ __forceinline__ void sort_select(const uint2 *list, uint32_t m, const
         pos[e] = j;
         if (j >= a) pos[e] = (j >= a + shift) ? j - shift : kNone;
         if (j >= m) pos[e] = kNone;
-        vv[e] = (p.vals_in && pos[e] < sg.k_i && id[e] < sg.n) ? p.vals_in[sg.begin + id[e]] : kNone;
+        vv[e] = (p.vals_in && pos[e] < sg.k_i && id[e] < sg.n) ? val_load(p, sg, id[e]) : kNone;
     }
 #pragma unroll
     for (int e = 0; e < E; ++e) {
@@ -1247,7 +1270,7 @@ __device__ __forceinline__ void sort_select(const uint2 *list, uint32_t m, const
                 static_cast<uint32_t *>(p.keys_out)[o] = rw;
             else
                 static_cast<uint16_t *>(p.keys_out)[o] = (uint16_t)rw;
-            if (p.vals_in) p.vals_out[o] = vv[e];
+            if (p.vals_in) val_store(p, o, vv[e]);
         }
     }
 }
@@ -1889,9 +1912,19 @@ __global__ __launch_bounds__(kThreads, (topk_waves<KT, U>())) void topk_kernel(P
 
     const uint32_t P = p.wg_per_seg;
     const uint32_t b = blockIdx.x;
-    const uint32_t qq = b >> 3;
-    int64_t s = (int64_t)(qq / P) * 8 + (b & 7u);
-    const uint32_t q = qq % P;
+    int64_t s;
+    uint32_t q;
+    if (p.spread) {
+        // A batch of few segments: each segment's workgroups are consecutive,
+        // so the dispatcher deals them over every XCD.
+        s = (int64_t)(b / P);
+        q = b % P;
+    } else {
+        // Workgroups of one segment share b % 8, the XCD they run on.
+        const uint32_t qq = b >> 3;
+        s = (int64_t)(qq / P) * 8 + (b & 7u);
+        q = qq % P;
+    }
     if (p.order) {  // one workgroup per segment, largest segments first
         if ((int64_t)b >= p.num_segments) return;
         s = p.order[b];
@@ -1903,12 +1936,17 @@ __global__ __launch_bounds__(kThreads, (topk_waves<KT, U>())) void topk_kernel(P
     const int64_t end = p.offsets[s + 1];
     sg.n = end > sg.begin ? (uint32_t)(end - sg.begin) : 0u;
     sg.k_i = sg.n < p.k ? sg.n : p.k;
+    if (p.kseg) {  // per-segment k, clamped to [0, k]
+        const int32_t ks = p.kseg[s];
+        const uint32_t ku = ks > 0 ? (uint32_t)ks : 0u;
+        sg.k_i = ku < sg.k_i ? ku : sg.k_i;
+    }
     sg.row = s;
     if (sg.k_i == 0) return;
 
     // Workgroups that share this segment.
     uint32_t ps = 1, slice = sg.n;
-    if (P > 1 && sg.n > p.k) {
+    if (P > 1 && sg.n > sg.k_i) {
         uint32_t sl = (uint32_t)(((uint64_t)sg.n + P - 1) / P);
         if (sl < p.min_slice) sl = p.min_slice;
         sl = (sl + 255u) & ~255u;
@@ -1917,7 +1955,7 @@ __global__ __launch_bounds__(kThreads, (topk_waves<KT, U>())) void topk_kernel(P
     }
     if (q >= ps) return;
 
-    if (sg.n <= p.k) {  // select-all: one wave does it
+    if (sg.n <= sg.k_i) {  // select-all: one wave does it
         if (w == 0) wave_select_all<KT, LARGEST>(outbuf, p, sg);
         return;
     }
@@ -2109,11 +2147,19 @@ __global__ __launch_bounds__(kThreads, (topk_waves<KT, U>())) void topk_kernel(P
     slice_last<KT, LARGEST, SLICED>(sh, stash, outbuf, p, sg, s, P, ps, slice);
 }
 
-// Dynamic LDS above 64 KiB has to be allowed per kernel.
+// Dynamic LDS above 64 KiB has to be allowed per kernel, once per device.
 template <typename K> hipError_t allow_lds(K kernel, size_t lds) {
+    static std::atomic<uint64_t> done{0};
     if (lds <= 64 * 1024) return hipSuccess;
-    return hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxDynLds);
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint64_t bit = dev < 64 ? (1ull << dev) : 0ull;
+    if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxDynLds);
+    if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_acq_rel);
+    return e;
 }
 
 template <int KT, bool LARGEST, int U, bool SLICED>

@@ -22,11 +22,13 @@ import oracle
 import segmented_top_selection_amd as st
 
 KEY_CANARY = {"f32": 0x7FC0BEEF, "u32": 0x7FC0BEEF, "i32": 0x7FC0BEEF, "bf16": 0xFFBE,
-              "f16": 0xFFBE}
+              "f16": 0xFFBE, "u16": 0xFFBE, "i16": 0xFFBE}
 VAL_CANARY = 0x5EEDF00D
+VAL_CANARY64 = 0x5EEDF00DCAFED00D
 
 TORCH_KEY_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16,
-                   "u32": torch.int32, "i32": torch.int32}
+                   "u32": torch.int32, "i32": torch.int32, "u16": torch.int16,
+                   "i16": torch.int16}
 
 
 def key_bits_np(t: torch.Tensor) -> np.ndarray:
@@ -45,14 +47,18 @@ def numeric_np(bits: np.ndarray, key_type: str) -> np.ndarray:
         return (bits << 16).astype(np.uint32).view(np.float32).astype(np.float64)
     if key_type == "f16":
         return bits.astype(np.uint16).view(np.float16).astype(np.float64)
-    if key_type == "u32":
+    if key_type in ("u32", "u16"):
         return bits.astype(np.float64)
+    if key_type == "i16":
+        return bits.astype(np.uint16).view(np.int16).astype(np.float64)
     return bits.view(np.int32).astype(np.float64)
 
 
 def oracle_keys_view(bits_u32: np.ndarray, key_type: str) -> np.ndarray:
-    if key_type in ("bf16", "f16"):
+    if key_type in ("bf16", "f16", "u16"):
         return bits_u32.astype(np.uint16)
+    if key_type == "i16":
+        return bits_u32.astype(np.uint16).view(np.int16)
     if key_type == "f32":
         return bits_u32.view(np.float32)
     if key_type == "u32":
@@ -60,7 +66,16 @@ def oracle_keys_view(bits_u32: np.ndarray, key_type: str) -> np.ndarray:
     return bits_u32.view(np.int32)
 
 
-def run_gpu(keys, values, offsets, k, key_type, largest, determinism, tie_break, ordering):
+def _vals_np(t):
+    """A payload tensor as uint32 or uint64 numpy (by element size)."""
+    a = t.detach().cpu().contiguous()
+    if a.element_size() == 8:
+        return a.view(torch.int64).numpy().view(np.uint64)
+    return a.view(torch.int32).numpy().view(np.uint32)
+
+
+def run_gpu(keys, values, offsets, k, key_type, largest, determinism, tie_break, ordering,
+            k_per_segment=None, max_segment_size=None):
     """Runs the library on device tensors with canary-filled outputs."""
     s = offsets.numel() - 1
     if os.environ.get("SEGTOPK_TEST_TRACE"):
@@ -75,13 +90,17 @@ def run_gpu(keys, values, offsets, k, key_type, largest, determinism, tie_break,
         out_k.view(torch.int32).fill_(KEY_CANARY[key_type])
     out_v = None
     if values is not None:
-        out_v = torch.full((s, k), VAL_CANARY, dtype=torch.int32, device=dev)
+        if values.element_size() == 8:
+            out_v = torch.full((s, k), VAL_CANARY64, dtype=torch.int64, device=dev)
+        else:
+            out_v = torch.full((s, k), VAL_CANARY, dtype=torch.int32, device=dev)
     st.batched_topk(keys, offsets, k, values=values, largest=largest, determinism=determinism,
                     tie_break=tie_break, ordering=ordering, key_type=key_type,
-                    out_keys=out_k, out_values=out_v)
+                    out_keys=out_k, out_values=out_v, k_per_segment=k_per_segment,
+                    max_segment_size=max_segment_size)
     torch.cuda.synchronize()
     gk = key_bits_np(out_k).reshape(s, k)
-    gv = out_v.cpu().numpy().view(np.uint32).reshape(s, k) if out_v is not None else None
+    gv = _vals_np(out_v).reshape(s, k) if out_v is not None else None
     return gk, gv
 
 
@@ -90,7 +109,7 @@ def host_problem(keys, values, offsets_np, rows=None):
     segments, or of the listed rows re-packed as consecutive segments."""
     if rows is None:
         kb = key_bits_np(keys)
-        vb = values.cpu().numpy().view(np.uint32) if values is not None else None
+        vb = _vals_np(values) if values is not None else None
         return kb, vb, offsets_np
     parts_k, parts_v, off = [], [], [0]
     for r in rows:
@@ -98,34 +117,38 @@ def host_problem(keys, values, offsets_np, rows=None):
         n = max(0, e - b)
         parts_k.append(key_bits_np(keys[b:b + n]))
         if values is not None:
-            parts_v.append(values[b:b + n].cpu().numpy().view(np.uint32))
+            parts_v.append(_vals_np(values[b:b + n]))
         off.append(off[-1] + n)
     kb = np.concatenate(parts_k) if parts_k else np.zeros(0, np.uint32)
     vb = np.concatenate(parts_v) if values is not None else None
     return kb, vb, np.array(off, dtype=np.int64)
 
 
-def run_oracle(keys_bits, values_u32, offsets_np, k, key_type, largest, prefer_larger):
+def run_oracle(keys_bits, values_u32, offsets_np, k, key_type, largest, prefer_larger,
+               k_per_segment=None):
     ok, ov = oracle.batched_topk(oracle_keys_view(keys_bits, key_type), offsets_np, k,
                                  key_type=key_type, values=values_u32, largest=largest,
-                                 prefer_larger=prefer_larger)
-    ok = ok.astype(np.uint32) if ok.dtype == np.uint16 else ok.view(np.uint32)
+                                 prefer_larger=prefer_larger, k_per_segment=k_per_segment)
+    ok = ok.view(np.uint16).astype(np.uint32) if ok.dtype.itemsize == 2 else ok.view(np.uint32)
     return ok, ov
 
 
-def _row_sizes(offsets_np, k):
+def _row_sizes(offsets_np, k, kseg=None):
     n = np.maximum(offsets_np[1:] - offsets_np[:-1], 0)
-    return n, np.minimum(n, k)
+    ki = np.minimum(n, k)
+    if kseg is not None:
+        ki = np.minimum(ki, np.clip(np.asarray(kseg, dtype=np.int64), 0, None))
+    return n, ki
 
 
 def compare(gk, gv, ok, ov, offsets_np, k, key_type, determinism, ordering, keys_bits,
-            values_are="index"):
+            values_are="index", kseg=None):
     """Asserts that the GPU rows (gk, gv) agree with the oracle rows (ok, ov);
     offsets_np / keys_bits describe exactly these rows.  ``values_are`` says
     what the payload holds, for the not_guaranteed validity check: the source
     index inside the segment ("index") or the key's position in the whole key
     array ("position"; needed when segments overlap)."""
-    n_all, ki = _row_sizes(offsets_np, k)
+    n_all, ki = _row_sizes(offsets_np, k, kseg)
     rows = np.arange(gk.shape[0])
     col = np.arange(k)[None, :]
     valid = col < ki[:, None]
@@ -134,7 +157,8 @@ def compare(gk, gv, ok, ov, offsets_np, k, key_type, determinism, ordering, keys
     # untouched tails
     assert np.all(gk[~valid] == key_canary), "key slot past k_i was written"
     if gv is not None:
-        assert np.all(gv[~valid] == VAL_CANARY), "value slot past k_i was written"
+        vcan = VAL_CANARY64 if gv.dtype == np.uint64 else VAL_CANARY
+        assert np.all(gv[~valid] == vcan), "value slot past k_i was written"
 
     if determinism != "not_guaranteed":
         if ordering != "unsorted":
@@ -145,13 +169,16 @@ def compare(gk, gv, ok, ov, offsets_np, k, key_type, determinism, ordering, keys
                 assert not badv.any(), f"value mismatch in rows {rows[np.nonzero(badv.any(1))[0][:8]]}"
         else:
             def canon(kk, vv):
-                c = kk.astype(np.uint64) << np.uint64(32)
-                if vv is not None:
-                    c |= vv.astype(np.uint64)
-                c = np.where(valid, c, np.uint64(0xFFFFFFFFFFFFFFFF))
-                return np.sort(c, axis=1)
+                # each row's (key bits, value) pairs in a canonical order
+                kcol = np.where(valid, kk.astype(np.uint64), np.uint64(2 ** 63))
+                if vv is None:
+                    return np.sort(kcol, axis=1)[:, None, :]
+                vcol = np.where(valid, vv.astype(np.uint64), np.uint64(0))
+                order = np.lexsort((vcol, kcol), axis=1)
+                return np.stack([np.take_along_axis(kcol, order, 1),
+                                 np.take_along_axis(vcol, order, 1)], axis=1)
             a, b = canon(gk, gv), canon(ok, ov)
-            bad = a != b
+            bad = (a != b).any(axis=1)
             assert not bad.any(), f"set mismatch in rows {rows[np.nonzero(bad.any(1))[0][:8]]}"
         return
 
@@ -177,19 +204,22 @@ def compare(gk, gv, ok, ov, offsets_np, k, key_type, determinism, ordering, keys
 
 def check(keys, values, offsets, k, key_type, largest=True, determinism="gpu_to_gpu",
           tie_break="prefer_smaller_index", ordering="stable_sorted", rows=None,
-          values_are="index"):
+          values_are="index", k_per_segment=None, max_segment_size=None):
     """GPU call on device tensors, oracle on host copies, row comparison.
     With ``rows`` only those rows are checked (the GPU still runs all)."""
     gk, gv = run_gpu(keys, values, offsets, k, key_type, largest, determinism, tie_break,
-                     ordering)
+                     ordering, k_per_segment, max_segment_size)
     off = offsets.cpu().numpy()
     kb, vb, sub_off = host_problem(keys, values, off, rows)
+    kseg = k_per_segment.cpu().numpy() if k_per_segment is not None else None
+    if kseg is not None and rows is not None:
+        kseg = kseg[np.asarray(rows)]
     ok, ov = run_oracle(kb, vb, sub_off, k, key_type, largest,
-                        tie_break == "prefer_larger_index")
+                        tie_break == "prefer_larger_index", kseg)
     if rows is not None:
         gk = gk[np.asarray(rows)]
         gv = gv[np.asarray(rows)] if gv is not None else None
-    compare(gk, gv, ok, ov, sub_off, k, key_type, determinism, ordering, kb, values_are)
+    compare(gk, gv, ok, ov, sub_off, k, key_type, determinism, ordering, kb, values_are, kseg)
     return gk, gv
 
 
@@ -209,7 +239,7 @@ def check_all_rows(keys, values, offsets, k, key_type, largest=True, determinism
         b, e = int(off[r0]), int(off[r1])
         assert np.all(np.diff(off[r0:r1 + 1]) >= 0), "check_all_rows needs ordered offsets"
         kb = key_bits_np(keys[b:e])
-        vb = values[b:e].cpu().numpy().view(np.uint32) if values is not None else None
+        vb = _vals_np(values[b:e]) if values is not None else None
         sub_off = off[r0:r1 + 1] - b
         ok, ov = run_oracle(kb, vb, sub_off, k, key_type, largest,
                             tie_break == "prefer_larger_index")

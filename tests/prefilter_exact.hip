@@ -124,8 +124,10 @@ template <int KT> static double decode(uint32_t x) {
         _Float16 h;
         std::memcpy(&h, &h16, 2);
         return (double)h;
-    } else if constexpr (KT == SEGTOPK_KEY_U32) {
+    } else if constexpr (KT == SEGTOPK_KEY_U32 || KT == SEGTOPK_KEY_U16) {
         return (double)x;
+    } else if constexpr (KT == SEGTOPK_KEY_I16) {
+        return (double)(int16_t)(uint16_t)x;
     } else {
         return (double)(int32_t)x;
     }
@@ -183,9 +185,11 @@ int main(int argc, char **argv) {
         check_order<SEGTOPK_KEY_F16>(k16, "f16"); types_caught += g_bad > before; before = g_bad;
         check_order<SEGTOPK_KEY_F32>(k32, "f32"); types_caught += g_bad > before; before = g_bad;
         check_order<SEGTOPK_KEY_U32>(k32, "u32"); types_caught += g_bad > before; before = g_bad;
-        check_order<SEGTOPK_KEY_I32>(k32, "i32"); types_caught += g_bad > before;
-        std::printf("perturbed transform caught for %ld of 5 key types\n", types_caught);
-        return types_caught == 5 ? 0 : 1;
+        check_order<SEGTOPK_KEY_I32>(k32, "i32"); types_caught += g_bad > before; before = g_bad;
+        check_order<SEGTOPK_KEY_U16>(k16, "u16"); types_caught += g_bad > before; before = g_bad;
+        check_order<SEGTOPK_KEY_I16>(k16, "i16"); types_caught += g_bad > before;
+        std::printf("perturbed transform caught for %ld of 7 key types\n", types_caught);
+        return types_caught == 7 ? 0 : 1;
     }
     std::vector<uint32_t> k16;
     for (uint32_t x = 0; x < 65536u; ++x) k16.push_back(x);
@@ -203,6 +207,8 @@ int main(int argc, char **argv) {
     }
     check_order<SEGTOPK_KEY_BF16>(k16, "bf16");
     check_order<SEGTOPK_KEY_F16>(k16, "f16");
+    check_order<SEGTOPK_KEY_U16>(k16, "u16");
+    check_order<SEGTOPK_KEY_I16>(k16, "i16");
     {
         // 32-bit keys: the boundary patterns, every pattern next to a power of
         // two, and a million seeded random ones.
@@ -221,6 +227,8 @@ int main(int argc, char **argv) {
     run<SEGTOPK_KEY_F32>(k32, "f32");
     run<SEGTOPK_KEY_U32>(k32, "u32");
     run<SEGTOPK_KEY_I32>(k32, "i32");
+    run<SEGTOPK_KEY_U16>(k16, "u16");
+    run<SEGTOPK_KEY_I16>(k16, "i16");
     std::printf("total mismatches: %ld\n", g_bad);
     return g_bad != 0;
 }

@@ -1,0 +1,178 @@
+"""GPU-vs-oracle parity for the extended call (batched_topk_ex): per-segment k,
+the segment-size hint, 8-byte payloads, 16-bit integer keys, and batches of
+fewer than eight segments, whose workgroups spread over the whole device.
+
+Rows are compared as in tests/parity.py (bitwise in the deterministic modes,
+key multiset plus validity in not_guaranteed, untouched slots past k_i).
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from parity import check, check_all_rows
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+MODES = [("not_guaranteed", "unspecified"), ("run_to_run", "unspecified"),
+         ("gpu_to_gpu", "unspecified"), ("gpu_to_gpu", "prefer_smaller_index"),
+         ("gpu_to_gpu", "prefer_larger_index")]
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def rand_keys(total, key_type, gen, levels=None):
+    if key_type in ("f32", "bf16", "f16"):
+        if levels:
+            x = torch.randint(-levels, levels, (total,), generator=gen, device=DEV).float() / 4
+        else:
+            x = torch.randn(total, generator=gen, device=DEV) * 3
+        return x.to({"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[key_type])
+    if key_type in ("u16", "i16"):
+        lo, hi = (-(2 ** 15), 2 ** 15) if not levels else (-levels, levels)
+        return torch.randint(lo, hi, (total,), generator=gen, device=DEV,
+                             dtype=torch.int32).to(torch.int16)
+    lo, hi = (-(2 ** 31), 2 ** 31) if not levels else (-levels, levels)
+    return torch.randint(lo, hi, (total,), generator=gen, device=DEV,
+                         dtype=torch.int64).to(torch.int32)
+
+
+def offsets_from(sizes, start=0):
+    off = [start]
+    for s_ in sizes:
+        off.append(off[-1] + int(s_))
+    return torch.tensor(off, dtype=torch.int64, device=DEV), max(off) + 3
+
+
+# Plans: many segments (one workgroup each), a few hundred (one workgroup each,
+# largest first), a few dozen long ones (several workgroups each).
+PLANS = {
+    "many": lambda rng: rng.choice([0, 1, 5, 64, 300, 1000, 4096, 5000, 20000], size=2100),
+    "ordered": lambda rng: rng.integers(0, 30000, 300),
+    "sliced": lambda rng: np.concatenate([rng.integers(100000, 400000, 12), [0, 7, 50, 2000]]),
+}
+
+
+@pytest.mark.parametrize("plan", list(PLANS))
+@pytest.mark.parametrize("key_type", ["f32", "bf16"])
+def test_per_segment_k(plan, key_type):
+    rng = np.random.default_rng(101)
+    sizes = PLANS[plan](rng)
+    off, total = offsets_from(sizes, 3)
+    S = len(sizes)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(202)
+    vals = torch.arange(total, dtype=torch.int32, device=DEV)
+    k = 300
+    kseg = rng.integers(-5, k + 50, S).astype(np.int32)
+    kseg[:6] = [0, 1, k, k + 7, 2 ** 31 - 1, -2 ** 31]
+    kseg_t = torch.from_numpy(kseg).to(DEV)
+    say(f"[per-segment k {plan} {key_type}] segments={S} keys={total}")
+    for levels in (None, 6):
+        keys = rand_keys(total, key_type, g, levels)
+        for largest in (True, False):
+            for det, tb in (MODES if levels else [MODES[0], MODES[3]]):
+                for ordering in ("unsorted", "stable_sorted"):
+                    check(keys, vals, off, k, key_type, largest, det, tb, ordering,
+                          values_are="position", k_per_segment=kseg_t)
+
+
+@pytest.mark.parametrize("hint_kind", ["exact", "too_small", "huge"])
+def test_max_segment_size_hint(hint_kind):
+    """The hint only steers the plan: results are the same when it is exact,
+    when a segment exceeds it, and when it is far too large."""
+    rng = np.random.default_rng(7)
+    cases = [
+        (rng.integers(100, 4000, 64), 33),        # small segments, few
+        (rng.integers(1000, 8000, 700), 100),     # small segments, a few hundred
+        (rng.integers(50000, 300000, 10), 500),   # long segments, few
+    ]
+    g = torch.Generator(device=DEV)
+    g.manual_seed(8)
+    for sizes, k in cases:
+        off, total = offsets_from(sizes)
+        keys = rand_keys(total, "f32", g, 40)
+        vals = torch.arange(total, dtype=torch.int32, device=DEV)
+        mx = int(sizes.max())
+        hint = {"exact": mx, "too_small": max(1, mx // 5), "huge": 2 ** 40}[hint_kind]
+        say(f"[hint {hint_kind}] segments={len(sizes)} max={mx} hint={hint} k={k}")
+        for largest in (True, False):
+            for det, tb in (MODES[0], MODES[4]):
+                check(keys, vals, off, k, "f32", largest, det, tb, "stable_sorted",
+                      values_are="position", max_segment_size=hint)
+                check(keys, vals, off, k, "f32", largest, det, tb, "unsorted",
+                      values_are="position", max_segment_size=hint)
+
+
+@pytest.mark.parametrize("plan", list(PLANS))
+def test_eight_byte_values(plan):
+    rng = np.random.default_rng(55)
+    sizes = PLANS[plan](rng)
+    off, total = offsets_from(sizes, 1)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(56)
+    keys = rand_keys(total, "f32", g, 9)
+    pos = torch.arange(total, dtype=torch.int64, device=DEV)
+    tagged = pos | (torch.randint(1, 2 ** 31, (total,), generator=g, device=DEV,
+                                  dtype=torch.int64) << 32)
+    kseg = torch.from_numpy(rng.integers(0, 80, len(sizes)).astype(np.int32)).to(DEV)
+    say(f"[8-byte values {plan}] segments={len(sizes)} keys={total}")
+    for largest in (True, False):
+        for det, tb in MODES[1:]:
+            for ordering in ("unsorted", "stable_sorted"):
+                check(keys, tagged, off, 64, "f32", largest, det, tb, ordering)
+                check(keys, tagged, off, 64, "f32", largest, det, tb, ordering,
+                      k_per_segment=kseg)
+        # not_guaranteed checks each value against the key at that position.
+        check(keys, pos, off, 64, "f32", largest, "not_guaranteed", "unspecified", "unsorted",
+              values_are="position")
+
+
+@pytest.mark.parametrize("key_type", ["u16", "i16"])
+def test_sixteen_bit_integer_keys(key_type):
+    rng = np.random.default_rng(71)
+    sizes = [0, 1, 7, 33, 34, 100, 4095, 8192, 9000, 40000, -3, 70000, 5]
+    off, total = offsets_from(sizes, 5)
+    vals = torch.arange(total, dtype=torch.int32, device=DEV)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(72)
+    pool = np.array([0, 1, 2, 0x7FFF, 0x8000, 0x8001, 0xFFFE, 0xFFFF], dtype=np.uint16)
+    extreme = torch.from_numpy(rng.choice(pool, total).view(np.int16).copy()).to(DEV)
+    for keys in (rand_keys(total, key_type, g), rand_keys(total, key_type, g, 5), extreme):
+        for largest in (True, False):
+            for det, tb in MODES:
+                for ordering in ("unsorted", "stable_sorted"):
+                    check(keys, vals, off, 33, key_type, largest, det, tb, ordering,
+                          values_are="position")
+    # many segments (one workgroup each) and a few long ones (several each)
+    for sizes in (rng.integers(0, 9000, 2500), rng.integers(100000, 300000, 5)):
+        off, total = offsets_from(sizes)
+        keys = rand_keys(total, key_type, g, 300)
+        vals = torch.arange(total, dtype=torch.int32, device=DEV)
+        for det, tb in (MODES[0], MODES[4]):
+            check(keys, vals, off, 200, key_type, True, det, tb, "unsorted",
+                  values_are="position")
+
+
+@pytest.mark.parametrize("S", [1, 2, 5, 7])
+def test_few_segments_spread_over_the_device(S):
+    """Fewer than eight segments: each segment's workgroups are dealt over
+    every XCD and merge through device-wide atomics."""
+    g = torch.Generator(device=DEV)
+    g.manual_seed(300 + S)
+    n = (1 << 24) // S
+    keys = torch.randn(S * n, generator=g, device=DEV) * 10
+    off = torch.arange(S + 1, dtype=torch.int64, device=DEV) * n
+    vals = torch.arange(n, dtype=torch.int32, device=DEV).repeat(S)
+    for det, tb in (MODES[0], MODES[3], MODES[4]):
+        say(f"[spread S={S}] n={n} {det}/{tb}")
+        check_all_rows(keys, vals, off, 2048, "f32", True, det, tb, "unsorted", chunk_rows=8)
+    # heavy ties: quantised keys
+    q = (torch.randint(0, 50, (S * n,), generator=g, device=DEV).float())
+    for det, tb in (MODES[0], MODES[4]):
+        check_all_rows(q, vals, off, 1000, "f32", False, det, tb, "unsorted", chunk_rows=8)

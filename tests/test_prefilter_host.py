@@ -35,7 +35,7 @@ def test_raw_bit_bound_test_is_exact(tmp_path):
     print(r.stdout)
     assert r.returncode == 0, r.stdout
     assert "total mismatches: 0" in r.stdout
-    assert r.stdout.count("ordered bits vs numeric order") == 5
+    assert r.stdout.count("ordered bits vs numeric order") == 7
     p = subprocess.run([str(exe), "--perturbed"], capture_output=True, text=True, timeout=300)
     print(p.stdout)
-    assert p.returncode == 0 and "caught for 5 of 5" in p.stdout, p.stdout
+    assert p.returncode == 0 and "caught for 7 of 7" in p.stdout, p.stdout
