@@ -34,6 +34,9 @@ extern "C" {
 #define SEGTOPK_INVALID_ARGUMENT 1 /* bad pointer, enum, pairing or size      */
 #define SEGTOPK_NOT_SUPPORTED 2    /* valid request this build does not serve */
 #define SEGTOPK_HIP_ERROR 3        /* a HIP runtime call or launch failed     */
+#define SEGTOPK_SCRATCH_TOO_SMALL 4 /* batched_topk_ex_noalloc: the request's
+                                       plan needs more scratch than
+                                       SEGTOPK_STATIC_SCRATCH_BYTES          */
 
 /* ---- key types ------------------------------------------------------- */
 /* Keys are compared by numeric value.  Floating-point keys: -0.0 and +0.0
@@ -206,6 +209,38 @@ int batched_topk_ex(const segtopk_keys *keys, const segtopk_values *values, int3
                     const int64_t *segment_offsets, int64_t num_segments, int64_t k,
                     const int32_t *k_per_segment, int64_t max_segment_size, int direction,
                     int determinism, int tie_break, int ordering, hipStream_t stream);
+
+/*
+ * batched_topk_ex_noalloc -- batched_topk_ex that allocates nothing.
+ *
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * arguments, results and errors are batched_topk_ex's.  Instead of a
+ * per-stream buffer from a memory pool, the scratch that plans for fewer than
+ * 2048 segments use (the segment processing order; the per-segment histograms,
+ * tickets and candidate slots when segments are split over workgroups) lives
+ * in one file-scope device array of SEGTOPK_STATIC_SCRATCH_BYTES, which every
+ * GPU the library runs on holds until the process ends.  The call makes no
+ * hipMalloc / hipFree / pool call and no allocating library call; it queues
+ * only kernels (a small fill kernel clears the words that must start at zero,
+ * on every call that uses the array), so it may be captured into a graph.
+ *
+ * All calls on one device share that device's array and it keeps the last
+ * call's contents: calls that can overlap on one device (on different
+ * streams, or replays of graphs holding such calls) race and must be ordered
+ * by the caller.  A request whose plan needs more than
+ * SEGTOPK_STATIC_SCRATCH_BYTES returns SEGTOPK_SCRATCH_TOO_SMALL and queues
+ * nothing (for instance six segments with k = 4096, unsorted: about 37 MiB
+ * of per-workgroup candidate slots; a max_segment_size hint that rules out
+ * splitting avoids the scratch).  32 x 4 Mi keys with k = 2048 (30.5 MiB) or
+ * one segment with k = 2048 (30 MiB) fit.
+ */
+#define SEGTOPK_STATIC_SCRATCH_BYTES (32u << 20)
+int batched_topk_ex_noalloc(const segtopk_keys *keys, const segtopk_values *values,
+                            int32_t value_bytes, const int64_t *segment_offsets,
+                            int64_t num_segments, int64_t k, const int32_t *k_per_segment,
+                            int64_t max_segment_size, int direction, int determinism,
+                            int tie_break, int ordering, hipStream_t stream);
 
 /* Human-readable name of a status code (static storage). */
 const char *segtopk_status_string(int status);

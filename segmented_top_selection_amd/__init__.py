@@ -26,7 +26,8 @@ DIRECTIONS = {"max": 0, "min": 1}
 DETERMINISM = {"not_guaranteed": 0, "run_to_run": 1, "gpu_to_gpu": 2}
 TIE_BREAK = {"unspecified": 0, "prefer_smaller_index": 1, "prefer_larger_index": 2}
 ORDERING = {"unsorted": 0, "sorted": 1, "stable_sorted": 2}
-STATUS = {0: "ok", 1: "invalid argument", 2: "not supported", 3: "HIP error"}
+STATUS = {0: "ok", 1: "invalid argument", 2: "not supported", 3: "HIP error",
+          4: "scratch too small"}
 MAX_SORTED_K = 4096
 
 _DTYPE_KEY = {torch.float32: "f32", torch.bfloat16: "bf16", torch.float16: "f16",
@@ -73,6 +74,8 @@ def library() -> ctypes.CDLL:
             ctypes.POINTER(_Keys), ctypes.POINTER(_Values), ctypes.c_int32, ctypes.c_void_p,
             ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
             ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+        lib.batched_topk_ex_noalloc.restype = ctypes.c_int
+        lib.batched_topk_ex_noalloc.argtypes = lib.batched_topk_ex.argtypes
         lib.segtopk_status_string.restype = ctypes.c_char_p
         lib.segtopk_status_string.argtypes = [ctypes.c_int]
         lib.segtopk_version.restype = ctypes.c_int
@@ -109,6 +112,18 @@ def raw_call_ex(keys_in, keys_out, key_type, values_in, values_out, value_bytes,
                                      value_bytes, offsets, num_segments, k, k_per_segment,
                                      max_segment_size, direction, determinism, tie_break,
                                      ordering, stream)
+
+
+def raw_call_ex_noalloc(keys_in, keys_out, key_type, values_in, values_out, value_bytes,
+                        offsets, num_segments, k, k_per_segment, max_segment_size, direction,
+                        determinism, tie_break, ordering, stream=None) -> int:
+    """Calls batched_topk_ex_noalloc (static scratch, no allocation)."""
+    kd = _Keys(keys_in, keys_out, key_type)
+    vd = _Values(values_in, values_out)
+    return library().batched_topk_ex_noalloc(
+        ctypes.byref(kd), ctypes.byref(vd) if values_in else None, value_bytes, offsets,
+        num_segments, k, k_per_segment, max_segment_size, direction, determinism, tie_break,
+        ordering, stream)
 
 
 def _device_tensor(name, t, device):

@@ -530,6 +530,53 @@ int run(const Request &r) {
     return err == hipSuccess ? SEGTOPK_OK : SEGTOPK_HIP_ERROR;
 }
 
+// ---------------------------------------------------------------------------
+// Scratch without allocation: one file-scope device array.  The library never
+// passes the array's name to a kernel or a copy (in host code it is a
+// host-side stand-in, not a device address); it takes each device's address
+// of it once, with hipGetSymbolAddress, and uses that.  Every call on a device
+// shares the array, so calls that overlap on one device race.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[SEGTOPK_STATIC_SCRATCH_BYTES];
+
+std::mutex g_static_mu;
+void *g_static_ptr[64];
+
+hipError_t static_scratch(int dev, void **out) {
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lk(g_static_mu);
+    if (!g_static_ptr[dev]) {
+        void *ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!ptr) return hipErrorInvalidSymbol;
+        g_static_ptr[dev] = ptr;
+    }
+    *out = g_static_ptr[dev];
+    return hipSuccess;
+}
+
+int run_noalloc(const Request &r) {
+    const int v = validate(r);
+    if (v >= 0) return v;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return SEGTOPK_HIP_ERROR;
+    Plan pl;
+    const int ps = make_plan(r, dev, pl);
+    if (ps != SEGTOPK_OK) return ps;
+    if (pl.scratch_bytes > (size_t)SEGTOPK_STATIC_SCRATCH_BYTES) return SEGTOPK_SCRATCH_TOO_SMALL;
+    bool clear = false;
+    if (pl.scratch_bytes) {
+        void *ptr = nullptr;
+        if (static_scratch(dev, &ptr) != hipSuccess) return SEGTOPK_HIP_ERROR;
+        bind_scratch(pl, ptr);
+        // The array keeps whatever the last call left: clear the words that
+        // must start at zero every time.
+        clear = pl.sliced;
+    }
+    return queue(r, pl, clear, r.stream) == hipSuccess ? SEGTOPK_OK : SEGTOPK_HIP_ERROR;
+}
+
 }  // namespace
 
 extern "C" int batched_topk(const segtopk_keys *keys, const segtopk_values *values,
@@ -551,12 +598,24 @@ extern "C" int batched_topk_ex(const segtopk_keys *keys, const segtopk_values *v
     return run(r);
 }
 
+extern "C" int batched_topk_ex_noalloc(const segtopk_keys *keys, const segtopk_values *values,
+                                       int32_t value_bytes, const int64_t *segment_offsets,
+                                       int64_t num_segments, int64_t k,
+                                       const int32_t *k_per_segment, int64_t max_segment_size,
+                                       int direction, int determinism, int tie_break,
+                                       int ordering, hipStream_t stream) {
+    const Request r{keys, values, value_bytes, segment_offsets, num_segments, k, k_per_segment,
+                    max_segment_size, direction, determinism, tie_break, ordering, stream};
+    return run_noalloc(r);
+}
+
 extern "C" const char *segtopk_status_string(int status) {
     switch (status) {
     case SEGTOPK_OK: return "ok";
     case SEGTOPK_INVALID_ARGUMENT: return "invalid argument";
     case SEGTOPK_NOT_SUPPORTED: return "not supported";
     case SEGTOPK_HIP_ERROR: return "HIP error";
+    case SEGTOPK_SCRATCH_TOO_SMALL: return "request needs more scratch than the static buffer holds";
     default: return "unknown status";
     }
 }
