@@ -34,14 +34,29 @@ def log(*a):
 
 
 def cpu_model():
+    """CPU model name from /proc/cpuinfo (plus family/model numbers when the
+    name is generic), read on the machine the benchmark runs on."""
+    info = {}
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                if ":" in line:
+                    k, v = line.split(":", 1)
+                    info.setdefault(k.strip(), v.strip())
     except OSError:
         pass
-    return platform.processor()
+    name = info.get("model name") or platform.processor() or "unknown"
+    if "cpu family" in info and "model" in info:
+        name += f" (family {info['cpu family']}, model {info['model']})"
+    return name
+
+
+def host_cpus():
+    """CPUs this process may run on (its affinity mask)."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        return os.cpu_count() or 1
 
 
 def workload_sizes(off_np, k):
@@ -142,6 +157,51 @@ def copy_probe(mib=256, reps=5):
     log(f"copy probe: {reps} copies of {mib} MiB")
 
 
+PROBE_LIB = os.path.join(ROOT, "segmented_top_selection_amd", "probe", "libsegtopk_probe.so")
+
+
+def stream_read_probe(gib=2, reps=10):
+    """GB/s of a plain streaming read (16-byte non-temporal loads, the load the
+    top-k kernels stream their keys with) of a `gib` GiB buffer, far beyond
+    the Infinity Cache: best over a few grid sizes of the median of `reps`
+    timed launches.  The reference point for each workload's probe_frac."""
+    import ctypes
+
+    import numpy as np
+    import torch
+    lib = ctypes.CDLL(PROBE_LIB)
+    lib.segtopk_probe_stream_read.restype = ctypes.c_int
+    lib.segtopk_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint32,
+                                              ctypes.c_void_p, ctypes.c_void_p]
+    nbytes = gib << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    buf.fill_(3)
+    stream = torch.cuda.current_stream()
+    best = None
+    for wgs in (768, 2048, 4096):
+        sink = torch.empty(wgs * 256, dtype=torch.int32, device="cuda")
+        times = []
+        for r in range(reps + 2):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            rc = lib.segtopk_probe_stream_read(buf.data_ptr(), nbytes, wgs, sink.data_ptr(),
+                                               stream.cuda_stream)
+            b.record(stream)
+            if rc != 0:
+                raise RuntimeError(f"stream-read probe failed: {rc}")
+            torch.cuda.synchronize()
+            if r >= 2:
+                times.append(a.elapsed_time(b))
+        gbs = nbytes / (float(np.median(times)) / 1e3) / 1e9
+        log(f"stream-read probe: {gib} GiB, {wgs} workgroups: {gbs:.0f} GB/s")
+        if best is None or gbs > best["gbs"]:
+            best = dict(gbs=gbs, workgroups=wgs, gib=gib, median_ms=float(np.median(times)))
+        del sink
+    del buf
+    torch.cuda.empty_cache()
+    return best
+
+
 KERNEL_SRC_DIR = os.path.join(ROOT, "segmented_top_selection_amd", "csrc")
 
 
@@ -212,11 +272,12 @@ def traffic_from(fetch_csv, write_csv, name):
     print(json.dumps(out))
 
 
-def cpu_baseline(name, budget_s=2.0):
-    """The oracle, as it stands, on a bounded sample of the workload's segments
-    (whole segments, taken from the start), on all host cores.  The sample
-    grows to the whole workload and is then repeated until about `budget_s`
-    seconds of wall time (times the core count of CPU work) have run."""
+def cpu_baseline(name, budget_s=2.0, max_sample_keys=1 << 23):
+    """The oracle, as it stands, on a bounded sample of the workload (whole
+    segments taken from the start; a single segment longer than
+    `max_sample_keys` is cut to its first `max_sample_keys` keys, taken as one
+    segment), on the host cores.  The sample grows until one run takes about a
+    quarter of `budget_s`, then runs are repeated for about `budget_s`."""
     import numpy as np
     import torch
 
@@ -228,16 +289,19 @@ def cpu_baseline(name, budget_s=2.0):
     keys, vals, off = w["gen"](device="cuda", **args)
     s = off.numel() - 1
     threads = oracle.default_threads()
-    # Grow the sample until it takes about `budget_s` seconds.
+    off_h = off.cpu().numpy()
     rows = min(s, 64)
     while True:
-        b, e = int(off[0]), int(off[rows])
+        b, e = int(off_h[0]), int(off_h[rows])
+        cut = False
+        if rows == 1 and e - b > max_sample_keys:
+            e, cut = b + max_sample_keys, True
         kb = keys[b:e].cpu()
         kb = kb.view(torch.int16).numpy().view(np.uint16) if kb.element_size() == 2 else \
             kb.view(torch.int32).numpy().view(np.uint32)
         kb = kb.view(np.float32) if w["key_type"] == "f32" else kb
         vb = vals[b:e].cpu().numpy().view(np.uint32) if w["pairs"] else None
-        o = off[:rows + 1].cpu().numpy() - b
+        o = np.array([0, e - b], np.int64) if cut else off_h[:rows + 1] - b
 
         def run():
             t0 = time.perf_counter()
@@ -255,10 +319,28 @@ def cpu_baseline(name, budget_s=2.0):
         times.append(run())
     t = float(np.median(times))
     n = int(o[-1])
-    return dict(value=n / t, unit="keys/s", cores=threads, kind="oracle",
-                sample=f"{rows} of {s} segments ({n} keys) of {name}, median of "
-                       f"{len(times)} runs, {t:.3f} s each",
-                cpu=cpu_model())
+    used = min(threads, rows)  # the oracle's threads work on whole segments
+    what = (f"the first {n} keys of segment 0 of {name}, as one segment" if cut else
+            f"{rows} of {s} segments ({n} keys) of {name}")
+    del keys, vals, off
+    torch.cuda.empty_cache()
+    return dict(value=n / t, unit="keys/s", cores=used, kind="oracle",
+                sample=f"{what}, median of {len(times)} runs, {t:.3f} s each",
+                threads_requested=threads, host_cpus=host_cpus(), cpu=cpu_model())
+
+
+def combined_pair(others):
+    """The two 32 x 4 Mi calls (uint32 and float32 halves) as one 64 x 4 Mi
+    workload: keys over the summed step times."""
+    a, b = others.get("uniform_u32_32x4Mi_k2048"), others.get("normal10_f32_32x4Mi_k2048")
+    if not a or not b:
+        return None
+    t = (a["ms_per_step"] + b["ms_per_step"]) / 1e3
+    alg = a["bytes_alg"] + b["bytes_alg"]
+    roof = a["bytes_roof"] + b["bytes_roof"]
+    return dict(keys_per_s=(a["keys"] + b["keys"]) / t, ms_per_step=t * 1e3,
+                alg_gbs=alg / t / 1e9, alg_frac=alg / t / 1e9 / HBM_PEAK_GBS,
+                hbm_roof_frac=roof / (HBM_PEAK_GBS * 1e9) / t)
 
 
 def main():
@@ -269,6 +351,7 @@ def main():
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--only-headline", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-probe", action="store_true", help="skip the stream-read probe")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a 256 MiB device copy (counter calibration)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -292,7 +375,10 @@ def main():
 
     if a.copy_probe:
         copy_probe()
+    probe = None if a.no_probe else stream_read_probe()
     head = measure(a.workload, a.steps, a.warmup)
+    if probe:
+        head["probe_frac"] = head["alg_gbs"] / probe["gbs"]
     log("headline", json.dumps(head))
     others = {}
     if not a.only_headline:
@@ -300,8 +386,14 @@ def main():
             if name == a.workload:
                 continue
             others[name] = measure(name, max(5, a.steps // 2), 2)
+            if probe:
+                others[name]["probe_frac"] = others[name]["alg_gbs"] / probe["gbs"]
             log(name, json.dumps(others[name]))
     cpu = None if a.no_cpu_baseline else cpu_baseline(a.workload)
+    if not a.no_cpu_baseline and not a.only_headline:
+        for name in others:
+            others[name]["cpu_baseline"] = cpu_baseline(name)
+            log(name, "cpu_baseline", json.dumps(others[name]["cpu_baseline"]))
 
     # The headline plan is one kernel launch per call, so the average over
     # the K back-to-back calls is that kernel's launch duration (an event pair
@@ -331,10 +423,14 @@ def main():
                      "launch_us": kernel_ms * 1e3,
                      "launch_us_event_pair": head["launch_ms_mean"] * 1e3,
                      "bytes_per_launch": head["bytes_alg"],
-                     "traffic": measured_traffic(a.workload)},
+                     "traffic": measured_traffic(a.workload),
+                     "probe_gbs": probe["gbs"] if probe else None,
+                     "probe_frac": head.get("probe_frac")},
+        "stream_read_probe": probe,
         "cpu_baseline": cpu,
         "workloads": {n: {kk: (round(v, 6) if isinstance(v, float) else v)
                           for kk, v in r.items()} for n, r in others.items()},
+        "combined_32x4Mi_pair": combined_pair(others),
     }
     print(json.dumps(line), flush=True)
 

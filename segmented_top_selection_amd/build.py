@@ -2,7 +2,9 @@
 
 Every source under csrc/ (the host code and one kernel unit per key type) is
 compiled to an object in parallel, then the objects are linked into one
-shared library.  Objects go to a build folder beside the sources.
+shared library.  Objects go to a build folder beside the sources.  The
+benchmark's stream-read probe (probe/stream_read.hip) is built alongside as
+libsegtopk_probe.so; the top-k library does not use it.
 """
 from __future__ import annotations
 
@@ -16,6 +18,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OBJ_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsegtopk.so")
+PROBE_SRC = os.path.join(HERE, "probe", "stream_read.hip")
+PROBE_LIB = os.path.join(HERE, "probe", "libsegtopk_probe.so")
 ARCH = os.environ.get("SEGTOPK_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [
@@ -37,6 +41,8 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
     srcs = sources()
     objs = [os.path.join(OBJ_DIR, os.path.basename(s)[:-4] + ".o") for s in srcs]
     cmds = [[hipcc, *HIPCC_FLAGS, "-c", s, "-o", o] for s, o in zip(srcs, objs)]
+    # The benchmark's stream-read probe: a library of its own.
+    cmds.append([hipcc, *HIPCC_FLAGS, "-shared", PROBE_SRC, "-o", PROBE_LIB])
     if verbose:
         for c in cmds:
             print(" ".join(c), flush=True)

@@ -1479,19 +1479,37 @@ struct alignas(16) Shared {
     uint32_t kb, kbefore, kcount, pad;            // the k-th bucket found by wave 0 (same)
 };
 
+// The splitter bits resolved before a finish starts: `hi` low bits are still
+// open; the resolved high bits of the k-th key are kpref under kmask.
+struct Prefix {
+    int hi;
+    uint32_t kmask, kpref;
+};
+
+// The prefix after pass 0 (the k-th key's pass-0 bucket b).
+template <int KT, bool LARGEST> __device__ __forceinline__ Prefix pass0_prefix(uint32_t b) {
+    constexpr int hi = Key<KT>::kBits - kDigit;
+    Prefix f;
+    f.hi = hi;
+    f.kmask = (uint32_t)(kBuckets - 1) << hi;
+    f.kpref = (LARGEST ? (uint32_t)(kBuckets - 1) - b : b) << hi;
+    return f;
+}
+
 // Passes 1.., the tie selection and the output by the four waves of the
-// workgroup together, over the LDS list list[0, count): in every visit each
-// wave takes a quarter of the list; the histograms and the output positions
-// are shared through LDS, with a workgroup barrier between the steps, and
-// every wave finds the same bucket in the shared histogram.  The result is
+// workgroup together, over the LDS list list[0, count) of keys that match the
+// resolved prefix pf0 (k0.before keys better than it come first in the
+// output; `placed` of them are written already): in every visit each wave
+// takes a quarter of the list; the histograms and the output positions are
+// shared through LDS, with a workgroup barrier between the steps, and every
+// wave finds the same bucket in the shared histogram.  The result is
 // wave_finish's: in the deterministic modes exactly the required ties pass
 // the final test, so arrival order decides only positions, which sorted
 // output fixes afterwards.  Called by all four waves.
 template <int KT, bool LARGEST>
 __device__ __forceinline__ void block_finish(Shared &sh, uint2 *outbuf, const Params &p,
                                              const Seg &sg, const uint2 *list, uint32_t count,
-                                             Kth k0, uint32_t placed) {
-    constexpr int KB = Key<KT>::kBits;
+                                             Kth k0, uint32_t placed, Prefix pf0) {
     const uint32_t t = threadIdx.x;
     const uint32_t w = t / kWave;
     const uint32_t ln = lane_id();
@@ -1508,9 +1526,9 @@ __device__ __forceinline__ void block_finish(Shared &sh, uint2 *outbuf, const Pa
         }
     };
 
-    int hi = KB - kDigit;
-    uint32_t kmask = (uint32_t)(kBuckets - 1) << hi;
-    uint32_t kpref = (LARGEST ? (uint32_t)(kBuckets - 1) - k0.b : k0.b) << hi;
+    int hi = pf0.hi;
+    uint32_t kmask = pf0.kmask;
+    uint32_t kpref = pf0.kpref;
     uint32_t krem = sg.k_i - k0.before;
     uint32_t front = k0.before;
     bool done = (k0.count == krem);
@@ -1611,6 +1629,15 @@ __device__ __forceinline__ void block_finish(Shared &sh, uint2 *outbuf, const Pa
     }
 }
 
+// block_finish right after pass 0.
+template <int KT, bool LARGEST>
+__device__ __forceinline__ void block_finish(Shared &sh, uint2 *outbuf, const Params &p,
+                                             const Seg &sg, const uint2 *list, uint32_t count,
+                                             Kth k0, uint32_t placed) {
+    block_finish<KT, LARGEST>(sh, outbuf, p, sg, list, count, k0, placed,
+                              pass0_prefix<KT, LARGEST>(k0.b));
+}
+
 // The last workgroup of a segment to finish pass 0, all four waves: the
 // segment's exact k-th bucket b* from the merged histogram, then every slot's
 // entries up to b* (a prefix, as the slots are sorted by bucket): those of
@@ -1682,32 +1709,87 @@ __device__ __forceinline__ void slice_last(Shared &sh, uint2 *stash, uint2 *outb
     }
     __syncthreads();
     const uint32_t total = sh.total;
-    const bool fast = sh.any_bad == 0 && ks.count <= p.stash_cap;
-    if (fast) {
-        // Batches of 8 entries per lane, spread over the waves; positions
-        // come from LDS counters, one reservation per batch and kind.
-        constexpr int kB = 8;
+    bool fast = sh.any_bad == 0 && ks.count <= p.stash_cap;
+
+    // Entries [base + u * 64 + lane] of the slots' prefixes laid end to end,
+    // 8 per lane, spread over the waves by the caller.
+    constexpr int kB = 8;
+    auto load_batch = [&](uint32_t base, uint2 (&e)[kB]) {
+#pragma unroll
+        for (int u = 0; u < kB; ++u) {
+            const uint32_t j = base + (uint32_t)u * kWave + ln;
+            e[u] = make_uint2(0u, kNone);
+            if (j < total) {
+                uint32_t a = 0, z = ps;  // pre[a] <= j < pre[z]
+                while (z - a > 1) {
+                    const uint32_t m = (a + z) >> 1;
+                    if (pre[m] <= j) a = m; else z = m;
+                }
+                e[u] = slot_data[(size_t)a * p.stash_cap + (j - pre[a])];
+            }
+        }
+    };
+    // Rank of the key's next digit below the pass-0 digit (best first).
+    constexpr int kSubW = (Key<KT>::kBits - kDigit) < kLaterDigit ? (Key<KT>::kBits - kDigit)
+                                                                    : kLaterDigit;
+    constexpr int kSubSh = Key<KT>::kBits - kDigit - kSubW;
+    constexpr uint32_t kSubN = 1u << kSubW;
+    auto sub_rank = [](uint32_t raw) {
+        const uint32_t d = (Key<KT>::ord(raw) >> kSubSh) & (kSubN - 1u);
+        return LARGEST ? kSubN - 1u - d : d;
+    };
+
+    // Bucket b* holds more keys than the LDS list: one more digit of its keys,
+    // counted from the slots by the four waves, narrows it (the better
+    // sub-buckets' keys become winners).  The count lives above the slot
+    // prefix table, which takes at most kMaxWgPerSeg + 1 words.
+    bool refine = false;
+    uint32_t dstar = 0, front = ks.before;
+    Kth kf = ks;
+    Prefix pf0 = pass0_prefix<KT, LARGEST>(ks.b);
+    if (!fast && sh.any_bad == 0) {
+        uint32_t *sub = sh.hist + kBuckets - kSubN;
+        for (uint32_t i = threadIdx.x; i < kSubN; i += kThreads) sub[i] = 0u;
+        __syncthreads();
         for (uint32_t base = w * kB * kWave; base < total; base += kWaves * kB * kWave) {
             uint2 e[kB];
+            load_batch(base, e);
+#pragma unroll
+            for (int u = 0; u < kB; ++u)
+                if (e[u].y != kNone && rank0<KT, LARGEST>(Key<KT>::ord(e[u].x)) == ks.b)
+                    atomicAdd(&sub[sub_rank(e[u].x)], 1u);
+        }
+        __syncthreads();
+        const Kth f2 = wave_find(sub, kSubN, sg.k_i - ks.before);  // alike in every wave
+        if (f2.found && f2.count <= p.stash_cap) {
+            refine = true;
+            dstar = f2.b;
+            front = ks.before + f2.before;
+            kf.before = front;
+            kf.count = f2.count;
+            pf0.hi = kSubSh;
+            pf0.kmask |= (kSubN - 1u) << kSubSh;
+            pf0.kpref |= (LARGEST ? kSubN - 1u - dstar : dstar) << kSubSh;
+        }
+        __syncthreads();
+    }
+    if (fast || refine) {
+        // Batches of 8 entries per lane, spread over the waves; positions
+        // come from LDS counters, one reservation per batch and kind.
+        for (uint32_t base = w * kB * kWave; base < total; base += kWaves * kB * kWave) {
+            uint2 e[kB];
+            load_batch(base, e);
+            uint32_t nb = 0, nt = 0;
+            bool bet[kB], tie[kB];
 #pragma unroll
             for (int u = 0; u < kB; ++u) {
-                const uint32_t j = base + (uint32_t)u * kWave + ln;
-                e[u] = make_uint2(0u, kNone);
-                if (j < total) {
-                    uint32_t a = 0, z = ps;  // pre[a] <= j < pre[z]
-                    while (z - a > 1) {
-                        const uint32_t m = (a + z) >> 1;
-                        if (pre[m] <= j) a = m; else z = m;
-                    }
-                    e[u] = slot_data[(size_t)a * p.stash_cap + (j - pre[a])];
-                }
-            }
-            uint32_t rk[kB], nb = 0, nt = 0;
-#pragma unroll
-            for (int u = 0; u < kB; ++u) {
-                rk[u] = e[u].y != kNone ? rank0<KT, LARGEST>(Key<KT>::ord(e[u].x)) : kNone;
-                nb += (uint32_t)__popcll(__ballot(rk[u] < ks.b));
-                nt += (uint32_t)__popcll(__ballot(rk[u] == ks.b));
+                const uint32_t rk =
+                    e[u].y != kNone ? rank0<KT, LARGEST>(Key<KT>::ord(e[u].x)) : kNone;
+                const uint32_t sr = refine ? sub_rank(e[u].x) : 0u;
+                bet[u] = rk < ks.b || (refine && rk == ks.b && sr < dstar);
+                tie[u] = rk == ks.b && (!refine || sr == dstar);
+                nb += (uint32_t)__popcll(__ballot(bet[u]));
+                nt += (uint32_t)__popcll(__ballot(tie[u]));
             }
             uint32_t fb = 0, tb = 0;
             if (ln == 0) {
@@ -1719,26 +1801,24 @@ __device__ __forceinline__ void slice_last(Shared &sh, uint2 *stash, uint2 *outb
             uint32_t fpos[kB];
 #pragma unroll
             for (int u = 0; u < kB; ++u) {
-                const bool better = rk[u] < ks.b;
-                const bool tie = rk[u] == ks.b;
-                const uint64_t mb = __ballot(better);
-                const uint64_t mt = __ballot(tie);
+                const uint64_t mb = __ballot(bet[u]);
+                const uint64_t mt = __ballot(tie[u]);
                 const uint32_t pb = fb + lanes_below(mb);
                 const uint32_t pt = tb + lanes_below(mt);
                 fb += (uint32_t)__popcll(mb);
                 tb += (uint32_t)__popcll(mt);
-                fpos[u] = (better && pb < ks.before) ? pb : kNone;
+                fpos[u] = (bet[u] && pb < front) ? pb : kNone;
                 if (outbuf && fpos[u] != kNone) outbuf[pb] = e[u];
-                if (tie && pt < p.stash_cap) stash[pt] = e[u];
+                if (tie[u] && pt < p.stash_cap) stash[pt] = e[u];
             }
             if (!outbuf) write_batch<KT, kB>(p, sg, fpos, e);
         }
     }
     __syncthreads();
-    if (fast) {
-        // The four waves finish together on bucket b*'s list.
+    if (fast || refine) {
+        // The four waves finish together on the list of keys at the prefix.
         block_finish<KT, LARGEST>(sh, outbuf, p, sg, stash,
-                                  sh.ntie < p.stash_cap ? sh.ntie : p.stash_cap, ks, ks.before);
+                                  sh.ntie < p.stash_cap ? sh.ntie : p.stash_cap, kf, front, pf0);
         return;
     }
     if (w != 0) return;
@@ -1757,14 +1837,10 @@ __device__ __forceinline__ void slice_last(Shared &sh, uint2 *stash, uint2 *outb
     cand.bstar = ks.b;
     cand.lds = false;
     cand.count = 0;
-    uint32_t placed = 0;
-    if (fast) {
-        cand.lds = true;
-        cand.count = sh.ntie < p.stash_cap ? sh.ntie : p.stash_cap;
-        placed = ks.before;
-    } else {
-        // Rare: a slice lost candidates or bucket b* does not fit in LDS.
-        // Pull what fits into LDS, else leave the candidates in place.
+    {
+        // Rare: a slice lost candidates, or bucket b* does not fit in LDS
+        // even narrowed by one more digit (heavy ties).  Pull what fits into
+        // LDS, else leave the candidates in place.
         const Prefilter pf = prefilter<KT, LARGEST>(ks.b);
         const uint32_t cap = p.stash_cap;
         uint32_t got = 0;
@@ -1781,7 +1857,7 @@ __device__ __forceinline__ void slice_last(Shared &sh, uint2 *stash, uint2 *outb
             cand.count = got;
         }
     }
-    wave_finish<KT, LARGEST>(sh.hist, outbuf, p, sg, cand, ks, placed);
+    wave_finish<KT, LARGEST>(sh.hist, outbuf, p, sg, cand, ks, 0u);
 }
 
 // A segment of one chunk per wave (each wave's quarter [wlo, whi) fits one

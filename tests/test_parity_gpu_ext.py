@@ -176,3 +176,59 @@ def test_few_segments_spread_over_the_device(S):
     q = (torch.randint(0, 50, (S * n,), generator=g, device=DEV).float())
     for det, tb in (MODES[0], MODES[4]):
         check_all_rows(q, vals, off, 1000, "f32", False, det, tb, "unsorted", chunk_rows=8)
+
+
+def _closed_form_check(keys_np, got_idx, got_bits, k, largest, det, tb):
+    """One segment: the result set against the definition, computed with
+    numpy instead of a sort of the whole segment.  s = the k-th best value;
+    every key strictly better than s is selected, and k - #better keys equal
+    to s, the smallest (prefer_smaller / unspecified deterministic) or largest
+    (prefer_larger) indices among them; not_guaranteed: any of them."""
+    n = keys_np.shape[0]
+    vals = keys_np.astype(np.float64)
+    kth = np.partition(-vals if largest else vals, k - 1)[k - 1]
+    s = -kth if largest else kth
+    better = np.nonzero(vals > s if largest else vals < s)[0]
+    ties = np.nonzero(vals == s)[0]
+    m = k - better.size
+    assert 0 < m <= ties.size
+    assert got_idx.size == k and np.unique(got_idx).size == k
+    assert np.all(got_idx < n)
+    assert np.array_equal(got_bits, keys_np.view(np.uint32)[got_idx])
+    got = np.sort(got_idx)
+    chosen_ties = np.setdiff1d(got, better, assume_unique=True)
+    assert np.all(np.isin(better, got)), "a strictly better key is missing"
+    assert chosen_ties.size == m and np.all(vals[chosen_ties] == s)
+    if det != "not_guaranteed":
+        want = ties[:m] if tb != "prefer_larger_index" else ties[-m:]
+        assert np.array_equal(chosen_ties, want), "wrong ties chosen"
+
+
+@pytest.mark.parametrize("det,tb", [MODES[0], MODES[3], MODES[4]])
+def test_one_segment_of_2_28_keys(det, tb):
+    """One segment of 2^28 float32 keys over the whole device, k = 2048."""
+    n, k = 1 << 28, 2048
+    g = torch.Generator(device=DEV)
+    g.manual_seed(2028)
+    keys = torch.randn(n, generator=g, device=DEV) * 10
+    off = torch.tensor([0, n], dtype=torch.int64, device=DEV)
+    vals = torch.arange(n, dtype=torch.int32, device=DEV)
+    say(f"[one segment 2^28] {det}/{tb}")
+    out_k = torch.empty((1, k), dtype=torch.float32, device=DEV)
+    out_v = torch.empty((1, k), dtype=torch.int32, device=DEV)
+    import segmented_top_selection_amd as st
+    st.batched_topk(keys, off, k, values=vals, largest=True, determinism=det, tie_break=tb,
+                    ordering="unsorted", out_keys=out_k, out_values=out_v)
+    torch.cuda.synchronize()
+    kn = keys.cpu().numpy()
+    _closed_form_check(kn, out_v.cpu().numpy()[0].astype(np.int64),
+                       out_k.cpu().numpy()[0].view(np.uint32), k, True, det, tb)
+    # coarse keys: thousands of copies of the k-th value
+    q = torch.randint(0, 1 << 16, (n,), generator=g, device=DEV).float()
+    st.batched_topk(q, off, k, values=vals, largest=False, determinism=det, tie_break=tb,
+                    ordering="unsorted", out_keys=out_k, out_values=out_v)
+    torch.cuda.synchronize()
+    _closed_form_check(q.cpu().numpy(), out_v.cpu().numpy()[0].astype(np.int64),
+                       out_k.cpu().numpy()[0].view(np.uint32), k, False, det, tb)
+    del keys, vals, q
+    torch.cuda.empty_cache()

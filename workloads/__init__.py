@@ -20,6 +20,7 @@ Workloads (one call each; see the design doc for the reading of each description):
   uniform_u32   S x L full-range uniform uint32 keys, index values
   normal10_f32  S x L float32 keys ~ 10 * N(0, 1), index values
   logits_bf16   S x L bfloat16 keys rounded from 3 * N(0, 1), index values
+  (one segment of 2^28 float32 keys ~ 10 * N(0, 1): normal10_f32 with S = 1)
 """
 from __future__ import annotations
 
@@ -125,6 +126,10 @@ WORKLOADS = {
         gen=normal10_f32, args=dict(num_segments=32, seg_len=4194304, seed=1014),
         key_type="f32", k=2048, largest=True, determinism="gpu_to_gpu",
         tie_break="prefer_larger_index", ordering="unsorted", pairs=True),
+    "normal10_f32_1x256Mi_k2048": dict(
+        gen=normal10_f32, args=dict(num_segments=1, seg_len=1 << 28, seed=1024),
+        key_type="f32", k=2048, largest=True, determinism="gpu_to_gpu",
+        tie_break="prefer_smaller_index", ordering="unsorted", pairs=True),
     "logits_bf16_16384x128Ki_k50": dict(
         gen=logits_bf16, args=dict(num_segments=16384, seg_len=131072, seed=1005),
         key_type="bf16", k=50, largest=True, determinism="not_guaranteed",
