@@ -53,7 +53,10 @@ typedef enum segtopk_key_type {
     SEGTOPK_KEY_I32 = 3,  /* signed 32-bit integer                  */
     SEGTOPK_KEY_F16 = 4,  /* IEEE binary16                          */
     SEGTOPK_KEY_U16 = 5,  /* unsigned 16-bit integer                */
-    SEGTOPK_KEY_I16 = 6   /* signed 16-bit integer                  */
+    SEGTOPK_KEY_I16 = 6,  /* signed 16-bit integer                  */
+    SEGTOPK_KEY_U64 = 7,  /* unsigned 64-bit integer                */
+    SEGTOPK_KEY_I64 = 8,  /* signed 64-bit integer                  */
+    SEGTOPK_KEY_F64 = 9   /* IEEE binary64                          */
 } segtopk_key_type;
 
 /* ---- request --------------------------------------------------------- */

@@ -92,12 +92,17 @@ constexpr uint32_t kTargetWorkgroups = 2048;  // enough to fill 256 CUs several 
 constexpr uint32_t kMinSlice = 16384;
 constexpr int64_t kOrderMinSegments = 256;  // fewer segments: no processing order
 constexpr size_t kMaxCachedStreams = 16;    // scratch buffers kept (LRU beyond that)
+constexpr uint32_t kCand64Entries = 2048;   // LDS candidate list of the 64-bit-key kernel
+
+bool is_wide_key(int type) {
+    return type == SEGTOPK_KEY_U64 || type == SEGTOPK_KEY_I64 || type == SEGTOPK_KEY_F64;
+}
 
 int key_bytes(int type) {
-    return (type == SEGTOPK_KEY_BF16 || type == SEGTOPK_KEY_F16 || type == SEGTOPK_KEY_U16 ||
-            type == SEGTOPK_KEY_I16)
-               ? 2
-               : 4;
+    if (type == SEGTOPK_KEY_BF16 || type == SEGTOPK_KEY_F16 || type == SEGTOPK_KEY_U16 ||
+        type == SEGTOPK_KEY_I16)
+        return 2;
+    return is_wide_key(type) ? 8 : 4;
 }
 
 // Smallest power of two >= x, for 1 <= x <= 2^62.
@@ -269,6 +274,9 @@ uint32_t resident_wgs_for(int type, int dev, bool largest, size_t lds) {
 hipError_t launch(int type, const Params &p, bool largest, int variant, uint32_t grid, size_t lds,
                   hipStream_t st) {
     switch (type) {
+    case SEGTOPK_KEY_U64: return launch_topk64<SEGTOPK_KEY_U64>(p, largest, grid, lds, st);
+    case SEGTOPK_KEY_I64: return launch_topk64<SEGTOPK_KEY_I64>(p, largest, grid, lds, st);
+    case SEGTOPK_KEY_F64: return launch_topk64<SEGTOPK_KEY_F64>(p, largest, grid, lds, st);
     case SEGTOPK_KEY_F32: return launch_topk<SEGTOPK_KEY_F32>(p, largest, variant, grid, lds, st);
     case SEGTOPK_KEY_BF16: return launch_topk<SEGTOPK_KEY_BF16>(p, largest, variant, grid, lds, st);
     case SEGTOPK_KEY_U32: return launch_topk<SEGTOPK_KEY_U32>(p, largest, variant, grid, lds, st);
@@ -308,7 +316,7 @@ struct Plan {
 int validate(const Request &r) {
     if (!r.keys) return SEGTOPK_INVALID_ARGUMENT;
     const int type = r.keys->type;
-    if (type < SEGTOPK_KEY_F32 || type > SEGTOPK_KEY_I16) return SEGTOPK_INVALID_ARGUMENT;
+    if (type < SEGTOPK_KEY_F32 || type > SEGTOPK_KEY_F64) return SEGTOPK_INVALID_ARGUMENT;
     if (r.direction != SEGTOPK_MAX && r.direction != SEGTOPK_MIN) return SEGTOPK_INVALID_ARGUMENT;
     if (r.determinism < SEGTOPK_NOT_GUARANTEED || r.determinism > SEGTOPK_GPU_TO_GPU)
         return SEGTOPK_INVALID_ARGUMENT;
@@ -370,6 +378,26 @@ int make_plan(const Request &r, int dev, Plan &pl) {
     p.vindex = pl.wide_values ? 1u : 0u;
     p.vshift = pl.wide_values ? 1u : 0u;
 
+    if (is_wide_key(type)) {
+        // 64-bit keys: one workgroup per segment, no scratch; dynamic LDS
+        // holds the candidate list and the output staging (16 bytes an entry).
+        uint64_t oc = 0;
+        if (sorted || k <= 256) oc = next_pow2(k < 2 ? 2 : k);
+        p.out_cap = (uint32_t)oc;
+        p.stash_cap = kCand64Entries;
+        p.wg_per_seg = 1;
+        pl.lds = 16 * (size_t)(kCand64Entries + oc);
+        if (pl.lds > kMaxDynLds) return SEGTOPK_NOT_SUPPORTED;
+        pl.largest = r.direction == SEGTOPK_MAX;
+        pl.type = type;
+        pl.pairs = pairs;
+        pl.grid = (uint32_t)S;
+        pl.variant = kVariantOne;
+        pl.order = pl.sliced = false;
+        pl.scratch_bytes = pl.zero_words = pl.data_off = pl.n_hist = pl.info_words = 0;
+        return SEGTOPK_OK;
+    }
+
     // Output staging: sorted output is staged and sorted in LDS (k is at most
     // SEGTOPK_MAX_SORTED_K then); unsorted output only for small k (coalesced
     // row writes), else written in place.  Sized by k, never by the hint: a
@@ -390,11 +418,15 @@ int make_plan(const Request &r, int dev, Plan &pl) {
     if (stash > 8192) stash = 8192;
     uint64_t stash_cap = next_pow2(stash < 1 ? 1 : stash);
     if (stash_cap < (split ? 2048u : 1024u)) stash_cap = split ? 2048u : 1024u;
-    while (stash_cap > 1024 && 8 * (stash_cap + out_cap) > kMaxDynLds) stash_cap >>= 1;
-    if (8 * (stash_cap + out_cap) > kMaxDynLds) return SEGTOPK_NOT_SUPPORTED;
+    // The sliced kernel also keeps a workgroup's shared-histogram
+    // contributions in LDS (kBuckets words after the stash and the staging).
+    const uint64_t extra = split ? 4u * kBuckets : 0u;
+    while (stash_cap > 1024 && 8 * (stash_cap + out_cap) + extra > kMaxDynLds) stash_cap >>= 1;
+    if (8 * (stash_cap + out_cap) + extra > kMaxDynLds) return SEGTOPK_NOT_SUPPORTED;
     p.stash_cap = (uint32_t)stash_cap;
     p.out_cap = (uint32_t)out_cap;
     pl.lds = 8 * (size_t)(stash_cap + out_cap);
+    const size_t lds_sliced = pl.lds + (size_t)extra;
     pl.largest = r.direction == SEGTOPK_MAX;
     pl.type = type;
     pl.pairs = pairs;
@@ -403,7 +435,7 @@ int make_plan(const Request &r, int dev, Plan &pl) {
     if (split) {
         // As many workgroups as the device holds at once, so that all the
         // slices of a segment run together and share their bound.
-        const uint64_t target = resident_wgs_for(type, dev, pl.largest, pl.lds);
+        const uint64_t target = resident_wgs_for(type, dev, pl.largest, lds_sliced);
         if (S < 8) {
             P = target / S;  // every slice of every segment resident at once
         } else {
@@ -422,6 +454,7 @@ int make_plan(const Request &r, int dev, Plan &pl) {
     if (grid > 0x7FFFFFFFull) return SEGTOPK_NOT_SUPPORTED;
     pl.grid = (uint32_t)grid;
     pl.variant = many ? kVariantOne : (P > 1 ? kVariantSliced : kVariantSplit);
+    if (P > 1) pl.lds = lds_sliced;
 
     // Scratch.  One workgroup per segment for many segments of unknown sizes
     // (not all within one chunk by the hint): process the largest first.

@@ -22,24 +22,37 @@ import oracle
 import segmented_top_selection_amd as st
 
 KEY_CANARY = {"f32": 0x7FC0BEEF, "u32": 0x7FC0BEEF, "i32": 0x7FC0BEEF, "bf16": 0xFFBE,
-              "f16": 0xFFBE, "u16": 0xFFBE, "i16": 0xFFBE}
+              "f16": 0xFFBE, "u16": 0xFFBE, "i16": 0xFFBE, "u64": 0x7FF0DEADBEEFCAFE,
+              "i64": 0x7FF0DEADBEEFCAFE, "f64": 0x7FF0DEADBEEFCAFE}
 VAL_CANARY = 0x5EEDF00D
 VAL_CANARY64 = 0x5EEDF00DCAFED00D
 
 TORCH_KEY_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16,
                    "u32": torch.int32, "i32": torch.int32, "u16": torch.int16,
-                   "i16": torch.int16}
+                   "i16": torch.int16, "u64": torch.int64, "i64": torch.int64,
+                   "f64": torch.float64}
 
 
 def key_bits_np(t: torch.Tensor) -> np.ndarray:
-    """Raw key bits of a CPU/GPU tensor as uint32 numpy."""
+    """Raw key bits of a CPU/GPU tensor as uint32 numpy (uint64 for 8-byte
+    keys)."""
     t = t.detach().cpu().contiguous()
     if t.element_size() == 2:
         return t.view(torch.int16).numpy().view(np.uint16).astype(np.uint32)
+    if t.element_size() == 8:
+        return t.view(torch.int64).numpy().view(np.uint64)
     return t.view(torch.int32).numpy().view(np.uint32)
 
 
 def numeric_np(bits: np.ndarray, key_type: str) -> np.ndarray:
+    """Key values from raw bits: float64 for the float types and the 32- and
+    16-bit integers (exact); the 64-bit integers stay integers (exact)."""
+    if key_type == "u64":
+        return np.asarray(bits, dtype=np.uint64)
+    if key_type == "i64":
+        return np.asarray(bits, dtype=np.uint64).view(np.int64)
+    if key_type == "f64":
+        return np.asarray(bits, dtype=np.uint64).view(np.float64)
     bits = np.asarray(bits, dtype=np.uint32)
     if key_type == "f32":
         return bits.view(np.float32).astype(np.float64)
@@ -55,6 +68,12 @@ def numeric_np(bits: np.ndarray, key_type: str) -> np.ndarray:
 
 
 def oracle_keys_view(bits_u32: np.ndarray, key_type: str) -> np.ndarray:
+    if key_type == "u64":
+        return bits_u32.astype(np.uint64)
+    if key_type == "i64":
+        return bits_u32.astype(np.uint64).view(np.int64)
+    if key_type == "f64":
+        return bits_u32.astype(np.uint64).view(np.float64)
     if key_type in ("bf16", "f16", "u16"):
         return bits_u32.astype(np.uint16)
     if key_type == "i16":
@@ -86,6 +105,8 @@ def run_gpu(keys, values, offsets, k, key_type, largest, determinism, tie_break,
     out_k = torch.empty((s, k), dtype=keys.dtype, device=dev)
     if keys.element_size() == 2:
         out_k.view(torch.int16).fill_(KEY_CANARY[key_type] - 65536)
+    elif keys.element_size() == 8:
+        out_k.view(torch.int64).fill_(KEY_CANARY[key_type])
     else:
         out_k.view(torch.int32).fill_(KEY_CANARY[key_type])
     out_v = None
@@ -129,7 +150,12 @@ def run_oracle(keys_bits, values_u32, offsets_np, k, key_type, largest, prefer_l
     ok, ov = oracle.batched_topk(oracle_keys_view(keys_bits, key_type), offsets_np, k,
                                  key_type=key_type, values=values_u32, largest=largest,
                                  prefer_larger=prefer_larger, k_per_segment=k_per_segment)
-    ok = ok.view(np.uint16).astype(np.uint32) if ok.dtype.itemsize == 2 else ok.view(np.uint32)
+    if ok.dtype.itemsize == 2:
+        ok = ok.view(np.uint16).astype(np.uint32)
+    elif ok.dtype.itemsize == 8:
+        ok = ok.view(np.uint64)
+    else:
+        ok = ok.view(np.uint32)
     return ok, ov
 
 
@@ -183,8 +209,10 @@ def compare(gk, gv, ok, ov, offsets_np, k, key_type, determinism, ordering, keys
         return
 
     # not_guaranteed: multiset of numeric key values
-    gnum = np.where(valid, numeric_np(gk, key_type), np.inf)
-    onum = np.where(valid, numeric_np(ok, key_type), np.inf)
+    gn, on = numeric_np(gk, key_type), numeric_np(ok, key_type)
+    fill = np.inf if gn.dtype.kind == "f" else np.iinfo(gn.dtype).max
+    gnum = np.where(valid, gn, fill)
+    onum = np.where(valid, on, fill)
     assert np.array_equal(np.sort(gnum, axis=1), np.sort(onum, axis=1)), "key multiset mismatch"
     if gv is not None:
         starts = offsets_np[:-1]

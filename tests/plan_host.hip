@@ -16,6 +16,10 @@ hipError_t launch_topk(const Params &, bool, int, uint32_t, size_t, hipStream_t)
     return hipSuccess;
 }
 template <int KT> int topk_per_cu(bool, size_t) { return 3; }
+template <int KT>
+hipError_t launch_topk64(const Params &, bool, uint32_t, size_t, hipStream_t) {
+    return hipSuccess;
+}
 }  // namespace segtopk_impl
 
 static long g_bad = 0, g_plans = 0;
@@ -36,7 +40,7 @@ int main() {
     const int64_t Ss[] = {1, 2, 3, 7, 8, 9, 100, 255, 256, 1000, 2047, 2048, 100000, INT32_MAX};
     const int64_t ks[] = {1, 2, 63, 64, 256, 4096, 4097, 65536, (1ll << 30) + 1, INT32_MAX};
     const int64_t hints[] = {0, 1, 1000, 16384, 1ll << 20, 1ll << 40};
-    for (int kt : {SEGTOPK_KEY_F32, SEGTOPK_KEY_BF16})
+    for (int kt : {SEGTOPK_KEY_F32, SEGTOPK_KEY_BF16, SEGTOPK_KEY_U64})
         for (int64_t S : Ss)
             for (int64_t k : ks)
                 for (int ord : {SEGTOPK_UNSORTED, SEGTOPK_STABLE_SORTED})
@@ -60,6 +64,13 @@ int main() {
                             continue;
                         }
                         const Params &p = pl.p;
+                        if (kt == SEGTOPK_KEY_U64) {
+                            // 64-bit keys: one workgroup per segment, no scratch
+                            if (pl.grid != (uint64_t)S || pl.scratch_bytes || pl.lds > kMaxDynLds ||
+                                (ord != SEGTOPK_UNSORTED && p.out_cap < (uint64_t)k))
+                                fail("64-bit plan", S, k, ord, hint);
+                            continue;
+                        }
                         if (p.stash_cap < 1024 || p.stash_cap > 8192 ||
                             (p.stash_cap & (p.stash_cap - 1)))
                             fail("stash size", S, k, ord, hint);

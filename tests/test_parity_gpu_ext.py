@@ -232,3 +232,68 @@ def test_one_segment_of_2_28_keys(det, tb):
                        out_k.cpu().numpy()[0].view(np.uint32), k, False, det, tb)
     del keys, vals, q
     torch.cuda.empty_cache()
+
+
+def _keys64(total, key_type, gen, rng, kind):
+    """64-bit keys: random full-width bits, a few tied levels, or extremes."""
+    if kind == "random":
+        if key_type == "f64":
+            return torch.randn(total, generator=gen, device=DEV, dtype=torch.float64) * 1e3
+        hi = torch.randint(-(2 ** 31), 2 ** 31, (total,), generator=gen, device=DEV, dtype=torch.int64)
+        lo = torch.randint(0, 2 ** 32, (total,), generator=gen, device=DEV, dtype=torch.int64)
+        return (hi << 32) | lo
+    if kind == "levels":
+        lv = torch.randint(-6, 7, (total,), generator=gen, device=DEV, dtype=torch.int64)
+        return lv.double() / 4 if key_type == "f64" else lv * 3
+    if key_type == "f64":
+        pool = np.array([0.0, -0.0, 5e-324, -5e-324, 1.0, -1.0, np.inf, -np.inf,
+                         1.7976931348623157e308, -1.7976931348623157e308])
+        return torch.from_numpy(rng.choice(pool, total)).to(DEV)
+    pool = np.array([0, 1, 2, 2 ** 62, 2 ** 63 - 1, -(2 ** 63), -(2 ** 63) + 1, -1, -2],
+                    dtype=np.int64)
+    return torch.from_numpy(rng.choice(pool, total)).to(DEV)
+
+
+@pytest.mark.parametrize("key_type", ["u64", "i64", "f64"])
+def test_sixty_four_bit_keys(key_type):
+    rng = np.random.default_rng(91)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(92)
+    sizes = [0, 1, 7, 33, 34, 100, 2047, 2048, 2049, 5000, -3, 40000, 70000, 5]
+    off, total = offsets_from(sizes, 5)
+    vals = torch.arange(total, dtype=torch.int32, device=DEV)
+    wide = torch.arange(total, dtype=torch.int64, device=DEV) | (7 << 40)
+    for kind in ("random", "levels", "extreme"):
+        keys = _keys64(total, key_type, g, rng, kind)
+        say(f"[64-bit {key_type} {kind}] keys={total}")
+        for largest in (True, False):
+            for det, tb in MODES:
+                for ordering in ("unsorted", "stable_sorted"):
+                    check(keys, vals, off, 33, key_type, largest, det, tb, ordering,
+                          values_are="position")
+            check(keys, wide, off, 300, key_type, largest, "gpu_to_gpu", "prefer_larger_index",
+                  "stable_sorted")
+            check(keys, None, off, 40, key_type, largest, "gpu_to_gpu", "prefer_smaller_index",
+                  "unsorted")
+    # many segments; a few long ones (passes streamed from HBM until the
+    # k-th bucket fits the candidate list); all-equal keys (index passes)
+    for sizes, kind, k in ((rng.integers(0, 9000, 2100), "random", 64),
+                           (rng.integers(200000, 500000, 4), "random", 1000),
+                           ([300000, 5000, 70000], "levels", 2500)):
+        off, total = offsets_from(sizes)
+        keys = _keys64(total, key_type, g, rng, kind)
+        vals = torch.arange(total, dtype=torch.int32, device=DEV)
+        kseg = torch.from_numpy(rng.integers(0, k + 10, len(sizes)).astype(np.int32)).to(DEV)
+        for det, tb in (MODES[0], MODES[3], MODES[4]):
+            check(keys, vals, off, k, key_type, True, det, tb, "unsorted", values_are="position")
+            check(keys, vals, off, k, key_type, False, det, tb, "unsorted",
+                  values_are="position", k_per_segment=kseg)
+        check(keys, vals, off, min(k, 4096), key_type, True, "gpu_to_gpu", "prefer_smaller_index",
+              "stable_sorted", values_are="position")
+    same = torch.full((100000,), 3, dtype=torch.int64, device=DEV)
+    if key_type == "f64":
+        same = same.double()
+    off = torch.tensor([0, 100000], dtype=torch.int64, device=DEV)
+    vals = torch.arange(100000, dtype=torch.int32, device=DEV)
+    for tb in ("prefer_smaller_index", "prefer_larger_index"):
+        check(same, vals, off, 3000, key_type, True, "gpu_to_gpu", tb, "stable_sorted")
