@@ -23,10 +23,10 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 
 # The oracle's own key-type codes (independent of the GPU library's header).
 KEY_TYPES = {"f32": 0, "bf16": 1, "u32": 2, "i32": 3, "f16": 4, "u16": 5, "i16": 6,
-             "u64": 7, "i64": 8, "f64": 9}
+             "u64": 7, "i64": 8, "f64": 9, "u8": 10, "i8": 11}
 KEY_NUMPY = {"f32": np.float32, "bf16": np.uint16, "u32": np.uint32, "i32": np.int32,
              "f16": np.uint16, "u16": np.uint16, "i16": np.int16, "u64": np.uint64,
-             "i64": np.int64, "f64": np.float64}
+             "i64": np.int64, "f64": np.float64, "u8": np.uint8, "i8": np.int8}
 
 _lib = None
 
@@ -72,8 +72,8 @@ def batched_topk(keys, offsets, k, *, key_type="f32", values=None, largest=True,
     """Sort-and-take top-k per segment.
 
     keys           1-D numpy array of raw key patterns (float32, uint16 bf16/f16
-                   bits, uint32, int32, uint16, int16, uint64, int64 or float64,
-                   matching ``key_type``)
+                   bits, uint32, int32, uint16, int16, uint64, int64, float64,
+                   uint8 or int8, matching ``key_type``)
     offsets        int64 array of num_segments + 1 offsets
     values         optional 1-D payload array of 4- or 8-byte items (viewed as
                    uint32 / uint64)

@@ -47,7 +47,7 @@
  * Key types (the caller's raw bit patterns):
  *   0 = binary32 float, 1 = bfloat16 (16 bits), 2 = uint32, 3 = int32,
  *   4 = binary16 float (16 bits), 5 = uint16, 6 = int16, 7 = uint64,
- *   8 = int64, 9 = binary64 float.
+ *   8 = int64, 9 = binary64 float, 10 = uint8, 11 = int8.
  * Floating-point keys are compared as C doubles (every binary16, bfloat16,
  * binary32 and binary64 value is one exactly); integer keys are compared as
  * integers (int64_t, and uint64_t for uint64 keys, which a double cannot
@@ -70,7 +70,7 @@
 #endif
 
 enum { OR_F32 = 0, OR_BF16 = 1, OR_U32 = 2, OR_I32 = 3, OR_F16 = 4, OR_U16 = 5, OR_I16 = 6,
-       OR_U64 = 7, OR_I64 = 8, OR_F64 = 9 };
+       OR_U64 = 7, OR_I64 = 8, OR_F64 = 9, OR_U8 = 10, OR_I8 = 11 };
 
 /* One item of a segment.  The key is held exactly in one of three fields
  * (the other two are zero): f for floating-point keys, s for signed and
@@ -175,6 +175,10 @@ static int64_t decode_int(const void *keys, int type, int64_t pos)
         memcpy(&v, (const char *)keys + 8 * pos, 8);
         return v;
     }
+    case OR_U8:
+        return (int64_t)((const uint8_t *)keys)[pos];
+    case OR_I8:
+        return (int64_t)((const int8_t *)keys)[pos];
     default:
         return 0;
     }
@@ -183,6 +187,7 @@ static int64_t decode_int(const void *keys, int type, int64_t pos)
 static int key_bytes(int type)
 {
     switch (type) {
+    case OR_U8: case OR_I8: return 1;
     case OR_BF16: case OR_F16: case OR_U16: case OR_I16: return 2;
     case OR_U64: case OR_I64: case OR_F64: return 8;
     default: return 4;
@@ -291,7 +296,7 @@ int oracle_batched_topk_ex(const void *keys_in, int key_type, const void *values
     int64_t i;
     int failed = 0;
 
-    if (num_segments < 0 || k < 0 || key_type < OR_F32 || key_type > OR_F64)
+    if (num_segments < 0 || k < 0 || key_type < OR_F32 || key_type > OR_I8)
         return 1;
     if (values_in && value_bytes != 4 && value_bytes != 8)
         return 1;

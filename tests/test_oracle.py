@@ -336,7 +336,7 @@ def test_rejects_bad_arguments():
                             out.ctypes.data, None, 1)
     assert lib.oracle_batched_topk(*args(-1, 1, 0)) == 1
     assert lib.oracle_batched_topk(*args(1, -1, 0)) == 1
-    assert lib.oracle_batched_topk(*args(1, 1, 10)) == 1
+    assert lib.oracle_batched_topk(*args(1, 1, 12)) == 1
     assert lib.oracle_batched_topk(*args(1, 1, -1)) == 1
     assert lib.oracle_batched_topk(*args(1, 1, 0)) == 0
 
@@ -347,7 +347,7 @@ def test_rejects_bad_arguments():
 #    any width), floats with numpy float64; neither goes through the oracle.
 # --------------------------------------------------------------------------
 WIDE_NUMPY = {"u16": np.uint16, "i16": np.int16, "u64": np.uint64, "i64": np.int64,
-              "f64": np.float64}
+              "f64": np.float64, "u8": np.uint8, "i8": np.int8}
 WIDE_ALPHABET = {
     "u16": [0, 1, 2, 2 ** 15, 2 ** 16 - 2, 2 ** 16 - 1],
     "i16": [-(2 ** 15), -1, 0, 1, 2 ** 15 - 1],
@@ -355,6 +355,8 @@ WIDE_ALPHABET = {
     "u64": [0, 1, 2 ** 53 + 1, 2 ** 63, 2 ** 63 + 1, 2 ** 64 - 2, 2 ** 64 - 1],
     "i64": [-(2 ** 63), -(2 ** 63) + 1, -1, 0, 2 ** 53 + 1, 2 ** 63 - 2, 2 ** 63 - 1],
     "f64": [float("-inf"), -1.5, -0.0, 0.0, 5e-324, 1.5, float("inf")],
+    "u8": [0, 1, 2, 127, 128, 254, 255],
+    "i8": [-128, -127, -1, 0, 1, 126, 127],
 }
 
 
@@ -451,6 +453,8 @@ def test_wide_types_against_python_sort_with_per_segment_k(key_type, largest, pr
         lo, hi = (0, 2 ** 64) if key_type == "u64" else (-(2 ** 63), 2 ** 63)
         pool = alpha + [int(x) for x in rng.integers(0, 2 ** 62, 40)] + [hi - 1 - j for j in range(5)]
         pool = [v for v in pool if lo <= v < hi]
+    elif key_type in ("u8", "i8"):
+        pool = alpha + [int(x) for x in rng.integers(0 if key_type == "u8" else -128, 128, 40)]
     else:
         pool = alpha + [int(x) for x in rng.integers(0 if key_type == "u16" else -(2 ** 15),
                                                       2 ** 15, 40)]
@@ -516,3 +520,16 @@ def test_per_segment_k_equal_to_k_matches_uniform_call():
     b = oracle.batched_topk(keys, off, 64, values=vals,
                             k_per_segment=np.full(4, 64, np.int32))
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("key_type", ["u8", "i8"])
+def test_every_8bit_pattern_in_order(key_type):
+    """All 256 patterns, select-all + stable order, against Python's ordering
+    of the integers they stand for."""
+    pats = np.arange(256, dtype=np.uint8).view(WIDE_NUMPY[key_type])
+    off = np.array([0, 256], dtype=np.int64)
+    for largest in (True, False):
+        _, ov = oracle.batched_topk(pats, off, 256, key_type=key_type,
+                                    values=np.arange(256, dtype=np.uint32), largest=largest)
+        want = sorted(range(256), key=lambda i: (-int(pats[i]) if largest else int(pats[i]), i))
+        assert list(ov[0]) == want
