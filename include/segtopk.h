@@ -56,7 +56,9 @@ typedef enum segtopk_key_type {
     SEGTOPK_KEY_I16 = 6,  /* signed 16-bit integer                  */
     SEGTOPK_KEY_U64 = 7,  /* unsigned 64-bit integer                */
     SEGTOPK_KEY_I64 = 8,  /* signed 64-bit integer                  */
-    SEGTOPK_KEY_F64 = 9   /* IEEE binary64                          */
+    SEGTOPK_KEY_F64 = 9,  /* IEEE binary64                          */
+    SEGTOPK_KEY_U8 = 10,  /* unsigned 8-bit integer                 */
+    SEGTOPK_KEY_I8 = 11   /* signed 8-bit integer                   */
 } segtopk_key_type;
 
 /* ---- request --------------------------------------------------------- */
@@ -233,10 +235,10 @@ int batched_topk_ex(const segtopk_keys *keys, const segtopk_values *values, int3
  * streams, or replays of graphs holding such calls) race and must be ordered
  * by the caller.  A request whose plan needs more than
  * SEGTOPK_STATIC_SCRATCH_BYTES returns SEGTOPK_SCRATCH_TOO_SMALL and queues
- * nothing (for instance six segments with k = 4096, unsorted: about 37 MiB
- * of per-workgroup candidate slots; a max_segment_size hint that rules out
- * splitting avoids the scratch).  32 x 4 Mi keys with k = 2048 (30.5 MiB) or
- * one segment with k = 2048 (30 MiB) fit.
+ * nothing (for instance 500 segments with k = 2048 of unknown sizes, split
+ * two ways: about 41 MB of per-workgroup candidate slots; a max_segment_size
+ * hint that rules out splitting avoids that scratch).  32 x 4 Mi keys with
+ * k = 2048 (30.5 MiB) or one segment with k = 2048 (30 MiB) fit.
  */
 #define SEGTOPK_STATIC_SCRATCH_BYTES (32u << 20)
 int batched_topk_ex_noalloc(const segtopk_keys *keys, const segtopk_values *values,

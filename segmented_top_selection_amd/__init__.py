@@ -21,9 +21,9 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "segtopk.h")
 
 # Values of the enums in include/segtopk.h.
 KEY_TYPES = {"f32": 0, "bf16": 1, "u32": 2, "i32": 3, "f16": 4, "u16": 5, "i16": 6,
-             "u64": 7, "i64": 8, "f64": 9}
+             "u64": 7, "i64": 8, "f64": 9, "u8": 10, "i8": 11}
 KEY_BYTES = {"f32": 4, "bf16": 2, "u32": 4, "i32": 4, "f16": 2, "u16": 2, "i16": 2,
-             "u64": 8, "i64": 8, "f64": 8}
+             "u64": 8, "i64": 8, "f64": 8, "u8": 1, "i8": 1}
 DIRECTIONS = {"max": 0, "min": 1}
 DETERMINISM = {"not_guaranteed": 0, "run_to_run": 1, "gpu_to_gpu": 2}
 TIE_BREAK = {"unspecified": 0, "prefer_smaller_index": 1, "prefer_larger_index": 2}
@@ -34,7 +34,7 @@ MAX_SORTED_K = 4096
 
 _DTYPE_KEY = {torch.float32: "f32", torch.bfloat16: "bf16", torch.float16: "f16",
               torch.int32: "i32", torch.int16: "i16", torch.int64: "i64",
-              torch.float64: "f64"}
+              torch.float64: "f64", torch.uint8: "u8", torch.int8: "i8"}
 if hasattr(torch, "uint32"):
     _DTYPE_KEY[torch.uint32] = "u32"
 if hasattr(torch, "uint16"):
@@ -160,9 +160,9 @@ def batched_topk(keys: torch.Tensor, segment_offsets: torch.Tensor, k: int, *,
     """Top-k of every segment of ``keys`` on the GPU.
 
     keys             1-D device tensor (float32, bfloat16, float16, float64,
-                     int32, int16, int64; for unsigned keys pass their bits as
-                     the signed type of the same width with key_type="u32" /
-                     "u16" / "u64")
+                     int32, int16, int64, int8, uint8; for the other unsigned
+                     keys pass their bits as the signed type of the same width
+                     with key_type="u32" / "u16" / "u64")
     segment_offsets  int64 device tensor of num_segments + 1 offsets
     values           optional 1-D payload of 4- or 8-byte items (any dtype),
                      same length as keys

@@ -1,7 +1,8 @@
 // Top-k kernel for IEEE binary64 keys (one translation unit per key type, so
 // that the library builds in parallel).
-#include "topk64_kernel.h"
+#include "topk_plain_kernel.h"
 
 namespace segtopk_impl {
-template hipError_t launch_topk64<SEGTOPK_KEY_F64>(const Params &, bool, uint32_t, size_t, hipStream_t);
+template hipError_t launch_topk_plain<SEGTOPK_KEY_F64>(const Params &, bool, uint32_t, size_t,
+                                                        hipStream_t);
 }  // namespace segtopk_impl

@@ -92,17 +92,21 @@ constexpr uint32_t kTargetWorkgroups = 2048;  // enough to fill 256 CUs several 
 constexpr uint32_t kMinSlice = 16384;
 constexpr int64_t kOrderMinSegments = 256;  // fewer segments: no processing order
 constexpr size_t kMaxCachedStreams = 16;    // scratch buffers kept (LRU beyond that)
-constexpr uint32_t kCand64Entries = 2048;   // LDS candidate list of the 64-bit-key kernel
+constexpr uint32_t kPlainCand = 2048;  // LDS candidate list of the plain kernel
 
-bool is_wide_key(int type) {
-    return type == SEGTOPK_KEY_U64 || type == SEGTOPK_KEY_I64 || type == SEGTOPK_KEY_F64;
+// Key types served by the plain kernel (64-bit and 8-bit keys).
+bool is_plain_key(int type) {
+    return type == SEGTOPK_KEY_U64 || type == SEGTOPK_KEY_I64 || type == SEGTOPK_KEY_F64 ||
+           type == SEGTOPK_KEY_U8 || type == SEGTOPK_KEY_I8;
 }
 
 int key_bytes(int type) {
-    if (type == SEGTOPK_KEY_BF16 || type == SEGTOPK_KEY_F16 || type == SEGTOPK_KEY_U16 ||
-        type == SEGTOPK_KEY_I16)
-        return 2;
-    return is_wide_key(type) ? 8 : 4;
+    switch (type) {
+    case SEGTOPK_KEY_U8: case SEGTOPK_KEY_I8: return 1;
+    case SEGTOPK_KEY_BF16: case SEGTOPK_KEY_F16: case SEGTOPK_KEY_U16: case SEGTOPK_KEY_I16: return 2;
+    case SEGTOPK_KEY_U64: case SEGTOPK_KEY_I64: case SEGTOPK_KEY_F64: return 8;
+    default: return 4;
+    }
 }
 
 // Smallest power of two >= x, for 1 <= x <= 2^62.
@@ -274,9 +278,11 @@ uint32_t resident_wgs_for(int type, int dev, bool largest, size_t lds) {
 hipError_t launch(int type, const Params &p, bool largest, int variant, uint32_t grid, size_t lds,
                   hipStream_t st) {
     switch (type) {
-    case SEGTOPK_KEY_U64: return launch_topk64<SEGTOPK_KEY_U64>(p, largest, grid, lds, st);
-    case SEGTOPK_KEY_I64: return launch_topk64<SEGTOPK_KEY_I64>(p, largest, grid, lds, st);
-    case SEGTOPK_KEY_F64: return launch_topk64<SEGTOPK_KEY_F64>(p, largest, grid, lds, st);
+    case SEGTOPK_KEY_U64: return launch_topk_plain<SEGTOPK_KEY_U64>(p, largest, grid, lds, st);
+    case SEGTOPK_KEY_I64: return launch_topk_plain<SEGTOPK_KEY_I64>(p, largest, grid, lds, st);
+    case SEGTOPK_KEY_F64: return launch_topk_plain<SEGTOPK_KEY_F64>(p, largest, grid, lds, st);
+    case SEGTOPK_KEY_U8: return launch_topk_plain<SEGTOPK_KEY_U8>(p, largest, grid, lds, st);
+    case SEGTOPK_KEY_I8: return launch_topk_plain<SEGTOPK_KEY_I8>(p, largest, grid, lds, st);
     case SEGTOPK_KEY_F32: return launch_topk<SEGTOPK_KEY_F32>(p, largest, variant, grid, lds, st);
     case SEGTOPK_KEY_BF16: return launch_topk<SEGTOPK_KEY_BF16>(p, largest, variant, grid, lds, st);
     case SEGTOPK_KEY_U32: return launch_topk<SEGTOPK_KEY_U32>(p, largest, variant, grid, lds, st);
@@ -316,7 +322,7 @@ struct Plan {
 int validate(const Request &r) {
     if (!r.keys) return SEGTOPK_INVALID_ARGUMENT;
     const int type = r.keys->type;
-    if (type < SEGTOPK_KEY_F32 || type > SEGTOPK_KEY_F64) return SEGTOPK_INVALID_ARGUMENT;
+    if (type < SEGTOPK_KEY_F32 || type > SEGTOPK_KEY_I8) return SEGTOPK_INVALID_ARGUMENT;
     if (r.direction != SEGTOPK_MAX && r.direction != SEGTOPK_MIN) return SEGTOPK_INVALID_ARGUMENT;
     if (r.determinism < SEGTOPK_NOT_GUARANTEED || r.determinism > SEGTOPK_GPU_TO_GPU)
         return SEGTOPK_INVALID_ARGUMENT;
@@ -378,15 +384,16 @@ int make_plan(const Request &r, int dev, Plan &pl) {
     p.vindex = pl.wide_values ? 1u : 0u;
     p.vshift = pl.wide_values ? 1u : 0u;
 
-    if (is_wide_key(type)) {
-        // 64-bit keys: one workgroup per segment, no scratch; dynamic LDS
-        // holds the candidate list and the output staging (16 bytes an entry).
+    if (is_plain_key(type)) {
+        // 64-bit and 8-bit keys: one workgroup per segment, no scratch;
+        // dynamic LDS holds the candidate list and the output staging (16
+        // bytes an entry).
         uint64_t oc = 0;
         if (sorted || k <= 256) oc = next_pow2(k < 2 ? 2 : k);
         p.out_cap = (uint32_t)oc;
-        p.stash_cap = kCand64Entries;
+        p.stash_cap = kPlainCand;
         p.wg_per_seg = 1;
-        pl.lds = 16 * (size_t)(kCand64Entries + oc);
+        pl.lds = 16 * (size_t)(kPlainCand + oc);
         if (pl.lds > kMaxDynLds) return SEGTOPK_NOT_SUPPORTED;
         pl.largest = r.direction == SEGTOPK_MAX;
         pl.type = type;

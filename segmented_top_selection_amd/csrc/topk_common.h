@@ -73,9 +73,10 @@ hipError_t launch_topk(const Params &p, bool largest, int variant, uint32_t grid
 // current device with `lds` bytes of dynamic LDS (at least 1).
 template <int KT> int topk_per_cu(bool largest, size_t lds);
 
-// Launches the 64-bit-key kernel for key type KT (one workgroup per segment,
-// grid workgroups, `lds` bytes of dynamic LDS).
+// Launches the plain kernel (64-bit and 8-bit keys) for key type KT: one
+// workgroup per segment, grid workgroups, `lds` bytes of dynamic LDS.
 template <int KT>
-hipError_t launch_topk64(const Params &p, bool largest, uint32_t grid, size_t lds, hipStream_t st);
+hipError_t launch_topk_plain(const Params &p, bool largest, uint32_t grid, size_t lds,
+                             hipStream_t st);
 
 }  // namespace segtopk_impl

@@ -1,4 +1,6 @@
-// topk64_kernel.h -- segmented top-k for 64-bit keys (uint64, int64, binary64).
+// topk_plain_kernel.h -- segmented top-k for the key widths the streaming
+// kernels do not serve: 64-bit keys (uint64, int64, binary64) and 8-bit keys
+// (uint8, int8).
 //
 // The same method as the 32- and 16-bit kernels -- most-significant-digit radix
 // selection with early stop, then a final filter that writes every key beyond
@@ -7,9 +9,10 @@
 //   [PR "Implement Segmented TopK using Thread-Block-Clusters", §1.2 Radix
 //    (digit) top-k, §1.4 Early stop, §1.5 Final filter and output placement,
 //    §1.6 Determinism / tie-breaking]
-// laid out more plainly, for the wider keys:
+// laid out more plainly:
 //  * one workgroup of four wave64 per segment;
-//  * 11-bit digits (64 = 5 x 11 + 9 bits), every pass a histogram of the next
+//  * 11-bit digits (64 = 5 x 11 + 9 bits; an 8-bit key is one digit of 8
+//    bits), every pass a histogram of the next
 //    digit of the keys that match the splitter so far, scanned best-first;
 //    buckets are reversed for MAX after the order-preserving transform, which
 //    folds -0.0 onto +0.0   [PR "Fix BlockTopK +/-0.0 handling", Fix];
@@ -29,22 +32,38 @@ namespace {
 
 constexpr uint32_t kCand64 = 2048;  // LDS candidate list entries (16 bytes each)
 
-// Order-preserving bits of 64-bit keys: ord(a) < ord(b) exactly when a < b,
-// ord(-0.0) == ord(+0.0).
-template <int KT> struct Key64;
-template <> struct Key64<SEGTOPK_KEY_U64> {
-    __host__ __device__ __forceinline__ static uint64_t ord(uint64_t r) { return r; }
+// Order-preserving bits, widened to 64: ord(a) < ord(b) exactly when a < b,
+// ord(-0.0) == ord(+0.0).  Raw is the key's storage type.
+template <int KT> struct KeyW;
+template <> struct KeyW<SEGTOPK_KEY_U64> {
+    typedef uint64_t Raw;
+    static constexpr int kBits = 64;
+    __host__ __device__ __forceinline__ static uint64_t ord(Raw r) { return r; }
 };
-template <> struct Key64<SEGTOPK_KEY_I64> {
-    __host__ __device__ __forceinline__ static uint64_t ord(uint64_t r) {
+template <> struct KeyW<SEGTOPK_KEY_I64> {
+    typedef uint64_t Raw;
+    static constexpr int kBits = 64;
+    __host__ __device__ __forceinline__ static uint64_t ord(Raw r) {
         return r ^ 0x8000000000000000ull;
     }
 };
-template <> struct Key64<SEGTOPK_KEY_F64> {
-    __host__ __device__ __forceinline__ static uint64_t ord(uint64_t r) {
+template <> struct KeyW<SEGTOPK_KEY_F64> {
+    typedef uint64_t Raw;
+    static constexpr int kBits = 64;
+    __host__ __device__ __forceinline__ static uint64_t ord(Raw r) {
         r = (r == 0x8000000000000000ull) ? 0ull : r;  // -0.0 joins +0.0
         return r ^ ((uint64_t)((int64_t)r >> 63) | 0x8000000000000000ull);
     }
+};
+template <> struct KeyW<SEGTOPK_KEY_U8> {
+    typedef uint8_t Raw;
+    static constexpr int kBits = 8;
+    __host__ __device__ __forceinline__ static uint64_t ord(Raw r) { return r; }
+};
+template <> struct KeyW<SEGTOPK_KEY_I8> {
+    typedef uint8_t Raw;
+    static constexpr int kBits = 8;
+    __host__ __device__ __forceinline__ static uint64_t ord(Raw r) { return (uint64_t)(r ^ 0x80u); }
 };
 
 struct Shared64 {
@@ -67,7 +86,8 @@ template <bool LARGEST> __device__ __forceinline__ bool out_before64(uint4 a, ui
 }
 
 template <int KT, bool LARGEST>
-__global__ __launch_bounds__(kThreads) void topk64_kernel(Params p) {
+__global__ __launch_bounds__(kThreads) void topk_plain_kernel(Params p) {
+    typedef typename KeyW<KT>::Raw Raw;
     __shared__ Shared64 sh;
     extern __shared__ uint4 dyn64[];
     uint4 *cand = dyn64;                                    // kCand64 entries
@@ -90,18 +110,18 @@ __global__ __launch_bounds__(kThreads) void topk64_kernel(Params p) {
     }
     sg.row = s;
     if (sg.k_i == 0) return;
-    const uint64_t *keys = static_cast<const uint64_t *>(p.keys_in) + sg.begin;
+    const Raw *keys = static_cast<const Raw *>(p.keys_in) + sg.begin;
 
     // Places one winner: staged for sorting, or written out.
-    auto emit = [&](uint32_t pos, uint64_t raw, uint32_t idx) {
+    auto emit = [&](uint32_t pos, Raw raw, uint32_t idx) {
         if (pos >= sg.k_i) return;
         if (stage) {
-            const uint64_t o = Key64<KT>::ord(raw);
+            const uint64_t o = KeyW<KT>::ord(raw);
             stage[pos] = make_uint4((uint32_t)o, (uint32_t)(o >> 32), idx, 0u);
             return;
         }
         const size_t oi = (size_t)sg.row * p.k + pos;
-        static_cast<uint64_t *>(p.keys_out)[oi] = raw;
+        static_cast<Raw *>(p.keys_out)[oi] = raw;
         if (p.vals_in) val_store(p, oi, val_load(p, sg, idx));
     };
 
@@ -120,7 +140,7 @@ __global__ __launch_bounds__(kThreads) void topk64_kernel(Params p) {
             }
         } else {
             for (uint32_t i = t; i < sg.n; i += kThreads) {
-                const uint64_t o = Key64<KT>::ord(keys[i]);
+                const uint64_t o = KeyW<KT>::ord(keys[i]);
                 if ((o & mask) == pref) f(o, i);
             }
         }
@@ -133,7 +153,7 @@ __global__ __launch_bounds__(kThreads) void topk64_kernel(Params p) {
         // ---- key digits ----
         uint32_t krem = sg.k_i, front = 0, placed = 0;
         bool done = false;
-        int shift = 64;
+        int shift = KeyW<KT>::kBits;
         while (!done && shift > 0) {
             const int wd = shift < kDigit ? shift : kDigit;
             const int sh_ = shift - wd;
@@ -171,8 +191,8 @@ __global__ __launch_bounds__(kThreads) void topk64_kernel(Params p) {
                 __syncthreads();
                 const uint64_t pmask = mask, ppref = pref;
                 for (uint32_t i = t; i < sg.n; i += kThreads) {
-                    const uint64_t raw = keys[i];
-                    const uint64_t o = Key64<KT>::ord(raw);
+                    const Raw raw = keys[i];
+                    const uint64_t o = KeyW<KT>::ord(raw);
                     const uint64_t m = o & pmask;
                     if (m == ppref) {
                         const uint32_t at = atomicAdd(&sh.ncand, 1u);
@@ -234,7 +254,7 @@ __global__ __launch_bounds__(kThreads) void topk64_kernel(Params p) {
             sh.ntie = 0;
         }
         __syncthreads();
-        auto classify = [&](uint64_t o, uint32_t idx, uint64_t raw) {
+        auto classify = [&](uint64_t o, uint32_t idx, Raw raw) {
             const uint64_t m = o & mask;
             if (better64<LARGEST>(m, pref)) {
                 const uint32_t at = atomicAdd(&sh.nfront, 1u);
@@ -258,8 +278,8 @@ __global__ __launch_bounds__(kThreads) void topk64_kernel(Params p) {
             }
         } else {
             for (uint32_t i = t; i < sg.n; i += kThreads) {
-                const uint64_t raw = keys[i];
-                classify(Key64<KT>::ord(raw), i, raw);
+                const Raw raw = keys[i];
+                classify(KeyW<KT>::ord(raw), i, raw);
             }
         }
     }
@@ -293,12 +313,12 @@ __global__ __launch_bounds__(kThreads) void topk64_kernel(Params p) {
         const uint4 e = stage[i];
         if (e.z == kNone) continue;
         const size_t oi = (size_t)sg.row * p.k + i;
-        static_cast<uint64_t *>(p.keys_out)[oi] = keys[e.z];
+        static_cast<Raw *>(p.keys_out)[oi] = keys[e.z];
         if (p.vals_in) val_store(p, oi, val_load(p, sg, e.z));
     }
 }
 
-template <typename K> hipError_t allow_lds64(K kernel, size_t lds) {
+template <typename K> hipError_t allow_lds_plain(K kernel, size_t lds) {
     static std::atomic<uint64_t> done{0};
     if (lds <= 64 * 1024) return hipSuccess;
     int dev = 0;
@@ -315,15 +335,15 @@ template <typename K> hipError_t allow_lds64(K kernel, size_t lds) {
 }  // namespace
 
 template <int KT>
-hipError_t launch_topk64(const Params &p, bool largest, uint32_t grid, size_t lds,
-                         hipStream_t st) {
+hipError_t launch_topk_plain(const Params &p, bool largest, uint32_t grid, size_t lds,
+                             hipStream_t st) {
     hipError_t e;
     if (largest) {
-        if ((e = allow_lds64(topk64_kernel<KT, true>, lds)) != hipSuccess) return e;
-        hipLaunchKernelGGL((topk64_kernel<KT, true>), dim3(grid), dim3(kThreads), lds, st, p);
+        if ((e = allow_lds_plain(topk_plain_kernel<KT, true>, lds)) != hipSuccess) return e;
+        hipLaunchKernelGGL((topk_plain_kernel<KT, true>), dim3(grid), dim3(kThreads), lds, st, p);
     } else {
-        if ((e = allow_lds64(topk64_kernel<KT, false>, lds)) != hipSuccess) return e;
-        hipLaunchKernelGGL((topk64_kernel<KT, false>), dim3(grid), dim3(kThreads), lds, st, p);
+        if ((e = allow_lds_plain(topk_plain_kernel<KT, false>, lds)) != hipSuccess) return e;
+        hipLaunchKernelGGL((topk_plain_kernel<KT, false>), dim3(grid), dim3(kThreads), lds, st, p);
     }
     return hipGetLastError();
 }

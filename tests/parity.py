@@ -23,20 +23,22 @@ import segmented_top_selection_amd as st
 
 KEY_CANARY = {"f32": 0x7FC0BEEF, "u32": 0x7FC0BEEF, "i32": 0x7FC0BEEF, "bf16": 0xFFBE,
               "f16": 0xFFBE, "u16": 0xFFBE, "i16": 0xFFBE, "u64": 0x7FF0DEADBEEFCAFE,
-              "i64": 0x7FF0DEADBEEFCAFE, "f64": 0x7FF0DEADBEEFCAFE}
+              "i64": 0x7FF0DEADBEEFCAFE, "f64": 0x7FF0DEADBEEFCAFE, "u8": 0xBE, "i8": 0xBE}
 VAL_CANARY = 0x5EEDF00D
 VAL_CANARY64 = 0x5EEDF00DCAFED00D
 
 TORCH_KEY_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16,
                    "u32": torch.int32, "i32": torch.int32, "u16": torch.int16,
                    "i16": torch.int16, "u64": torch.int64, "i64": torch.int64,
-                   "f64": torch.float64}
+                   "f64": torch.float64, "u8": torch.uint8, "i8": torch.int8}
 
 
 def key_bits_np(t: torch.Tensor) -> np.ndarray:
     """Raw key bits of a CPU/GPU tensor as uint32 numpy (uint64 for 8-byte
     keys)."""
     t = t.detach().cpu().contiguous()
+    if t.element_size() == 1:
+        return t.view(torch.uint8).numpy().astype(np.uint32)
     if t.element_size() == 2:
         return t.view(torch.int16).numpy().view(np.uint16).astype(np.uint32)
     if t.element_size() == 8:
@@ -54,6 +56,10 @@ def numeric_np(bits: np.ndarray, key_type: str) -> np.ndarray:
     if key_type == "f64":
         return np.asarray(bits, dtype=np.uint64).view(np.float64)
     bits = np.asarray(bits, dtype=np.uint32)
+    if key_type == "u8":
+        return bits.astype(np.float64)
+    if key_type == "i8":
+        return bits.astype(np.uint8).view(np.int8).astype(np.float64)
     if key_type == "f32":
         return bits.view(np.float32).astype(np.float64)
     if key_type == "bf16":
@@ -68,6 +74,10 @@ def numeric_np(bits: np.ndarray, key_type: str) -> np.ndarray:
 
 
 def oracle_keys_view(bits_u32: np.ndarray, key_type: str) -> np.ndarray:
+    if key_type == "u8":
+        return bits_u32.astype(np.uint8)
+    if key_type == "i8":
+        return bits_u32.astype(np.uint8).view(np.int8)
     if key_type == "u64":
         return bits_u32.astype(np.uint64)
     if key_type == "i64":
@@ -103,7 +113,9 @@ def run_gpu(keys, values, offsets, k, key_type, largest, determinism, tie_break,
         sys.stdout.flush()
     dev = keys.device
     out_k = torch.empty((s, k), dtype=keys.dtype, device=dev)
-    if keys.element_size() == 2:
+    if keys.element_size() == 1:
+        out_k.view(torch.uint8).fill_(KEY_CANARY[key_type])
+    elif keys.element_size() == 2:
         out_k.view(torch.int16).fill_(KEY_CANARY[key_type] - 65536)
     elif keys.element_size() == 8:
         out_k.view(torch.int64).fill_(KEY_CANARY[key_type])
@@ -150,7 +162,9 @@ def run_oracle(keys_bits, values_u32, offsets_np, k, key_type, largest, prefer_l
     ok, ov = oracle.batched_topk(oracle_keys_view(keys_bits, key_type), offsets_np, k,
                                  key_type=key_type, values=values_u32, largest=largest,
                                  prefer_larger=prefer_larger, k_per_segment=k_per_segment)
-    if ok.dtype.itemsize == 2:
+    if ok.dtype.itemsize == 1:
+        ok = ok.view(np.uint8).astype(np.uint32)
+    elif ok.dtype.itemsize == 2:
         ok = ok.view(np.uint16).astype(np.uint32)
     elif ok.dtype.itemsize == 8:
         ok = ok.view(np.uint64)

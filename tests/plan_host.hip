@@ -17,7 +17,7 @@ hipError_t launch_topk(const Params &, bool, int, uint32_t, size_t, hipStream_t)
 }
 template <int KT> int topk_per_cu(bool, size_t) { return 3; }
 template <int KT>
-hipError_t launch_topk64(const Params &, bool, uint32_t, size_t, hipStream_t) {
+hipError_t launch_topk_plain(const Params &, bool, uint32_t, size_t, hipStream_t) {
     return hipSuccess;
 }
 }  // namespace segtopk_impl

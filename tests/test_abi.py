@@ -47,7 +47,7 @@ def test_null_keys_descriptor():
 
 @pytest.mark.parametrize("kw", [
     dict(keys_in=0), dict(keys_out=0), dict(offsets=0), dict(values_out=0),
-    dict(key_type=-1), dict(key_type=10), dict(direction=2), dict(determinism=3),
+    dict(key_type=-1), dict(key_type=12), dict(direction=2), dict(determinism=3),
     dict(tie_break=3), dict(ordering=3), dict(k=-1), dict(k=2 ** 31),
     dict(num_segments=-1), dict(num_segments=2 ** 31),
     dict(keys_in=K_IN + 2), dict(key_type=1, keys_out=K_OUT + 1), dict(values_in=V_IN + 2),
@@ -87,7 +87,7 @@ def call_ex(**kw):
 @pytest.mark.parametrize("kw", [
     dict(value_bytes=2), dict(value_bytes=0), dict(value_bytes=16),
     dict(value_bytes=8, values_in=V_IN + 4), dict(k_per_segment=0x60002),
-    dict(keys_in=0), dict(key_type=10), dict(k=-1), dict(determinism=1, tie_break=2),
+    dict(keys_in=0), dict(key_type=12), dict(k=-1), dict(determinism=1, tie_break=2),
 ])
 def test_ex_invalid_arguments(kw):
     assert call_ex(**kw) == 1
@@ -120,6 +120,6 @@ def test_binding_rejects_unknown_key_type_and_negative_k():
     keys = torch.zeros(10)
     off = torch.tensor([0, 10], dtype=torch.int64)
     with pytest.raises(TypeError):
-        st.batched_topk(keys.to(torch.int8), off, 3)
+        st.batched_topk(keys.to(torch.complex64), off, 3)
     with pytest.raises(ValueError):
         st.batched_topk(keys, off, 3, key_type="x")

@@ -297,3 +297,45 @@ def test_sixty_four_bit_keys(key_type):
     vals = torch.arange(100000, dtype=torch.int32, device=DEV)
     for tb in ("prefer_smaller_index", "prefer_larger_index"):
         check(same, vals, off, 3000, key_type, True, "gpu_to_gpu", tb, "stable_sorted")
+
+
+@pytest.mark.parametrize("key_type", ["u8", "i8"])
+def test_eight_bit_keys(key_type):
+    """8-bit keys: every value repeats, so the index passes decide most rows."""
+    rng = np.random.default_rng(81)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(82)
+    dt = torch.uint8 if key_type == "u8" else torch.int8
+
+    def keys_of(total, kind):
+        if kind == "random":
+            return torch.randint(0, 256, (total,), generator=g, device=DEV).to(torch.uint8).view(dt)
+        if kind == "few":
+            return torch.randint(0, 3, (total,), generator=g, device=DEV).to(torch.uint8).view(dt)
+        pool = np.array([0, 1, 127, 128, 254, 255], dtype=np.uint8)
+        return torch.from_numpy(rng.choice(pool, total)).to(DEV).view(dt)
+
+    sizes = [0, 1, 7, 33, 34, 100, 2047, 2048, 2049, 5000, -3, 40000, 70000, 5]
+    off, total = offsets_from(sizes, 5)
+    vals = torch.arange(total, dtype=torch.int32, device=DEV)
+    for kind in ("random", "few", "extreme"):
+        keys = keys_of(total, kind)
+        say(f"[8-bit {key_type} {kind}] keys={total}")
+        for largest in (True, False):
+            for det, tb in MODES:
+                for ordering in ("unsorted", "stable_sorted"):
+                    check(keys, vals, off, 33, key_type, largest, det, tb, ordering,
+                          values_are="position")
+            check(keys, None, off, 500, key_type, largest, "gpu_to_gpu", "prefer_larger_index",
+                  "stable_sorted")
+    for sizes, k in ((rng.integers(0, 5000, 2100), 64), (rng.integers(100000, 300000, 3), 3000)):
+        off, total = offsets_from(sizes)
+        keys = keys_of(total, "random")
+        vals = torch.arange(total, dtype=torch.int32, device=DEV)
+        wide = torch.arange(total, dtype=torch.int64, device=DEV) | (5 << 33)
+        kseg = torch.from_numpy(rng.integers(-1, k + 5, len(sizes)).astype(np.int32)).to(DEV)
+        for det, tb in (MODES[0], MODES[3], MODES[4]):
+            check(keys, vals, off, k, key_type, True, det, tb, "unsorted", values_are="position",
+                  k_per_segment=kseg)
+        check(keys, wide, off, k, key_type, False, "gpu_to_gpu", "prefer_smaller_index",
+              "stable_sorted")

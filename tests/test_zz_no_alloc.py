@@ -116,21 +116,23 @@ def test_noalloc_first_case_against_the_oracle():
 
 
 def test_noalloc_refuses_a_plan_larger_than_the_buffer():
-    # Six segments split over the device with k = 4096: about 37 MiB of
-    # per-workgroup candidate slots, more than the static buffer's 32 MiB.
-    keys, vals, off = problem(6, 20000, 16)
-    ok, ov = outputs(6, 4096)
+    # 500 segments with k = 2048, split two ways when their sizes are unknown:
+    # about 41 MB of per-workgroup candidate slots, more than the static
+    # buffer's 32 MiB.
+    keys, vals, off = problem(500, 10000, 16)
+    ok, ov = outputs(500, 2048)
     s = torch.cuda.current_stream().cuda_stream
-    rc = call(st.raw_call_ex_noalloc, keys, vals, off, 4096, ok, ov, "max", "gpu_to_gpu",
+    rc = call(st.raw_call_ex_noalloc, keys, vals, off, 2048, ok, ov, "max", "gpu_to_gpu",
               "prefer_smaller_index", "unsorted", s)
     torch.cuda.synchronize()
     assert rc == 4
     assert st.library().segtopk_status_string(4).startswith(b"request needs more scratch")
     assert bool((ok == KEY_CANARY).all()) and bool((ov == VAL_CANARY).all())
-    # The same request with a hint that rules out splitting takes no scratch.
-    assert call(st.raw_call_ex_noalloc, keys, vals, off, 4096, ok, ov, "max", "gpu_to_gpu",
-                "prefer_smaller_index", "unsorted", s, hint=20000) == 0
+    # The same request with a hint that rules out splitting needs only the
+    # segment order (2 KB).
+    assert call(st.raw_call_ex_noalloc, keys, vals, off, 2048, ok, ov, "max", "gpu_to_gpu",
+                "prefer_smaller_index", "unsorted", s, hint=10000) == 0
     torch.cuda.synchronize()
-    ref = reference(keys, vals, off, 4096, "max", "gpu_to_gpu", "prefer_smaller_index",
+    ref = reference(keys, vals, off, 2048, "max", "gpu_to_gpu", "prefer_smaller_index",
                     "unsorted")
     assert same((ok, ov), ref, "unsorted")
