@@ -630,6 +630,7 @@ struct Share {
     uint32_t *gearly;    // global: the segment's shared histogram, or nullptr
     uint32_t *glast;     // LDS: this workgroup's contributions so far
     uint32_t wave;       // this wave's index in the workgroup
+    uint32_t spread;     // the segment's workgroups span every XCD
 };
 
 struct Pass0 {
@@ -751,7 +752,24 @@ __device__ __forceinline__ Pass0 wave_pass0(uint32_t *hist, uint2 *stash, uint32
         L.template load_body<true>(0, ln, raw);
     else
         L.template load_chunk<true>(0, ln, raw, vidx);
+    // Slice mode: a read of the shared histogram issued in the previous
+    // iteration (1: into registers, 2: to be read in two rounds now).
+    GlobalRun gr;
+    uint32_t pending = 0;
     for (uint32_t c = 0; c < nch; ++c) {
+        if constexpr (SLICED) {
+            if (pending) {
+                const Kth g = pending == 1u ? find_global_scan(gr, target)
+                                            : wave_find_global(sh.gearly, r.R + 1, target);
+                pending = 0;
+                if (g.found && g.b < r.R) {
+                    r.R = g.b;
+                    below = 0;
+                    pf = prefilter<KT, LARGEST>(r.R);
+                    if (ln == 0) atomicMin(sh.rg, g.b);
+                }
+            }
+        }
         uint32_t cur[K], cv[Rg::kU];
 #pragma unroll
         for (int j = 0; j < K; ++j) cur[j] = raw[j];
@@ -768,16 +786,55 @@ __device__ __forceinline__ Pass0 wave_pass0(uint32_t *hist, uint2 *stash, uint32
             if (c + 1 < nch) L.template load_chunk<true>(c + 1, ln, raw, vidx);  // prefetch
         }
 
-        // This wave's turn to read the segment's shared histogram: the reads
-        // go out now, behind the prefetch, and are used at the end of the
-        // iteration, when the prefetch has to be waited for anyway.
-        const bool find_turn =
-            sh.gearly && bounded && c >= 2u && ((c - 2u - 2u * sh.wave) & 7u) == 0u;
-        const bool find_regs = find_turn && r.R < 512u;
-        GlobalRun gr;
-        if (find_regs) find_global_issue(sh.gearly, r.R + 1, gr);
+        // Shared bounds, two ways.  A segment spread over every XCD reads the
+        // shared histogram through device-wide atomics that take long: each
+        // wave's turn issues the reads now, behind the prefetch, and uses them
+        // at the top of the next iteration, where the prefetch has to be
+        // waited for anyway.  A segment on one XCD reads it in place (the
+        // reads are short, and this form measured faster there).
+        if constexpr (SLICED) {
+            if (sh.gearly && sh.spread && bounded && c >= 2u &&
+                ((c - 2u - 2u * sh.wave) & 7u) == 0u) {
+                pending = r.R < 512u ? 1u : 2u;
+                if (pending == 1u) find_global_issue(sh.gearly, r.R + 1, gr);
+            }
+        }
+        if (sh.gearly && !(SLICED && sh.spread)) {
+            const uint32_t rg = __builtin_amdgcn_readfirstlane(
+                __hip_atomic_load(sh.rg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+            if (rg < r.R) {
+                r.R = rg;
+                below = 0;  // not known for a bound found elsewhere
+                bounded = true;
+                pf = prefilter<KT, LARGEST>(r.R);
+            }
+            if (bounded && c >= 1) {
+                if (sh.wave == 0 && ((c - 1) & 7u) == 0u) {
+                    // Add what the workgroup's histogram gained since the last
+                    // time.  Later bounds are never looser, so every bucket
+                    // read back from glast was written the first time.
+                    const bool first = !contributed;
+                    contributed = true;
+                    for (uint32_t b = ln; b <= r.R; b += kWave) {
+                        const uint32_t v = hist[b];
+                        const uint32_t l = first ? 0u : sh.glast[b];
+                        if (v > l) atomicAdd(&sh.gearly[b], v - l);
+                        if (first || v != l) sh.glast[b] = v;
+                    }
+                }
+                if (((c - 2u - 2u * sh.wave) & 7u) == 0u && c >= 2u) {
+                    const Kth g = wave_find_global(sh.gearly, r.R + 1, target);
+                    if (g.found && g.b < r.R) {
+                        r.R = g.b;
+                        below = 0;
+                        pf = prefilter<KT, LARGEST>(r.R);
+                        if (ln == 0) atomicMin(sh.rg, g.b);
+                    }
+                }
+            }
+        }
 
-        if (sh.gearly) {
+        if (SLICED && sh.gearly && sh.spread) {
             // Adopt a tighter bound found by another wave of this workgroup
             // (one lane reads it, so that the wave agrees on it).
             const uint32_t rg = __builtin_amdgcn_readfirstlane(
@@ -803,164 +860,151 @@ __device__ __forceinline__ Pass0 wave_pass0(uint32_t *hist, uint2 *stash, uint32
             }
         }
 
-        do {  // the chunk; `break` ends it early
-            if (!bounded) {
-                // No bound yet: count every key, then look for the bound.
-                bool any = false;
+        if (!bounded) {
+            // No bound yet: count every key, then look for the bound.
+            bool any = false;
 #pragma unroll
-                for (int u = 0; u < Rg::kU; ++u)
+            for (int u = 0; u < Rg::kU; ++u)
 #pragma unroll
-                    for (int e = 0; e < V; ++e) {
-                        if (cv[u] != kNone) {
-                            atomicAdd(&hist[rank0<KT, LARGEST>(Key<KT>::ord(Rg::key_at(cur, u * V + e)))], 1u);
-                            any = true;
-                        }
+                for (int e = 0; e < V; ++e) {
+                    if (cv[u] != kNone) {
+                        atomicAdd(&hist[rank0<KT, LARGEST>(Key<KT>::ord(Rg::key_at(cur, u * V + e)))], 1u);
+                        any = true;
                     }
-                if (s0) {
-                    atomicAdd(&hist[rank0<KT, LARGEST>(Key<KT>::ord(sx))], 1u);
-                    any = true;
                 }
-                r.defer = c + 1;
-                if (!__any(any)) break;
-                wave_sync();
-                const Kth f = wave_find(hist, kBuckets, target);
-                if (!f.found) break;
-                r.R = f.b;
-                below = f.before;
-                bounded = true;
-                pf = prefilter<KT, LARGEST>(r.R);
-                // Stash this chunk's keys within the bound from the registers,
-                // if they fit; earlier chunks stay deferred.
-                const bool sin = s0 && pf_key(pf, sx);
-                uint32_t cnt = sin ? 1u : 0u;
-#pragma unroll
-                for (int u = 0; u < Rg::kU; ++u)
-#pragma unroll
-                    for (int e = 0; e < V; ++e)
-                        cnt += (cv[u] != kNone && pf_key(pf, Rg::key_at(cur, u * V + e))) ? 1u : 0u;
-                const uint32_t incl = wave_incl_sum(cnt);
-                const uint32_t total = wave_bcast(incl, kWave - 1);
-                if (r.count + total > cap) break;  // the stash is empty: defer the chunk
-                uint32_t pos = r.count + incl - cnt;
-                if (sin) stash[pos++] = make_uint2(sx, si);
-#pragma unroll
-                for (int u = 0; u < Rg::kU; ++u)
-#pragma unroll
-                    for (int e = 0; e < V; ++e) {
-                        const uint32_t x = Rg::key_at(cur, u * V + e);
-                        if (cv[u] != kNone && pf_key(pf, x))
-                            stash[pos++] = make_uint2(x, cv[u] + (uint32_t)e);
-                    }
-                r.count += total;
-                if constexpr (kLazy) flushed = r.count;  // counted above already
-                r.defer = c;
-                break;
+            if (s0) {
+                atomicAdd(&hist[rank0<KT, LARGEST>(Key<KT>::ord(sx))], 1u);
+                any = true;
             }
-
-            // Bounded: one min or max per key decides whether any key of the
-            // chunk can be within the bound; only then are the keys tested one
-            // by one, and only a key position in which some lane passes takes
-            // the exact rank test, the count and the stash push.
-            // 16-bit keys test load by load, so that only the loads in which
-            // some lane passes have their key positions tested one by one.
-            bool lp[Rg::kU];
-            if constexpr (kLazy) {
-                bool cp = s0 && pf_key(pf, sx);
+            r.defer = c + 1;
+            if (!__any(any)) continue;
+            wave_sync();
+            const Kth f = wave_find(hist, kBuckets, target);
+            if (!f.found) continue;
+            r.R = f.b;
+            below = f.before;
+            bounded = true;
+            pf = prefilter<KT, LARGEST>(r.R);
+            // Stash this chunk's keys within the bound from the registers,
+            // if they fit; earlier chunks stay deferred.
+            const bool sin = s0 && pf_key(pf, sx);
+            uint32_t cnt = sin ? 1u : 0u;
 #pragma unroll
-                for (int u = 0; u < Rg::kU; ++u) {
-                    lp[u] = pf_chunk<KT>(pf, *reinterpret_cast<const uint32_t(*)[4]>(&cur[u * 4]));
-                    cp = cp | lp[u];
-                }
-                if (!__any(cp)) break;
-            } else {
-                const bool cp = pf_chunk<KT>(pf, cur);
-                const bool sp = s0 && pf_key(pf, sx);
-                if (!__any(cp || sp)) break;
-            }
-            bool ok = true;
-            auto take = [&](uint32_t x, uint32_t idx, bool valid) {
-                const bool pv = valid && pf_key(pf, x);
-                if (!__any(pv)) return;
-                if constexpr (kLazy) {
-                    // The bound test is exact, so pv already means rank <= R.
-                    if (ok) {
-                        const uint64_t m = __ballot(pv);
-                        const uint32_t n = (uint32_t)__popcll(m);
-                        if (r.count + n <= cap) {
-                            if (pv) stash[r.count + lanes_below(m)] = make_uint2(x, idx);
-                            r.count += n;
-                            return;
-                        }
-                        ok = false;
-                    }
-                    // Not stashed (the stash is dropped after this chunk): count now.
-                    const uint32_t rk = rank0<KT, LARGEST>(Key<KT>::ord(x));
-                    if (pv) atomicAdd(&hist[rk], 1u);
-                    nbelow += (uint32_t)__popcll(__ballot(pv && rk < r.R));
-                    return;
-                }
-                const uint32_t rk = rank0<KT, LARGEST>(Key<KT>::ord(x));
-                const bool ex = pv && rk <= r.R;
-                if (ex) atomicAdd(&hist[rk], 1u);
-                nbelow += (uint32_t)__popcll(__ballot(ex && (!kLazy || rk < r.R)));
-                if (ok) ok = wave_push<KT, LARGEST>(stash, cap, r.count, pf, ex, x, idx);
-            };
-            take(sx, si, s0);
-#pragma unroll
-            for (int u = 0; u < Rg::kU; ++u) {
-                if constexpr (kLazy)
-                    if (!__any(lp[u])) continue;
+            for (int u = 0; u < Rg::kU; ++u)
 #pragma unroll
                 for (int e = 0; e < V; ++e)
-                    take(Rg::key_at(cur, u * V + e), cv[u] + (uint32_t)e, cv[u] != kNone);
-            }
-            if constexpr (kLazy) {
-                // One place for the deferred counts: before a drop, before a
-                // compaction (the stash half full and the bound tighter than at
-                // the last one), and when the bound may move (unflushed entries
-                // bound the uncounted keys before its bucket).
-                const bool half = r.count > cap / 2u && r.R < compR;
-                if (!ok || half ||
-                    below + (uint32_t)kWaves * (nbelow + (r.count - flushed)) >= target) {
-                    flush();
-                    if (ok && half) {
-                        wave_sync();
-                        r.count = wave_compact<KT, LARGEST>(stash, r.count, pf);
-                        flushed = r.count;
-                        compR = r.R;
-                    }
+                    cnt += (cv[u] != kNone && pf_key(pf, Rg::key_at(cur, u * V + e))) ? 1u : 0u;
+            const uint32_t incl = wave_incl_sum(cnt);
+            const uint32_t total = wave_bcast(incl, kWave - 1);
+            if (r.count + total > cap) continue;  // the stash is empty: defer the chunk
+            uint32_t pos = r.count + incl - cnt;
+            if (sin) stash[pos++] = make_uint2(sx, si);
+#pragma unroll
+            for (int u = 0; u < Rg::kU; ++u)
+#pragma unroll
+                for (int e = 0; e < V; ++e) {
+                    const uint32_t x = Rg::key_at(cur, u * V + e);
+                    if (cv[u] != kNone && pf_key(pf, x))
+                        stash[pos++] = make_uint2(x, cv[u] + (uint32_t)e);
                 }
-            }
-            if (!ok) {
-                // The stash is full even within the bound: drop it and read this
-                // and every earlier chunk again later.
-                r.count = 0;
-                r.defer = c + 1;
-                if constexpr (kLazy) flushed = 0;
-            }
-            if (nbelow != 0 && (!kLazy || below + (uint32_t)kWaves * nbelow >= target)) {
-                // The bound may move: recompute it from everything counted.
-                nbelow = 0;
-                wave_sync();
-                const Kth f = wave_find(hist, r.R + 1, target);
-                if (f.found) {
-                    below = f.before;
-                    if (f.b < r.R) {
-                        r.R = f.b;
-                        pf = prefilter<KT, LARGEST>(r.R);
-                    }
-                }
-            }
-        } while (false);
+            r.count += total;
+            if constexpr (kLazy) flushed = r.count;  // counted above already
+            r.defer = c;
+            continue;
+        }
 
-        if (find_turn) {
-            const Kth g = find_regs ? find_global_scan(gr, target)
-                                    : wave_find_global(sh.gearly, r.R + 1, target);
-            if (g.found && g.b < r.R) {
-                r.R = g.b;
-                below = 0;
-                pf = prefilter<KT, LARGEST>(r.R);
-                if (ln == 0) atomicMin(sh.rg, g.b);
+        // Bounded: one min or max per key decides whether any key of the
+        // chunk can be within the bound; only then are the keys tested one
+        // by one, and only a key position in which some lane passes takes
+        // the exact rank test, the count and the stash push.
+        // 16-bit keys test load by load, so that only the loads in which
+        // some lane passes have their key positions tested one by one.
+        bool lp[Rg::kU];
+        if constexpr (kLazy) {
+            bool cp = s0 && pf_key(pf, sx);
+#pragma unroll
+            for (int u = 0; u < Rg::kU; ++u) {
+                lp[u] = pf_chunk<KT>(pf, *reinterpret_cast<const uint32_t(*)[4]>(&cur[u * 4]));
+                cp = cp | lp[u];
+            }
+            if (!__any(cp)) continue;
+        } else {
+            const bool cp = pf_chunk<KT>(pf, cur);
+            const bool sp = s0 && pf_key(pf, sx);
+            if (!__any(cp || sp)) continue;
+        }
+        bool ok = true;
+        auto take = [&](uint32_t x, uint32_t idx, bool valid) {
+            const bool pv = valid && pf_key(pf, x);
+            if (!__any(pv)) return;
+            if constexpr (kLazy) {
+                // The bound test is exact, so pv already means rank <= R.
+                if (ok) {
+                    const uint64_t m = __ballot(pv);
+                    const uint32_t n = (uint32_t)__popcll(m);
+                    if (r.count + n <= cap) {
+                        if (pv) stash[r.count + lanes_below(m)] = make_uint2(x, idx);
+                        r.count += n;
+                        return;
+                    }
+                    ok = false;
+                }
+                // Not stashed (the stash is dropped after this chunk): count now.
+                const uint32_t rk = rank0<KT, LARGEST>(Key<KT>::ord(x));
+                if (pv) atomicAdd(&hist[rk], 1u);
+                nbelow += (uint32_t)__popcll(__ballot(pv && rk < r.R));
+                return;
+            }
+            const uint32_t rk = rank0<KT, LARGEST>(Key<KT>::ord(x));
+            const bool ex = pv && rk <= r.R;
+            if (ex) atomicAdd(&hist[rk], 1u);
+            nbelow += (uint32_t)__popcll(__ballot(ex && (!kLazy || rk < r.R)));
+            if (ok) ok = wave_push<KT, LARGEST>(stash, cap, r.count, pf, ex, x, idx);
+        };
+        take(sx, si, s0);
+#pragma unroll
+        for (int u = 0; u < Rg::kU; ++u) {
+            if constexpr (kLazy)
+                if (!__any(lp[u])) continue;
+#pragma unroll
+            for (int e = 0; e < V; ++e)
+                take(Rg::key_at(cur, u * V + e), cv[u] + (uint32_t)e, cv[u] != kNone);
+        }
+        if constexpr (kLazy) {
+            // One place for the deferred counts: before a drop, before a
+            // compaction (the stash half full and the bound tighter than at
+            // the last one), and when the bound may move (unflushed entries
+            // bound the uncounted keys before its bucket).
+            const bool half = r.count > cap / 2u && r.R < compR;
+            if (!ok || half ||
+                below + (uint32_t)kWaves * (nbelow + (r.count - flushed)) >= target) {
+                flush();
+                if (ok && half) {
+                    wave_sync();
+                    r.count = wave_compact<KT, LARGEST>(stash, r.count, pf);
+                    flushed = r.count;
+                    compR = r.R;
+                }
+            }
+        }
+        if (!ok) {
+            // The stash is full even within the bound: drop it and read this
+            // and every earlier chunk again later.
+            r.count = 0;
+            r.defer = c + 1;
+            if constexpr (kLazy) flushed = 0;
+        }
+        if (nbelow != 0 && (!kLazy || below + (uint32_t)kWaves * nbelow >= target)) {
+            // The bound may move: recompute it from everything counted.
+            nbelow = 0;
+            wave_sync();
+            const Kth f = wave_find(hist, r.R + 1, target);
+            if (f.found) {
+                below = f.before;
+                if (f.b < r.R) {
+                    r.R = f.b;
+                    pf = prefilter<KT, LARGEST>(r.R);
+                }
             }
         }
     }
@@ -2125,6 +2169,7 @@ __global__ __launch_bounds__(kThreads, (topk_waves<KT, U>())) void topk_kernel(P
                       ? reinterpret_cast<uint32_t *>(stash + p.stash_cap + p.out_cap)
                       : nullptr;
     share.wave = w;
+    share.spread = p.spread;
     const Pass0 r0 = wave_pass0_stash<KT, LARGEST, U, SLICED>(sh.hist, stash + w * capw, capw, p.keys_in,
                                                    sg.begin, wlo, whi, sg.k_i, share);
     if (ln == 0) {
