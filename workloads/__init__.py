@@ -11,7 +11,7 @@ bytes.  Keys are returned as torch tensors holding the raw bit patterns the
 library reads: float32, bfloat16, or int32 bits for uint32 keys.  Values are
 int32 tensors holding the source index inside each segment.
 
-Workloads (one call each; see the design doc for the reading of each description):
+Workloads (one call each; the seeds and shapes are in WORKLOADS below):
   uniform_f32   S x L float32 keys uniform in [-1, 1), keys only
   normal_f32    S x L float32 keys ~ N(0, 1), index values
   quantized     S variable-size segments (sizes uniform in [1, max_len]),
