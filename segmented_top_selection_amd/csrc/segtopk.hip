@@ -427,13 +427,17 @@ int make_plan(const Request &r, int dev, Plan &pl) {
     if (stash_cap < (split ? 2048u : 1024u)) stash_cap = split ? 2048u : 1024u;
     // The sliced kernel also keeps a workgroup's shared-histogram
     // contributions in LDS (kBuckets words after the stash and the staging).
+    // The kernels for 16-bit keys with one workgroup per segment keep rings
+    // of loads waiting to be tested there instead.
     const uint64_t extra = split ? 4u * kBuckets : 0u;
-    while (stash_cap > 1024 && 8 * (stash_cap + out_cap) + extra > kMaxDynLds) stash_cap >>= 1;
-    if (8 * (stash_cap + out_cap) + extra > kMaxDynLds) return SEGTOPK_NOT_SUPPORTED;
+    const uint64_t ring = key_bytes(type) == 2 ? kRingBytes : 0u;
+    const uint64_t more = extra > ring ? extra : ring;
+    while (stash_cap > 1024 && 8 * (stash_cap + out_cap) + more > kMaxDynLds) stash_cap >>= 1;
+    if (8 * (stash_cap + out_cap) + more > kMaxDynLds) return SEGTOPK_NOT_SUPPORTED;
     p.stash_cap = (uint32_t)stash_cap;
     p.out_cap = (uint32_t)out_cap;
-    pl.lds = 8 * (size_t)(stash_cap + out_cap);
-    const size_t lds_sliced = pl.lds + (size_t)extra;
+    pl.lds = 8 * (size_t)(stash_cap + out_cap) + (size_t)ring;
+    const size_t lds_sliced = 8 * (size_t)(stash_cap + out_cap) + (size_t)extra;
     pl.largest = r.direction == SEGTOPK_MAX;
     pl.type = type;
     pl.pairs = pairs;

@@ -23,6 +23,10 @@ constexpr uint32_t kNone = 0xFFFFFFFFu; // "no element" / sort padding
 constexpr int kSplitU = 8;               // loads per lane per chunk when segments are split
 constexpr size_t kMaxDynLds = 120 * 1024;
 constexpr uint32_t kMaxWgPerSeg = 1024;  // slices of one segment (the last arriver's prefix table fits LDS)
+// 16-bit keys with one workgroup per segment: per wave, a ring of this many
+// 16-byte loads (and their element indices) waiting to be tested key by key.
+constexpr uint32_t kRingLoads = 128;
+constexpr size_t kRingBytes = 4 * kRingLoads * (16 + 4);  // four waves
 
 // ---------------------------------------------------------------------------
 // Kernel arguments.

@@ -631,6 +631,8 @@ struct Share {
     uint32_t *glast;     // LDS: this workgroup's contributions so far
     uint32_t wave;       // this wave's index in the workgroup
     uint32_t spread;     // the segment's workgroups span every XCD
+    uint4 *ring;         // LDS: this wave's ring of loads to test (16-bit keys)
+    uint32_t *ring_idx;  // LDS: element index of each ring entry's first key
 };
 
 struct Pass0 {
@@ -740,6 +742,61 @@ __device__ __forceinline__ Pass0 wave_pass0(uint32_t *hist, uint2 *stash, uint32
             nbelow += (uint32_t)__popcll(__ballot(rk < r.R));
         }
         flushed = r.count;
+    };
+
+    // 16-bit keys with one workgroup per segment: about 0.4% of the keys of
+    // a long stream pass the running bound, so most 16-byte loads of a wave
+    // hold a passing key in some lane, yet few lanes do.  Testing such a load
+    // key position by key position costs the wave eight tests for one or two
+    // keys.  Instead the lanes whose load may pass append it (16 bytes and
+    // the element index of its first key) to the wave's ring in LDS, and
+    // once a wave's worth of loads wait, every lane tests one of them key by
+    // key.  A load waiting in the ring is tested later under a bound that can
+    // only be tighter, and its keys are counted when they are stashed (or at
+    // once if the stash is full), so the histogram still only undercounts.
+    constexpr bool kRing = Key<KT>::kBytes == 2 && !SLICED;
+    uint32_t rhead = 0, rtail = 0;  // ring entries [rhead, rtail) wait
+    // The deferred-count form of a key's test and stash push (see flush()).
+    auto lazy_take = [&](uint32_t x, uint32_t idx, bool valid, bool &okr) {
+        const bool pv = valid && pf_key(pf, x);
+        if (!__any(pv)) return;
+        if (okr) {
+            const uint64_t m = __ballot(pv);
+            const uint32_t n = (uint32_t)__popcll(m);
+            if (r.count + n <= cap) {
+                if (pv) stash[r.count + lanes_below(m)] = make_uint2(x, idx);
+                r.count += n;
+                return;
+            }
+            okr = false;
+        }
+        // Not stashed (the stash is dropped after this chunk): count now.
+        const uint32_t rk = rank0<KT, LARGEST>(Key<KT>::ord(x));
+        if (pv) atomicAdd(&hist[rk], 1u);
+        nbelow += (uint32_t)__popcll(__ballot(pv && rk < r.R));
+    };
+    // Tests the n (at most 64) oldest loads of the ring, one per lane.
+    auto drain = [&](uint32_t n, bool &okr) {
+        wave_sync();
+        const bool act = ln < n;
+        const uint32_t slot = (rhead + ln) & (kRingLoads - 1u);
+        uint32_t d[4] = {0u, 0u, 0u, 0u};
+        uint32_t vi = 0;
+        if (act) {
+            const uint4 v = sh.ring[slot];
+            d[0] = v.x;
+            d[1] = v.y;
+            d[2] = v.z;
+            d[3] = v.w;
+            vi = sh.ring_idx[slot];
+        }
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+            const uint32_t dw = d[(e * Key<KT>::kBytes) >> 2];
+            const uint32_t x = Key<KT>::kBytes == 4 ? dw : ((e & 1) ? (dw >> 16) : (dw & 0xFFFFu));
+            lazy_take(x, vi + (uint32_t)e, act, okr);
+        }
+        rhead += n;
     };
 
     // The unaligned head and tail ride along with chunk 0.
@@ -961,14 +1018,36 @@ __device__ __forceinline__ Pass0 wave_pass0(uint32_t *hist, uint2 *stash, uint32
             nbelow += (uint32_t)__popcll(__ballot(ex && (!kLazy || rk < r.R)));
             if (ok) ok = wave_push<KT, LARGEST>(stash, cap, r.count, pf, ex, x, idx);
         };
-        take(sx, si, s0);
+        if constexpr (kRing) {
+            lazy_take(sx, si, s0, ok);
 #pragma unroll
-        for (int u = 0; u < Rg::kU; ++u) {
-            if constexpr (kLazy)
-                if (!__any(lp[u])) continue;
+            for (int u = 0; u < Rg::kU; ++u) {
+                const bool f = lp[u] && cv[u] != kNone;
+                const uint64_t m = __ballot(f);
+                if (m == 0) continue;
+                if (f) {
+                    const uint32_t slot = (rtail + lanes_below(m)) & (kRingLoads - 1u);
+                    sh.ring[slot] = make_uint4(cur[u * 4], cur[u * 4 + 1], cur[u * 4 + 2], cur[u * 4 + 3]);
+                    sh.ring_idx[slot] = cv[u];
+                }
+                rtail += (uint32_t)__popcll(m);
+                if (rtail - rhead >= (uint32_t)kWave) drain(kWave, ok);
+            }
+            // A drop of the stash follows: every waiting load is tested (and
+            // its passing keys counted) first.
+            if (!ok)
+                while (rtail != rhead)
+                    drain(rtail - rhead < (uint32_t)kWave ? rtail - rhead : (uint32_t)kWave, ok);
+        } else {
+            take(sx, si, s0);
 #pragma unroll
-            for (int e = 0; e < V; ++e)
-                take(Rg::key_at(cur, u * V + e), cv[u] + (uint32_t)e, cv[u] != kNone);
+            for (int u = 0; u < Rg::kU; ++u) {
+                if constexpr (kLazy)
+                    if (!__any(lp[u])) continue;
+#pragma unroll
+                for (int e = 0; e < V; ++e)
+                    take(Rg::key_at(cur, u * V + e), cv[u] + (uint32_t)e, cv[u] != kNone);
+            }
         }
         if constexpr (kLazy) {
             // One place for the deferred counts: before a drop, before a
@@ -1006,6 +1085,19 @@ __device__ __forceinline__ Pass0 wave_pass0(uint32_t *hist, uint2 *stash, uint32
                     pf = prefilter<KT, LARGEST>(r.R);
                 }
             }
+        }
+    }
+    if constexpr (kRing) {
+        // The loads still waiting; if their keys do not fit, the stash is
+        // dropped and every chunk is read again later.
+        bool ok = true;
+        while (rtail != rhead)
+            drain(rtail - rhead < (uint32_t)kWave ? rtail - rhead : (uint32_t)kWave, ok);
+        if (!ok) {
+            flush();
+            r.count = 0;
+            r.defer = nch;
+            flushed = 0;
         }
     }
     if constexpr (kLazy) flush();
@@ -2170,6 +2262,16 @@ __global__ __launch_bounds__(kThreads, (topk_waves<KT, U>())) void topk_kernel(P
                       : nullptr;
     share.wave = w;
     share.spread = p.spread;
+    if constexpr (Key<KT>::kBytes == 2 && !SLICED) {
+        // After the stash and the output staging: four rings of loads, then
+        // their element indices.
+        uint4 *rb = reinterpret_cast<uint4 *>(stash + p.stash_cap + p.out_cap);
+        share.ring = rb + w * kRingLoads;
+        share.ring_idx = reinterpret_cast<uint32_t *>(rb + kWaves * kRingLoads) + w * kRingLoads;
+    } else {
+        share.ring = nullptr;
+        share.ring_idx = nullptr;
+    }
     const Pass0 r0 = wave_pass0_stash<KT, LARGEST, U, SLICED>(sh.hist, stash + w * capw, capw, p.keys_in,
                                                    sg.begin, wlo, whi, sg.k_i, share);
     if (ln == 0) {
