@@ -316,7 +316,7 @@ struct Plan {
     bool pairs, wide_values;
     // scratch: the order array (order), or the slice-mode layout (sliced)
     bool order, sliced;
-    size_t scratch_bytes, zero_words, data_off, n_hist, info_words;
+    size_t scratch_bytes, zero_words, data_off, n_hist, n_early, info_words;
 };
 
 int validate(const Request &r) {
@@ -401,7 +401,7 @@ int make_plan(const Request &r, int dev, Plan &pl) {
         pl.grid = (uint32_t)S;
         pl.variant = kVariantOne;
         pl.order = pl.sliced = false;
-        pl.scratch_bytes = pl.zero_words = pl.data_off = pl.n_hist = pl.info_words = 0;
+        pl.scratch_bytes = pl.zero_words = pl.data_off = pl.n_hist = pl.n_early = pl.info_words = 0;
         return SEGTOPK_OK;
     }
 
@@ -471,12 +471,14 @@ int make_plan(const Request &r, int dev, Plan &pl) {
     // (not all within one chunk by the hint): process the largest first.
     pl.order = split && P == 1 && S >= (uint64_t)kOrderMinSegments && !(hint && hint <= 8192);
     pl.sliced = P > 1;
-    pl.scratch_bytes = pl.zero_words = pl.data_off = pl.n_hist = pl.info_words = 0;
+    pl.scratch_bytes = pl.zero_words = pl.data_off = pl.n_hist = pl.n_early = pl.info_words = 0;
     if (pl.order) {
         pl.scratch_bytes = S * sizeof(uint32_t);
     } else if (pl.sliced) {
+        // A segment spread over every XCD keeps one shared histogram per XCD.
         pl.n_hist = S * kBuckets;
-        pl.zero_words = 2 * pl.n_hist + S;  // merged and shared histograms, tickets
+        pl.n_early = (p.spread ? 8u : 1u) * pl.n_hist;
+        pl.zero_words = pl.n_hist + pl.n_early + S;  // merged and shared histograms, tickets
         pl.info_words = S * P * 4;
         const size_t cum_words = S * P * kBuckets;
         size_t bytes = (pl.zero_words + pl.info_words + cum_words) * 4;
@@ -496,7 +498,7 @@ void bind_scratch(Plan &pl, void *ws) {
     } else if (pl.sliced) {
         p.ws_hist = wsw;
         p.ws_early = wsw + pl.n_hist;
-        p.ws_ticket = wsw + 2 * pl.n_hist;
+        p.ws_ticket = wsw + pl.n_hist + pl.n_early;
         p.ws_slot_info = wsw + pl.zero_words;
         p.ws_slot_cum = wsw + pl.zero_words + pl.info_words;
         p.ws_slot_data = reinterpret_cast<uint2 *>(static_cast<char *>(ws) + pl.data_off);

@@ -48,7 +48,7 @@ struct Params {
     uint32_t wg_per_seg;     // workgroups per segment (1: one workgroup each)
     uint32_t min_slice;      // smallest slice a segment is split into
     uint32_t *ws_hist;       // [segments][kBuckets]    merged pass-0 histograms
-    uint32_t *ws_early;      // [segments][kBuckets]    early snapshots (bound sharing)
+    uint32_t *ws_early;      // [segments][1 or 8][kBuckets] shared histograms (bound sharing)
     uint32_t *ws_ticket;     // [segments]              arrival tickets
     uint32_t *ws_slot_info;  // [segments][P][4]        (count, overflowed, bound, -)
     uint32_t *ws_slot_cum;   // [segments][P][kBuckets] entries with rank <= r

@@ -1865,11 +1865,12 @@ __device__ __forceinline__ void slice_last(Shared &sh, uint2 *stash, uint2 *outb
     if constexpr (CLEAN) {
         // Every other slice has taken its ticket: none reads these any more.
         uint4 *m4 = reinterpret_cast<uint4 *>(p.ws_hist + (size_t)s * kBuckets);
-        uint4 *e4 = reinterpret_cast<uint4 *>(p.ws_early + (size_t)s * kBuckets);
-        for (uint32_t i = threadIdx.x; i < (uint32_t)kBuckets / 4; i += kThreads) {
+        const uint32_t ne = p.spread ? 8u : 1u;  // shared histograms of the segment
+        uint4 *e4 = reinterpret_cast<uint4 *>(p.ws_early + (size_t)s * ne * kBuckets);
+        for (uint32_t i = threadIdx.x; i < (uint32_t)kBuckets / 4; i += kThreads)
             m4[i] = make_uint4(0u, 0u, 0u, 0u);
+        for (uint32_t i = threadIdx.x; i < ne * (uint32_t)kBuckets / 4; i += kThreads)
             e4[i] = make_uint4(0u, 0u, 0u, 0u);
-        }
         if (threadIdx.x == 0) p.ws_ticket[s] = 0u;
     }
     const Kth ks = wave_find(sh.hist, kBuckets, sg.k_i);  // alike in every wave
@@ -2254,7 +2255,13 @@ __global__ __launch_bounds__(kThreads, (topk_waves<KT, U>())) void topk_kernel(P
     __syncthreads();
     Share share;
     share.rg = &sh.rg;
-    share.gearly = ps > 1 ? p.ws_early + (size_t)s * kBuckets : nullptr;
+    // A segment spread over every XCD has one shared histogram per XCD (the
+    // dispatcher deals workgroups to XCDs in turn): eight times fewer
+    // workgroups add to and read each one.  Any of them gives a valid bound,
+    // since each undercounts the segment.
+    share.gearly = ps > 1 ? p.ws_early + ((size_t)s * (p.spread ? 8u : 1u) + (p.spread ? (b & 7u) : 0u)) *
+                                             kBuckets
+                          : nullptr;
     // The sliced variant keeps the workgroup's contributions in dynamic LDS
     // after the stash and the output staging.
     share.glast = (SLICED && ps > 1)
