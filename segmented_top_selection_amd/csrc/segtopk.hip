@@ -316,7 +316,7 @@ struct Plan {
     bool pairs, wide_values;
     // scratch: the order array (order), or the slice-mode layout (sliced)
     bool order, sliced;
-    size_t scratch_bytes, zero_words, data_off, n_hist, n_early, info_words;
+    size_t scratch_bytes, zero_words, data_off, n_hist, n_early, info_words, stage_off;
 };
 
 int validate(const Request &r) {
@@ -401,7 +401,7 @@ int make_plan(const Request &r, int dev, Plan &pl) {
         pl.grid = (uint32_t)S;
         pl.variant = kVariantOne;
         pl.order = pl.sliced = false;
-        pl.scratch_bytes = pl.zero_words = pl.data_off = pl.n_hist = pl.n_early = pl.info_words = 0;
+        pl.scratch_bytes = pl.zero_words = pl.data_off = pl.n_hist = pl.n_early = pl.info_words = pl.stage_off = 0;
         return SEGTOPK_OK;
     }
 
@@ -471,7 +471,7 @@ int make_plan(const Request &r, int dev, Plan &pl) {
     // (not all within one chunk by the hint): process the largest first.
     pl.order = split && P == 1 && S >= (uint64_t)kOrderMinSegments && !(hint && hint <= 8192);
     pl.sliced = P > 1;
-    pl.scratch_bytes = pl.zero_words = pl.data_off = pl.n_hist = pl.n_early = pl.info_words = 0;
+    pl.scratch_bytes = pl.zero_words = pl.data_off = pl.n_hist = pl.n_early = pl.info_words = pl.stage_off = 0;
     if (pl.order) {
         pl.scratch_bytes = S * sizeof(uint32_t);
     } else if (pl.sliced) {
@@ -485,6 +485,10 @@ int make_plan(const Request &r, int dev, Plan &pl) {
         bytes = (bytes + 255) & ~(size_t)255;
         pl.data_off = bytes;
         pl.scratch_bytes = bytes + S * P * (size_t)stash_cap * sizeof(uint2);
+        if (p.spread) {
+            pl.stage_off = pl.scratch_bytes;
+            pl.scratch_bytes += S * (size_t)kStageCap * sizeof(uint2);
+        }
     }
     return SEGTOPK_OK;
 }
@@ -502,6 +506,8 @@ void bind_scratch(Plan &pl, void *ws) {
         p.ws_slot_info = wsw + pl.zero_words;
         p.ws_slot_cum = wsw + pl.zero_words + pl.info_words;
         p.ws_slot_data = reinterpret_cast<uint2 *>(static_cast<char *>(ws) + pl.data_off);
+        p.ws_stage = pl.stage_off ? reinterpret_cast<uint2 *>(static_cast<char *>(ws) + pl.stage_off)
+                                  : nullptr;
     }
 }
 

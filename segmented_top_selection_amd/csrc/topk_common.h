@@ -27,6 +27,9 @@ constexpr uint32_t kMaxWgPerSeg = 1024;  // slices of one segment (the last arri
 // 16-byte loads (and their element indices) waiting to be tested key by key.
 constexpr uint32_t kRingLoads = 128;
 constexpr size_t kRingBytes = 4 * kRingLoads * (16 + 4);  // four waves
+// A segment spread over every XCD: room for this many entries of its k-th
+// bucket, copied in a row by the last workgroup when it narrows the bucket.
+constexpr uint32_t kStageCap = 32768;
 
 // ---------------------------------------------------------------------------
 // Kernel arguments.
@@ -53,6 +56,7 @@ struct Params {
     uint32_t *ws_slot_info;  // [segments][P][4]        (count, overflowed, bound, -)
     uint32_t *ws_slot_cum;   // [segments][P][kBuckets] entries with rank <= r
     uint2 *ws_slot_data;     // [segments][P][stash_cap] candidates sorted by rank
+    uint2 *ws_stage;         // [segments][kStageCap] bucket b*'s entries in a row (spread plans), or nullptr
     const uint32_t *order;   // [segments] processing order (one workgroup each), or nullptr
     uint32_t spread;         // workgroup b serves segment b / P, slice b % P (small batches)
     uint32_t vindex;         // write the source index as the value (no gather)

@@ -1671,7 +1671,7 @@ struct alignas(16) Shared {
     uint32_t wbad[kWaves];
     uint32_t wdefer[kWaves];
     uint32_t rg;
-    uint32_t last, total, any_bad, nfront, ntie;  // the last arriver's state
+    uint32_t last, total, any_bad, nfront, ntie, nstage;  // the last arriver's state
     uint32_t ncand;                               // candidates listed (one-chunk segments)
     uint32_t kb, kbefore, kcount, pad;            // the k-th bucket found by wave 0 (same)
 };
@@ -1876,22 +1876,27 @@ __device__ __forceinline__ void slice_last(Shared &sh, uint2 *stash, uint2 *outb
     const Kth ks = wave_find(sh.hist, kBuckets, sg.k_i);  // alike in every wave
     __syncthreads();
 
-    // Per slot, the prefix up to b*, laid end to end (exclusive prefix).
+    // Per slot, the prefix up to b*, laid end to end (exclusive prefix).  The
+    // slots' counts are read by every thread at once (one round of loads),
+    // then scanned by wave 0.
     uint32_t *pre = sh.hist;
+    for (uint32_t qi = threadIdx.x; qi < ps; qi += kThreads) {
+        uint32_t c = kNone;  // a slice that lost candidates
+        if (info[4 * qi + 1] == 0) {
+            c = slot_cum[(size_t)qi * kBuckets + ks.b];
+            c = c < p.stash_cap ? c : p.stash_cap;
+        }
+        pre[qi] = c;
+    }
+    __syncthreads();
     if (w == 0) {
         uint32_t total = 0;
         bool any_bad = false;
         for (uint32_t base = 0; base < ps; base += kWave) {
             const uint32_t qi = base + ln;
-            uint32_t c = 0;
-            bool bd = false;
-            if (qi < ps) {
-                bd = info[4 * qi + 1] != 0;
-                if (!bd) {
-                    c = slot_cum[(size_t)qi * kBuckets + ks.b];
-                    c = c < p.stash_cap ? c : p.stash_cap;
-                }
-            }
+            uint32_t c = qi < ps ? pre[qi] : 0u;
+            const bool bd = c == kNone;
+            if (bd) c = 0;
             any_bad = any_bad || __any(bd);
             const uint32_t incl = wave_incl_sum(c);
             if (qi < ps) pre[qi] = total + incl - c;
@@ -1903,6 +1908,7 @@ __device__ __forceinline__ void slice_last(Shared &sh, uint2 *stash, uint2 *outb
             sh.any_bad = any_bad ? 1u : 0u;
             sh.nfront = 0;
             sh.ntie = 0;
+            sh.nstage = 0;
         }
     }
     __syncthreads();
@@ -1912,19 +1918,34 @@ __device__ __forceinline__ void slice_last(Shared &sh, uint2 *stash, uint2 *outb
     // Entries [base + u * 64 + lane] of the slots' prefixes laid end to end,
     // 8 per lane, spread over the waves by the caller.
     constexpr int kB = 8;
+    // The slot of entry j is the last a with pre[a] <= j; the eight searches
+    // of a lane step together (eight LDS reads in flight per step).
+    uint32_t top = 1;
+    while (top * 2u <= ps) top *= 2u;  // the largest power of two <= ps
     auto load_batch = [&](uint32_t base, uint2 (&e)[kB]) {
+        uint32_t a[kB], pa[kB];
+#pragma unroll
+        for (int u = 0; u < kB; ++u) {
+            a[u] = 0;
+            pa[u] = 0;  // pre[0]
+        }
+        for (uint32_t h = top; h != 0; h >>= 1) {
+#pragma unroll
+            for (int u = 0; u < kB; ++u) {
+                const uint32_t j = base + (uint32_t)u * kWave + ln;
+                const uint32_t m = a[u] + h;
+                const uint32_t v = m < ps ? pre[m] : kNone;
+                if (v <= j) {
+                    a[u] = m;
+                    pa[u] = v;
+                }
+            }
+        }
 #pragma unroll
         for (int u = 0; u < kB; ++u) {
             const uint32_t j = base + (uint32_t)u * kWave + ln;
             e[u] = make_uint2(0u, kNone);
-            if (j < total) {
-                uint32_t a = 0, z = ps;  // pre[a] <= j < pre[z]
-                while (z - a > 1) {
-                    const uint32_t m = (a + z) >> 1;
-                    if (pre[m] <= j) a = m; else z = m;
-                }
-                e[u] = slot_data[(size_t)a * p.stash_cap + (j - pre[a])];
-            }
+            if (j < total) e[u] = slot_data[(size_t)a[u] * p.stash_cap + (j - pa[u])];
         }
     };
     // Rank of the key's next digit below the pass-0 digit (best first).
@@ -1941,10 +1962,23 @@ __device__ __forceinline__ void slice_last(Shared &sh, uint2 *stash, uint2 *outb
     // counted from the slots by the four waves, narrows it (the better
     // sub-buckets' keys become winners).  The count lives above the slot
     // prefix table, which takes at most kMaxWgPerSeg + 1 words.
+    // With room for them in the staging area (a segment spread over every
+    // XCD), the same pass also writes the keys of better buckets, which win
+    // whatever the narrowing gives, and copies bucket b*'s entries in a row,
+    // so that the pass after the narrowing reads them from there instead of
+    // searching the slots again.
     bool refine = false;
     uint32_t dstar = 0, front = ks.before;
     Kth kf = ks;
     Prefix pf0 = pass0_prefix<KT, LARGEST>(ks.b);
+    // Unsorted 4-byte values: the passes write each winner's source index in
+    // its value slot, and one gather at the end replaces the indices by the
+    // values, so that no batch waits for its values' loads.
+    Params q = p;
+    const bool late_vals = p.vals_in != nullptr && p.vindex == 0u && outbuf == nullptr;
+    if (late_vals) q.vindex = 1u;
+    const bool stage = !fast && sh.any_bad == 0 && p.ws_stage != nullptr && ks.count <= kStageCap;
+    uint2 *stg = stage ? p.ws_stage + (size_t)s * kStageCap : nullptr;
     if (!fast && sh.any_bad == 0) {
         uint32_t *sub = sh.hist + kBuckets - kSubN;
         for (uint32_t i = threadIdx.x; i < kSubN; i += kThreads) sub[i] = 0u;
@@ -1952,10 +1986,42 @@ __device__ __forceinline__ void slice_last(Shared &sh, uint2 *stash, uint2 *outb
         for (uint32_t base = w * kB * kWave; base < total; base += kWaves * kB * kWave) {
             uint2 e[kB];
             load_batch(base, e);
+            bool bet[kB], tie[kB];
+            uint32_t nb = 0, nt = 0;
 #pragma unroll
-            for (int u = 0; u < kB; ++u)
-                if (e[u].y != kNone && rank0<KT, LARGEST>(Key<KT>::ord(e[u].x)) == ks.b)
-                    atomicAdd(&sub[sub_rank(e[u].x)], 1u);
+            for (int u = 0; u < kB; ++u) {
+                const uint32_t rk =
+                    e[u].y != kNone ? rank0<KT, LARGEST>(Key<KT>::ord(e[u].x)) : kNone;
+                bet[u] = rk < ks.b;
+                tie[u] = rk == ks.b;
+                if (tie[u]) atomicAdd(&sub[sub_rank(e[u].x)], 1u);
+                if (stage) {
+                    nb += (uint32_t)__popcll(__ballot(bet[u]));
+                    nt += (uint32_t)__popcll(__ballot(tie[u]));
+                }
+            }
+            if (!stage) continue;
+            uint32_t fb = 0, tb = 0;
+            if (ln == 0) {
+                fb = nb ? atomicAdd(&sh.nfront, nb) : 0u;
+                tb = nt ? atomicAdd(&sh.nstage, nt) : 0u;
+            }
+            fb = wave_bcast(fb, 0);
+            tb = wave_bcast(tb, 0);
+            uint32_t fpos[kB];
+#pragma unroll
+            for (int u = 0; u < kB; ++u) {
+                const uint64_t mb = __ballot(bet[u]);
+                const uint64_t mt = __ballot(tie[u]);
+                const uint32_t pb = fb + lanes_below(mb);
+                const uint32_t pt = tb + lanes_below(mt);
+                fb += (uint32_t)__popcll(mb);
+                tb += (uint32_t)__popcll(mt);
+                fpos[u] = (bet[u] && pb < ks.before) ? pb : kNone;
+                if (outbuf && fpos[u] != kNone) outbuf[pb] = e[u];
+                if (tie[u] && pt < kStageCap) stg[pt] = e[u];
+            }
+            if (!outbuf) write_batch<KT, kB>(q, sg, fpos, e);
         }
         __syncthreads();
         const Kth f2 = wave_find(sub, kSubN, sg.k_i - ks.before);  // alike in every wave
@@ -1971,12 +2037,24 @@ __device__ __forceinline__ void slice_last(Shared &sh, uint2 *stash, uint2 *outb
         }
         __syncthreads();
     }
+    // Staged and narrowed: bucket b*'s entries in a row, the better buckets'
+    // keys written already.
+    const bool staged = refine && stage;
+    const uint32_t nread = staged ? (sh.nstage < kStageCap ? sh.nstage : kStageCap) : total;
     if (fast || refine) {
         // Batches of 8 entries per lane, spread over the waves; positions
         // come from LDS counters, one reservation per batch and kind.
-        for (uint32_t base = w * kB * kWave; base < total; base += kWaves * kB * kWave) {
+        for (uint32_t base = w * kB * kWave; base < nread; base += kWaves * kB * kWave) {
             uint2 e[kB];
-            load_batch(base, e);
+            if (staged) {
+#pragma unroll
+                for (int u = 0; u < kB; ++u) {
+                    const uint32_t j = base + (uint32_t)u * kWave + ln;
+                    e[u] = j < nread ? stg[j] : make_uint2(0u, kNone);
+                }
+            } else {
+                load_batch(base, e);
+            }
             uint32_t nb = 0, nt = 0;
             bool bet[kB], tie[kB];
 #pragma unroll
@@ -2009,14 +2087,35 @@ __device__ __forceinline__ void slice_last(Shared &sh, uint2 *stash, uint2 *outb
                 if (outbuf && fpos[u] != kNone) outbuf[pb] = e[u];
                 if (tie[u] && pt < p.stash_cap) stash[pt] = e[u];
             }
-            if (!outbuf) write_batch<KT, kB>(p, sg, fpos, e);
+            if (!outbuf) write_batch<KT, kB>(q, sg, fpos, e);
         }
     }
     __syncthreads();
     if (fast || refine) {
         // The four waves finish together on the list of keys at the prefix.
-        block_finish<KT, LARGEST>(sh, outbuf, p, sg, stash,
+        block_finish<KT, LARGEST>(sh, outbuf, q, sg, stash,
                                   sh.ntie < p.stash_cap ? sh.ntie : p.stash_cap, kf, front, pf0);
+        if (late_vals) {
+            // Every winner is written: replace the indices by the values, 8
+            // per thread in flight.
+            __syncthreads();
+            const size_t row = (size_t)sg.row * p.k;
+            for (uint32_t o0 = threadIdx.x; o0 < sg.k_i; o0 += 8u * kThreads) {
+                uint32_t v[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const uint32_t o = o0 + (uint32_t)u * kThreads;
+                    v[u] = o < sg.k_i ? p.vals_out[row + o] : kNone;
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u) v[u] = v[u] < sg.n ? p.vals_in[sg.begin + v[u]] : kNone;
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const uint32_t o = o0 + (uint32_t)u * kThreads;
+                    if (o < sg.k_i) p.vals_out[row + o] = v[u];
+                }
+            }
+        }
         return;
     }
     if (w != 0) return;
@@ -2324,7 +2423,7 @@ __global__ __launch_bounds__(kThreads, (topk_waves<KT, U>())) void topk_kernel(P
         }
         if (!sh.last) return;
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        slice_last<KT, LARGEST, SLICED>(sh, stash, outbuf, p, sg, s, P, ps, slice);
+        if constexpr (SLICED) slice_last<KT, LARGEST, SLICED>(sh, stash, outbuf, p, sg, s, P, ps, slice);
         return;
     }
 
@@ -2439,7 +2538,7 @@ __global__ __launch_bounds__(kThreads, (topk_waves<KT, U>())) void topk_kernel(P
     __syncthreads();  // pairs with the one the other waves wait in
     if (!last) return;
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    slice_last<KT, LARGEST, SLICED>(sh, stash, outbuf, p, sg, s, P, ps, slice);
+    if constexpr (SLICED) slice_last<KT, LARGEST, SLICED>(sh, stash, outbuf, p, sg, s, P, ps, slice);
 }
 
 // Dynamic LDS above 64 KiB has to be allowed per kernel, once per device.
