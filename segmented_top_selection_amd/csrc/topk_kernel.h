@@ -848,10 +848,15 @@ __device__ __forceinline__ Pass0 wave_pass0(uint32_t *hist, uint2 *stash, uint32
         // wave's turn issues the reads now, behind the prefetch, and uses them
         // at the top of the next iteration, where the prefetch has to be
         // waited for anyway.  A segment on one XCD reads it in place (the
-        // reads are short, and this form measured faster there).
+        // reads are short, and this form measured faster there).  Spread
+        // segments also share half as often (every 16 chunks of a wave): 768
+        // workgroups' device-wide reads and adds cost more stream time than
+        // the tighter bound saves (one segment of 2^28 keys: 383 -> 346 us),
+        // while a segment on one XCD needs the 8-chunk rhythm to keep its
+        // slices' stashes from overflowing.
         if constexpr (SLICED) {
             if (sh.gearly && sh.spread && bounded && c >= 2u &&
-                ((c - 2u - 2u * sh.wave) & 7u) == 0u) {
+                ((c - 2u - 2u * sh.wave) & 15u) == 0u) {
                 pending = r.R < 512u ? 1u : 2u;
                 if (pending == 1u) find_global_issue(sh.gearly, r.R + 1, gr);
             }
@@ -902,7 +907,7 @@ __device__ __forceinline__ Pass0 wave_pass0(uint32_t *hist, uint2 *stash, uint32
                 bounded = true;
                 pf = prefilter<KT, LARGEST>(r.R);
             }
-            if (bounded && c >= 1 && sh.wave == 0 && ((c - 1) & 7u) == 0u) {
+            if (bounded && c >= 1 && sh.wave == 0 && ((c - 1) & 15u) == 0u) {
                 // Add what the workgroup's histogram gained since the last
                 // time.  Later bounds are never looser, so every bucket read
                 // back from glast was written the first time.
