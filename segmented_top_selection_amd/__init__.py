@@ -201,8 +201,10 @@ def batched_topk(keys: torch.Tensor, segment_offsets: torch.Tensor, k: int, *,
     k = int(k)
     if k < 0:
         raise ValueError("k must be >= 0")
-    keys = keys.reshape(-1).contiguous()
-    segment_offsets = segment_offsets.contiguous()
+    if keys.dim() != 1 or not keys.is_contiguous():
+        keys = keys.reshape(-1).contiguous()
+    if not segment_offsets.is_contiguous():
+        segment_offsets = segment_offsets.contiguous()
     s = segment_offsets.numel() - 1
     if out_keys is None:
         out_keys = torch.empty((s, k), dtype=keys.dtype, device=dev)
@@ -214,7 +216,8 @@ def batched_topk(keys: torch.Tensor, segment_offsets: torch.Tensor, k: int, *,
         vbytes = values.element_size()
         if vbytes not in (4, 8):
             raise TypeError("values must be a 4- or 8-byte payload")
-        values = values.reshape(-1).contiguous()
+        if values.dim() != 1 or not values.is_contiguous():
+            values = values.reshape(-1).contiguous()
         if values.numel() < keys.numel():
             raise ValueError("values must hold one item per key")
         if out_values is None:
