@@ -315,6 +315,39 @@ __device__ __forceinline__ uint32_t wave_bcast(uint32_t x, uint32_t src) {
     return (uint32_t)__builtin_amdgcn_readlane((int)x, (int)src);
 }
 
+// Wave-wide OR and AND (every lane of the wave active): row scans with DPP
+// shifts, then the four rows' last lanes combined on the scalar unit.
+__device__ __forceinline__ void wave_or_and(uint32_t &o, uint32_t &a) {
+    o |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)o, 0x111, 0xF, 0xF, false);   // row_shr:1
+    a &= (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)a, 0x111, 0xF, 0xF, false);
+    o |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)o, 0x112, 0xF, 0xF, false);   // row_shr:2
+    a &= (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)a, 0x112, 0xF, 0xF, false);
+    o |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)o, 0x114, 0xF, 0xF, false);   // row_shr:4
+    a &= (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)a, 0x114, 0xF, 0xF, false);
+    o |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)o, 0x118, 0xF, 0xF, false);   // row_shr:8
+    a &= (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)a, 0x118, 0xF, 0xF, false);
+    o = wave_bcast(o, 15) | wave_bcast(o, 31) | wave_bcast(o, 47) | wave_bcast(o, 63);
+    a = wave_bcast(a, 15) & wave_bcast(a, 31) & wave_bcast(a, 47) & wave_bcast(a, 63);
+}
+
+// Key bits [lo, hi) on which every candidate at the prefix agrees (their OR
+// and AND over those bits are equal) need no digit pass: they extend the
+// prefix at once.  `o` and `a` are the OR and AND of those candidates' ordered
+// keys; lowers hi to just above the highest bit on which they differ.
+__device__ __forceinline__ void skip_common_bits(uint32_t o, uint32_t a, int &hi, uint32_t &kmask,
+                                                 uint32_t &kpref) {
+    if (hi <= 0) return;
+    const uint32_t low = hi >= 32 ? ~0u : ((1u << hi) - 1u);
+    const uint32_t diff = (o ^ a) & low;
+    const int hb = diff ? 32 - __clz((int)diff) : 0;
+    if (hb >= hi) return;
+    const uint32_t keep = hb == 0 ? 0u : ((1u << hb) - 1u);
+    const uint32_t m = low & ~keep;
+    kpref |= a & m;
+    kmask |= m;
+    hi = hb;
+}
+
 // Orders this wave's LDS accesses across lanes (lanes run in lockstep; this
 // keeps the compiler from moving LDS traffic across the point).
 __device__ __forceinline__ void wave_sync() {
@@ -1541,18 +1574,24 @@ __device__ __forceinline__ void wave_finish(uint32_t *hist, uint2 *outbuf, const
     uint32_t front = k0.before;
     bool done = (k0.count == krem);
 
-    // Key digits.
+    // Key digits.  The first pass also takes the OR and AND of the keys at
+    // the prefix: digits on which they all agree (heavy ties) are then taken
+    // without a pass.
+    bool first = true;
     while (!done && hi > 0) {
         const int w = hi < kLaterDigit ? hi : kLaterDigit;
         const int sh = hi - w;
         const uint32_t nb = 1u << w;
         wave_clear(hist, nb);
         wave_sync();
+        uint32_t co = 0, ca = ~0u;
         cand.visit([&](uint32_t r, uint32_t idx, bool act) {
             const uint32_t o = Key<KT>::ord(r);
             if (act && (o & kmask) == kpref) {
                 const uint32_t d = (o >> sh) & (nb - 1);
                 atomicAdd(&hist[LARGEST ? nb - 1 - d : d], 1u);
+                co |= o;
+                ca &= o;
             }
         });
         wave_sync();
@@ -1563,6 +1602,11 @@ __device__ __forceinline__ void wave_finish(uint32_t *hist, uint2 *outbuf, const
         kmask |= (nb - 1) << sh;
         done = (f.count == krem);
         hi = sh;
+        if (first && !done) {
+            wave_or_and(co, ca);
+            skip_common_bits(co, ca, hi, kmask, kpref);
+        }
+        first = false;
         wave_sync();
     }
 
@@ -1735,20 +1779,37 @@ __device__ __forceinline__ void block_finish(Shared &sh, uint2 *outbuf, const Pa
     uint32_t front = k0.before;
     bool done = (k0.count == krem);
 
-    // Key digits.
+    // Key digits.  The first pass also takes the OR and AND of the keys at
+    // the prefix (in the histogram's last two words): digits on which they
+    // all agree (heavy ties) are then taken without a pass.
+    bool first = true;
     while (!done && hi > 0) {
         const int wd = hi < kLaterDigit ? hi : kLaterDigit;
         const int sh_ = hi - wd;
         const uint32_t nb = 1u << wd;
         for (uint32_t i = t; i < nb; i += kThreads) hist[i] = 0u;
+        if (t == 0) {
+            hist[kBuckets - 2] = 0u;
+            hist[kBuckets - 1] = ~0u;
+        }
         __syncthreads();
+        uint32_t co = 0, ca = ~0u;
         visit([&](uint32_t r, uint32_t idx, bool act) {
             const uint32_t o = Key<KT>::ord(r);
             if (act && (o & kmask) == kpref) {
                 const uint32_t d = (o >> sh_) & (nb - 1);
                 atomicAdd(&hist[LARGEST ? nb - 1 - d : d], 1u);
+                co |= o;
+                ca &= o;
             }
         });
+        if (first) {
+            wave_or_and(co, ca);
+            if (ln == 0) {
+                atomicOr(&hist[kBuckets - 2], co);
+                atomicAnd(&hist[kBuckets - 1], ca);
+            }
+        }
         __syncthreads();
         const Kth f = wave_find(hist, nb, krem);
         krem -= f.before;
@@ -1757,6 +1818,8 @@ __device__ __forceinline__ void block_finish(Shared &sh, uint2 *outbuf, const Pa
         kmask |= (nb - 1) << sh_;
         done = (f.count == krem);
         hi = sh_;
+        if (first && !done) skip_common_bits(hist[kBuckets - 2], hist[kBuckets - 1], hi, kmask, kpref);
+        first = false;
         __syncthreads();
     }
 

@@ -234,6 +234,32 @@ def test_one_segment_of_2_28_keys(det, tb):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("det,tb", [MODES[0], MODES[4]])
+def test_one_segment_wide_kth_bucket(det, tb):
+    """One segment of 2^27 uniform uint32 keys, k = 2048: the k-th pass-0
+    bucket holds about 65,536 keys, more than the staging area of a spread
+    segment, so the last workgroup narrows it by reading the slots twice."""
+    n, k = 1 << 27, 2048
+    g = torch.Generator(device=DEV)
+    g.manual_seed(2027)
+    keys = torch.randint(-(2 ** 31), 2 ** 31, (n,), generator=g, device=DEV,
+                         dtype=torch.int64).to(torch.int32)
+    off = torch.tensor([0, n], dtype=torch.int64, device=DEV)
+    vals = torch.arange(n, dtype=torch.int32, device=DEV)
+    say(f"[one segment 2^27 u32] {det}/{tb}")
+    out_k = torch.empty((1, k), dtype=torch.int32, device=DEV)
+    out_v = torch.empty((1, k), dtype=torch.int32, device=DEV)
+    import segmented_top_selection_amd as st
+    st.batched_topk(keys, off, k, values=vals, largest=True, determinism=det, tie_break=tb,
+                    ordering="unsorted", key_type="u32", out_keys=out_k, out_values=out_v)
+    torch.cuda.synchronize()
+    kn = keys.cpu().numpy().view(np.uint32)
+    _closed_form_check(kn, out_v.cpu().numpy()[0].astype(np.int64),
+                       out_k.cpu().numpy()[0].view(np.uint32), k, True, det, tb)
+    del keys, vals
+    torch.cuda.empty_cache()
+
+
 def _keys64(total, key_type, gen, rng, kind):
     """64-bit keys: random full-width bits, a few tied levels, or extremes."""
     if kind == "random":
