@@ -170,7 +170,8 @@ def batched_topk(keys: torch.Tensor, segment_offsets: torch.Tensor, k: int, *,
                      min(max(k_per_segment[i], 0), k, n_i) items; k stays the
                      row stride of the outputs
     max_segment_size optional host-side hint: no segment is longer (it steers
-                     the launch plan only)
+                     the launch plan only); without one, the number of keys
+                     is passed, which bounds every segment of valid offsets
     Defaults follow the requirements page: gpu_to_gpu determinism,
     prefer_smaller_index ties, stable_sorted output.
     Returns (out_keys, out_values) of shape (num_segments, k); out_values is
@@ -237,13 +238,12 @@ def batched_topk(keys: torch.Tensor, segment_offsets: torch.Tensor, k: int, *,
         stream = torch.cuda.current_stream(dev)
     args = (DIRECTIONS["max" if largest else "min"], DETERMINISM[determinism],
             TIE_BREAK[tie_break], ORDERING[ordering], stream.cuda_stream)
-    if kseg_ptr is None and max_segment_size is None and vbytes == 4:
-        rc = raw_call(keys.data_ptr(), out_keys.data_ptr(), KEY_TYPES[key_type], vin, vout,
-                      segment_offsets.data_ptr(), s, k, *args)
-    else:
-        rc = raw_call_ex(keys.data_ptr(), out_keys.data_ptr(), KEY_TYPES[key_type], vin, vout,
-                         vbytes, segment_offsets.data_ptr(), s, k, kseg_ptr,
-                         int(max_segment_size or 0), *args)
+    # Offsets index the keys, so no segment of a valid call is longer than
+    # the key count: a hint the plan can use when the caller gives none (a
+    # batch of small segments then needs no splitting and no scratch).
+    hint = keys.numel() if max_segment_size is None else int(max_segment_size)
+    rc = raw_call_ex(keys.data_ptr(), out_keys.data_ptr(), KEY_TYPES[key_type], vin, vout,
+                     vbytes, segment_offsets.data_ptr(), s, k, kseg_ptr, hint, *args)
     if rc != 0:
         raise SegTopKError(rc)
     return out_keys, (out_values if values is not None else None)
