@@ -238,7 +238,7 @@ int batched_topk_ex(const segtopk_keys *keys, const segtopk_values *values, int3
  * nothing (for instance 500 segments with k = 2048 of unknown sizes, split
  * two ways: about 41 MB of per-workgroup candidate slots; a max_segment_size
  * hint that rules out splitting avoids that scratch).  32 x 4 Mi keys with
- * k = 2048 (30.5 MiB) or one segment with k = 2048 (30 MiB) fit.
+ * k = 2048 (30.5 MiB) or one segment with k = 2048 (30.3 MiB) fit.
  */
 #define SEGTOPK_STATIC_SCRATCH_BYTES (32u << 20)
 int batched_topk_ex_noalloc(const segtopk_keys *keys, const segtopk_values *values,
