@@ -1982,6 +1982,24 @@ __device__ __forceinline__ void slice_last(Shared &sh, uint2 *stash, uint2 *outb
     __syncthreads();
     const uint32_t total = sh.total;
     bool fast = sh.any_bad == 0 && ks.count <= p.stash_cap;
+    // Bucket b* too large for the LDS list, with room to stage it in a row.
+    const bool stage = !fast && sh.any_bad == 0 && p.ws_stage != nullptr && ks.count <= kStageCap;
+
+    // The slot of every prefix entry, when the table fits: in the words that
+    // kept this workgroup's shared-histogram contributions (free after the
+    // stream; 2 * kBuckets entries), or in the stash when bucket b* is staged
+    // (the pass that reads the slots then writes no LDS list).  Else each
+    // entry's slot is found by binary search over the prefixes.
+    uint16_t *owner = nullptr;
+    if (total <= 2u * kBuckets)
+        owner = reinterpret_cast<uint16_t *>(stash + p.stash_cap + p.out_cap);
+    else if (stage && total <= 4u * p.stash_cap)
+        owner = reinterpret_cast<uint16_t *>(stash);
+    if (owner) {
+        for (uint32_t a = threadIdx.x; a < ps; a += kThreads)
+            for (uint32_t j = pre[a]; j < pre[a + 1]; ++j) owner[j] = (uint16_t)a;
+        __syncthreads();
+    }
 
     // Entries [base + u * 64 + lane] of the slots' prefixes laid end to end,
     // 8 per lane, spread over the waves by the caller.
@@ -1991,6 +2009,18 @@ __device__ __forceinline__ void slice_last(Shared &sh, uint2 *stash, uint2 *outb
     uint32_t top = 1;
     while (top * 2u <= ps) top *= 2u;  // the largest power of two <= ps
     auto load_batch = [&](uint32_t base, uint2 (&e)[kB]) {
+        if (owner) {
+#pragma unroll
+            for (int u = 0; u < kB; ++u) {
+                const uint32_t j = base + (uint32_t)u * kWave + ln;
+                e[u] = make_uint2(0u, kNone);
+                if (j < total) {
+                    const uint32_t a = owner[j];
+                    e[u] = slot_data[(size_t)a * p.stash_cap + (j - pre[a])];
+                }
+            }
+            return;
+        }
         uint32_t a[kB], pa[kB];
 #pragma unroll
         for (int u = 0; u < kB; ++u) {
@@ -2045,15 +2075,20 @@ __device__ __forceinline__ void slice_last(Shared &sh, uint2 *stash, uint2 *outb
     Params q = p;
     const bool late_vals = p.vals_in != nullptr && p.vindex == 0u && outbuf == nullptr;
     if (late_vals) q.vindex = 1u;
-    const bool stage = !fast && sh.any_bad == 0 && p.ws_stage != nullptr && ks.count <= kStageCap;
     uint2 *stg = stage ? p.ws_stage + (size_t)s * kStageCap : nullptr;
     if (!fast && sh.any_bad == 0) {
         uint32_t *sub = sh.hist + kBuckets - kSubN;
         for (uint32_t i = threadIdx.x; i < kSubN; i += kThreads) sub[i] = 0u;
         __syncthreads();
+        // Software-pipelined: the next batch's loads are issued before this
+        // batch's stores, so the wait for them does not also wait for the
+        // stores (the memory counter retires in order).
+        uint2 e[kB];
+        if (w * kB * kWave < total) load_batch(w * kB * kWave, e);
         for (uint32_t base = w * kB * kWave; base < total; base += kWaves * kB * kWave) {
-            uint2 e[kB];
-            load_batch(base, e);
+            uint2 en[kB];
+            const bool more = base + kWaves * kB * kWave < total;
+            if (more) load_batch(base + kWaves * kB * kWave, en);
             bool bet[kB], tie[kB];
             uint32_t nb = 0, nt = 0;
 #pragma unroll
@@ -2068,7 +2103,12 @@ __device__ __forceinline__ void slice_last(Shared &sh, uint2 *stash, uint2 *outb
                     nt += (uint32_t)__popcll(__ballot(tie[u]));
                 }
             }
-            if (!stage) continue;
+            if (!stage) {
+                if (more)
+#pragma unroll
+                    for (int u = 0; u < kB; ++u) e[u] = en[u];
+                continue;
+            }
             uint32_t fb = 0, tb = 0;
             if (ln == 0) {
                 fb = nb ? atomicAdd(&sh.nfront, nb) : 0u;
@@ -2090,6 +2130,9 @@ __device__ __forceinline__ void slice_last(Shared &sh, uint2 *stash, uint2 *outb
                 if (tie[u] && pt < kStageCap) stg[pt] = e[u];
             }
             if (!outbuf) write_batch<KT, kB>(q, sg, fpos, e);
+            if (more)
+#pragma unroll
+                for (int u = 0; u < kB; ++u) e[u] = en[u];
         }
         __syncthreads();
         const Kth f2 = wave_find(sub, kSubN, sg.k_i - ks.before);  // alike in every wave
@@ -2112,8 +2155,7 @@ __device__ __forceinline__ void slice_last(Shared &sh, uint2 *stash, uint2 *outb
     if (fast || refine) {
         // Batches of 8 entries per lane, spread over the waves; positions
         // come from LDS counters, one reservation per batch and kind.
-        for (uint32_t base = w * kB * kWave; base < nread; base += kWaves * kB * kWave) {
-            uint2 e[kB];
+        auto fetch = [&](uint32_t base, uint2 (&e)[kB]) {
             if (staged) {
 #pragma unroll
                 for (int u = 0; u < kB; ++u) {
@@ -2123,6 +2165,13 @@ __device__ __forceinline__ void slice_last(Shared &sh, uint2 *stash, uint2 *outb
             } else {
                 load_batch(base, e);
             }
+        };
+        uint2 e[kB];
+        if (w * kB * kWave < nread) fetch(w * kB * kWave, e);
+        for (uint32_t base = w * kB * kWave; base < nread; base += kWaves * kB * kWave) {
+            uint2 en[kB];
+            const bool more = base + kWaves * kB * kWave < nread;
+            if (more) fetch(base + kWaves * kB * kWave, en);
             uint32_t nb = 0, nt = 0;
             bool bet[kB], tie[kB];
 #pragma unroll
@@ -2156,6 +2205,9 @@ __device__ __forceinline__ void slice_last(Shared &sh, uint2 *stash, uint2 *outb
                 if (tie[u] && pt < p.stash_cap) stash[pt] = e[u];
             }
             if (!outbuf) write_batch<KT, kB>(q, sg, fpos, e);
+            if (more)
+#pragma unroll
+                for (int u = 0; u < kB; ++u) e[u] = en[u];
         }
     }
     __syncthreads();
