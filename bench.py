@@ -144,7 +144,10 @@ def measure(name, steps, warmup, stream_rotate=True):
     return res
 
 
-def copy_probe(mib=256, reps=5):
+COPY_PROBE_REPS = 5
+
+
+def copy_probe(mib=256, reps=COPY_PROBE_REPS):
     """A plain device-to-device copy of known size, for scaling the HBM byte
     counters (FETCH_SIZE / WRITE_SIZE) of a profiled run."""
     import torch
@@ -247,10 +250,13 @@ def traffic_from(fetch_csv, write_csv, name):
                 if "topk_kernel" in row["Kernel_Name"]:
                     topk.append(v)
                 elif "copyBuffer" in row["Kernel_Name"]:
-                    copies.append(v)
+                    copies.append((int(row["Dispatch_Id"]), v))
         if not topk or not copies:
             raise SystemExit(f"{path}: no topk_kernel or copy dispatches with {counter}")
-        return sum(topk) / len(topk), max(copies), len(topk)
+        # The probe's copies are the run's first ones (input generation may
+        # copy other buffers later).
+        probe = [v for _, v in sorted(copies)[:COPY_PROBE_REPS]]
+        return sum(topk) / len(topk), max(probe), len(topk)
 
     copy_bytes = 256 << 20
     f_kib, f_copy, n_f = per_kernel(fetch_csv, "FETCH_SIZE")
