@@ -1719,6 +1719,7 @@ struct alignas(16) Shared {
     uint32_t wcount[kWaves];
     uint32_t wbad[kWaves];
     uint32_t wdefer[kWaves];
+    uint32_t wkept[kWaves];  // entries of each wave's region within the workgroup's bound
     uint32_t rg;
     uint32_t last, total, any_bad, nfront, ntie, nstage;  // the last arriver's state
     uint32_t ncand;                               // candidates listed (one-chunk segments)
@@ -2524,6 +2525,42 @@ __global__ __launch_bounds__(kThreads, (topk_waves<KT, U>())) void topk_kernel(P
         }
         __syncthreads();
     }
+    // One workgroup per segment: every wave finds the workgroup's k-th bucket
+    // itself (alike in every wave) and keeps, in place, the entries of its
+    // own stash region within it; wave 0 then only closes the gaps between
+    // the regions.  32-bit keys only: the 16-bit kernels measured slower with
+    // it (their register budget is tighter).
+    bool pgather = false;
+    Kth kw1;
+    kw1.found = 0;
+    kw1.b = kBuckets - 1;
+    kw1.before = 0;
+    kw1.count = 0;
+    if (Key<KT>::kBytes == 4 && ps == 1) {
+        bool anybad = false;
+        for (uint32_t v = 0; v < (uint32_t)kWaves; ++v) anybad = anybad || sh.wbad[v] != 0;
+        if (!anybad) {
+            pgather = true;
+            kw1 = wave_find(sh.hist, kBuckets, sg.k_i);
+            const Prefilter pf = prefilter<KT, LARGEST>(kw1.b);
+            const uint32_t cnt = sh.wcount[w];
+            uint2 *reg = stash + w * capw;
+            uint32_t n = 0;
+            for (uint32_t base = 0; base < cnt; base += kWave) {
+                const uint32_t i = base + ln;
+                const bool act = i < cnt;
+                const uint2 e = act ? reg[i] : make_uint2(0u, 0u);
+                const bool keep = act && pf_key(pf, e.x);
+                const uint64_t m = __ballot(keep);
+                wave_sync();
+                if (keep) reg[n + lanes_below(m)] = e;
+                n += (uint32_t)__popcll(m);
+                wave_sync();
+            }
+            if (ln == 0) sh.wkept[w] = n;
+        }
+        __syncthreads();
+    }
     if (w != 0) {
         // Wave 0 gathers the workgroup's candidates; with one workgroup per
         // segment a long list is finished by the four waves together, with
@@ -2548,7 +2585,7 @@ __global__ __launch_bounds__(kThreads, (topk_waves<KT, U>())) void topk_kernel(P
     }
 
     // ---- wave 0: this workgroup's k-th bucket, then its candidates ----
-    const Kth kw = wave_find(sh.hist, kBuckets, sg.k_i);
+    const Kth kw = pgather ? kw1 : wave_find(sh.hist, kBuckets, sg.k_i);
     uint32_t R = kw.b;  // the last bucket when the range holds fewer keys
     // A bound shared by the segment's workgroups is valid for this slice too.
     if (ps > 1 && sh.rg < R) R = sh.rg;
@@ -2557,7 +2594,23 @@ __global__ __launch_bounds__(kThreads, (topk_waves<KT, U>())) void topk_kernel(P
     // Gather, in place, every stash entry with rank <= R (wave regions are
     // visited in order, so writes never pass reads).
     uint32_t ncand = 0;
-    if (!bad) {
+    if (pgather) {
+        // The regions hold only entries within the bound: move regions 1..3
+        // down behind region 0 (each destination starts before its source).
+        ncand = sh.wkept[0];
+        for (uint32_t v = 1; v < (uint32_t)kWaves; ++v) {
+            const uint32_t cnt = sh.wkept[v];
+            const uint2 *src = stash + v * capw;
+            for (uint32_t base = 0; base < cnt; base += kWave) {
+                const uint32_t i = base + ln;
+                const uint2 e = i < cnt ? src[i] : make_uint2(0u, 0u);
+                wave_sync();
+                if (i < cnt) stash[ncand + i] = e;
+                wave_sync();
+            }
+            ncand += cnt;
+        }
+    } else if (!bad) {
         const Prefilter pf = prefilter<KT, LARGEST>(R);
         for (uint32_t v = 0; v < (uint32_t)kWaves; ++v) {
             const uint32_t cnt = sh.wcount[v];
