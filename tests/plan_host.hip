@@ -91,6 +91,23 @@ int main() {
                             fail("scratch", S, k, ord, hint);
                         if (S >= 2048 && (pl.scratch_bytes != 0 || p.wg_per_seg != 1))
                             fail("many segments need no scratch", S, k, ord, hint);
+                        if (pl.sliced) {
+                            // Zeroed words: merged histograms, shared histograms
+                            // (one per XCD when spread), tickets; a spread plan
+                            // ends with the staging area of bucket b*.
+                            const uint64_t ne = (p.spread ? 8u : 1u) * (uint64_t)S * kBuckets;
+                            if (pl.n_hist != (uint64_t)S * kBuckets || pl.n_early != ne ||
+                                pl.zero_words != pl.n_hist + ne + (uint64_t)S)
+                                fail("zeroed words", S, k, ord, hint);
+                            const uint64_t slots = pl.data_off +
+                                                   (uint64_t)S * p.wg_per_seg * p.stash_cap * 8;
+                            if (p.spread ? (pl.stage_off != slots ||
+                                            pl.scratch_bytes != slots + (uint64_t)S * kStageCap * 8)
+                                         : (pl.stage_off != 0 || pl.scratch_bytes != slots))
+                                fail("slots and staging", S, k, ord, hint);
+                            if (pl.data_off < 4 * (pl.zero_words + pl.info_words) || (pl.data_off & 255))
+                                fail("layout order", S, k, ord, hint);
+                        }
                     }
     std::printf("plans checked: %ld, bad: %ld\n", g_plans, g_bad);
     return g_bad != 0;
