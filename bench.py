@@ -65,9 +65,12 @@ def workload_sizes(off_np, k):
     return int(n.sum()), int(np.minimum(n, k).sum())
 
 
-def measure(name, steps, warmup, stream_rotate=True):
+def measure(name, steps, warmup, stream_rotate=True, min_timed_ms=0.0):
     """Times `steps` back-to-back calls (after `warmup`) with HIP events on the
-    stream the library launches on.  Returns a dict of figures."""
+    stream the library launches on.  Returns a dict of figures.  With
+    `min_timed_ms`, calls far shorter than that get more steps (and warmup
+    calls), so that the timed region is not a handful of calls on a cold host
+    path."""
     import numpy as np
     import torch
 
@@ -103,6 +106,18 @@ def measure(name, steps, warmup, stream_rotate=True):
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
+    if min_timed_ms > 0:
+        t0 = time.perf_counter()
+        for i in range(3):
+            step(warmup + i)
+        torch.cuda.synchronize()
+        est_ms = (time.perf_counter() - t0) / 3 * 1e3
+        if steps * est_ms < min_timed_ms:
+            steps = min(2000, int(np.ceil(min_timed_ms / est_ms)))
+            for i in range(20):
+                step(warmup + 3 + i)
+            warmup += 23
+            torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     # Whole-job rate: `steps` back-to-back calls between two events.
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -129,7 +144,8 @@ def measure(name, steps, warmup, stream_rotate=True):
     bytes_roof = N * (sk + sv) + KK * (sk + sv)          # metric's single-read roofline
     bytes_alg = N * sk + KK * sv + KK * (sk + sv)         # what the method must move
     res = dict(
-        workload=name, segments=s, keys=N, k=w["k"], key_type=w["key_type"],
+        workload=name, segments=s, keys=N, k=w["k"], key_type=w["key_type"], steps=steps,
+        warmup=warmup,
         mode=f"{'Max' if w['largest'] else 'Min'}{'Pairs' if vals is not None else 'Keys'} "
              f"{w['determinism']}/{w['tie_break']}/{w['ordering']}",
         ms_per_step=ms, launch_ms_mean=float(np.mean(per)), launch_ms_min=min(per),
@@ -396,7 +412,7 @@ def main():
         for name in workloads.WORKLOADS:
             if name == a.workload:
                 continue
-            others[name] = measure(name, max(5, a.steps // 2), 2)
+            others[name] = measure(name, max(5, a.steps // 2), 2, min_timed_ms=5.0)
             if probe:
                 others[name]["probe_frac"] = others[name]["alg_gbs"] / probe["gbs"]
             log(name, json.dumps(others[name]))

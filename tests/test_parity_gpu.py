@@ -567,6 +567,35 @@ def test_scratch_reuse_across_streams():
             assert np.array_equal(got[0], ref[0]) and np.array_equal(got[1], ref[1]), (pi, r)
 
 
+def test_current_stream_without_argument():
+    """Without a stream argument the call goes to torch's current stream: under
+    a side stream that first spins and then writes the keys, the result must
+    be the one for the written keys (a launch on any other stream would run
+    ahead of the write and see zeros)."""
+    import segmented_top_selection_amd as st
+    sleep = getattr(torch.cuda, "_sleep", None)
+    if sleep is None:
+        pytest.skip("torch.cuda._sleep is not available")
+    gen = torch.Generator(device=DEV).manual_seed(31)
+    s, n, k = 64, 3000, 32
+    keys = random_keys(s * n, "f32", gen)
+    off = torch.arange(0, s * n + 1, n, dtype=torch.int64, device=DEV)
+    vals = index_values(off)
+    gk, gv = check(keys, vals, off, k, "f32")
+    x = torch.zeros_like(keys)
+    ok = torch.empty((s, k), dtype=keys.dtype, device=DEV)
+    ov = torch.empty((s, k), dtype=torch.int32, device=DEV)
+    side = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(side):
+        sleep(20_000_000)
+        x.copy_(keys)
+        st.batched_topk(x, off, k, values=vals, out_keys=ok, out_values=ov)
+    torch.cuda.synchronize()
+    assert np.array_equal(key_bits_np(ok).reshape(s, k), gk)
+    assert np.array_equal(ov.cpu().numpy().view(np.uint32).reshape(s, k), gv)
+
+
 def test_heavy_ties_long_segments_bf16():
     """16-bit keys whose passing keys overflow the stash: the deferred counts
     are flushed before the stash is dropped or compacted.  2048 segments (one
