@@ -101,7 +101,7 @@ def measure(name, steps, warmup, stream_rotate=True, min_timed_ms=0.0):
         st.batched_topk(kk, off, w["k"], values=vv, largest=w["largest"],
                         determinism=w["determinism"], tie_break=w["tie_break"],
                         ordering=w["ordering"], key_type=w["key_type"], out_keys=out_k,
-                        out_values=out_v)
+                        out_values=out_v, max_segment_size=w.get("max_segment_size"))
 
     for i in range(warmup):
         step(i)

@@ -466,10 +466,19 @@ int make_plan(const Request &r, int dev, Plan &pl) {
     pl.grid = (uint32_t)grid;
     pl.variant = many ? kVariantOne : (P > 1 ? kVariantSliced : kVariantSplit);
     if (P > 1) pl.lds = lds_sliced;
+    // Every segment within one load of four per lane in each wave (by the
+    // hint): the kernel that holds only that path.
+    const uint64_t small = key_bytes(type) == 2 ? kSmallKeys16 : kSmallKeys32;
+    if (P == 1 && hint && hint <= small) {
+        pl.variant = kVariantSmall;
+        pl.grid = (uint32_t)S;
+        pl.lds = 8 * (size_t)(stash_cap + out_cap);
+    }
 
     // Scratch.  One workgroup per segment for many segments of unknown sizes
     // (not all within one chunk by the hint): process the largest first.
-    pl.order = split && P == 1 && S >= (uint64_t)kOrderMinSegments && !(hint && hint <= 8192);
+    pl.order = split && P == 1 && S >= (uint64_t)kOrderMinSegments && !(hint && hint <= 8192) &&
+               pl.variant != kVariantSmall;
     pl.sliced = P > 1;
     pl.scratch_bytes = pl.zero_words = pl.data_off = pl.n_hist = pl.n_early = pl.info_words = pl.stage_off = 0;
     if (pl.order) {

@@ -21,6 +21,12 @@ constexpr int kLaterDigit = 8;          // digit width of the passes over the ca
 constexpr uint32_t kBlockFinishMin = 512;  // longer candidate lists are finished by all four waves
 constexpr uint32_t kNone = 0xFFFFFFFFu; // "no element" / sort padding
 constexpr int kSplitU = 8;               // loads per lane per chunk when segments are split
+constexpr int kSmallWaves32 = 8;        // waves per SIMD of the small-segment kernel, 32-bit keys
+constexpr int kSmallWaves16 = 6;        // and 16-bit keys
+// Longest segment of the small-segment kernel: one load of four per lane in
+// each of the four waves (16 bytes a load).
+constexpr uint32_t kSmallKeys32 = 4096;
+constexpr uint32_t kSmallKeys16 = 8192;
 constexpr size_t kMaxDynLds = 120 * 1024;
 constexpr uint32_t kMaxWgPerSeg = 1024;  // slices of one segment (the last arriver's prefix table fits LDS)
 // 16-bit keys with one workgroup per segment: per wave, a ring of this many
@@ -70,6 +76,7 @@ struct Params {
 constexpr int kVariantOne = 0;
 constexpr int kVariantSplit = 1;
 constexpr int kVariantSliced = 2;
+constexpr int kVariantSmall = 3;
 
 // Launches the top-k kernel for key type KT on `st`: grid workgroups of
 // kThreads threads with `lds` bytes of dynamic LDS, in the given variant.

@@ -2385,6 +2385,85 @@ __device__ __forceinline__ void small_block(Shared &sh, uint2 *stash, uint2 *out
     wave_finish<KT, LARGEST>(sh.hist, outbuf, p, sg, cand, kw);
 }
 
+// ---------------------------------------------------------------------------
+// Batches whose segments all fit one load of four per lane in each wave (the
+// caller's size hint says so): a kernel with only that path, so that its
+// register budget is not set by the streaming code.  A segment longer than
+// the hint is still answered exactly: every wave counts its share, and wave 0
+// finishes with passes that read the segment again.
+// ---------------------------------------------------------------------------
+template <int KT> constexpr uint32_t small_keys() { return kWaves * WaveRange<KT, 4>::kChunkKeys; }
+static_assert(small_keys<SEGTOPK_KEY_F32>() == kSmallKeys32 && small_keys<SEGTOPK_KEY_BF16>() == kSmallKeys16,
+              "the host's small-segment limits match one load of four per lane");
+template <int KT> constexpr int small_waves() { return Key<KT>::kBytes == 4 ? kSmallWaves32 : kSmallWaves16; }
+
+template <int KT, bool LARGEST>
+__global__ __launch_bounds__(kThreads, (small_waves<KT>())) void topk_small_kernel(Params p) {
+    __shared__ Shared sh;
+    extern __shared__ uint4 dyn[];
+    uint2 *stash = reinterpret_cast<uint2 *>(dyn);
+    uint2 *outbuf = p.out_cap ? stash + p.stash_cap : nullptr;
+    const uint32_t t = threadIdx.x;
+    const uint32_t w = t / kWave;
+    const uint32_t ln = lane_id();
+    const int64_t s = (int64_t)blockIdx.x;
+    if (s >= p.num_segments) return;
+
+    Seg sg;
+    sg.begin = p.offsets[s];
+    const int64_t end = p.offsets[s + 1];
+    sg.n = end > sg.begin ? (uint32_t)(end - sg.begin) : 0u;
+    sg.k_i = sg.n < p.k ? sg.n : p.k;
+    if (p.kseg) {
+        const int32_t ks = p.kseg[s];
+        const uint32_t ku = ks > 0 ? (uint32_t)ks : 0u;
+        sg.k_i = ku < sg.k_i ? ku : sg.k_i;
+    }
+    sg.row = s;
+    if (sg.k_i == 0) return;
+    if (sg.n <= sg.k_i) {
+        if (w == 0) wave_select_all<KT, LARGEST>(outbuf, p, sg);
+        return;
+    }
+    uint32_t part = (sg.n + kWaves - 1) / kWaves;
+    part = (part + 63u) & ~63u;
+    const uint32_t wlo = w * part < sg.n ? w * part : sg.n;
+    const uint32_t whi = (w + 1) * part < sg.n ? (w + 1) * part : sg.n;
+    if (part <= WaveRange<KT, 4>::kChunkKeys) {
+        small_block<KT, LARGEST, 4>(sh, stash, outbuf, p, sg, wlo, whi);
+        return;
+    }
+    // Longer than the hint: count every key, then finish from the keys.
+    for (uint32_t i = t * 4; i < (uint32_t)kBuckets; i += 4 * kThreads)
+        *reinterpret_cast<uint4 *>(&sh.hist[i]) = make_uint4(0u, 0u, 0u, 0u);
+    __syncthreads();
+    {
+        WaveRange<KT> L;
+        L.init(p.keys_in, sg.begin, wlo, whi);
+        L.for_each(ln, [&](uint32_t r, uint32_t, bool act) {
+            if (act) atomicAdd(&sh.hist[rank0<KT, LARGEST>(Key<KT>::ord(r))], 1u);
+        });
+    }
+    __syncthreads();
+    if (w != 0) return;
+    const Kth kw = wave_find(sh.hist, kBuckets, sg.k_i);
+    Cands<KT> cand;
+    cand.list = stash;
+    cand.count = 0;
+    cand.lds = false;
+    cand.keys_in = p.keys_in;
+    cand.begin = sg.begin;
+    cand.n = sg.n;
+    cand.nslices = 1;
+    cand.slice = sg.n;
+    cand.slot_info = nullptr;
+    cand.slot_cum = nullptr;
+    cand.slot_data = nullptr;
+    cand.slot_cap = p.stash_cap;
+    cand.bstar = 0;
+    wave_finish<KT, LARGEST>(sh.hist, outbuf, p, sg, cand, kw);
+}
+
 // Waves per SIMD the kernel is built for.  With 4 loads per lane: 6 for
 // 32-bit keys (at most 80 VGPRs; some spill, but the many-small-segment
 // batches this serves gain more from the extra resident workgroups than they
@@ -2715,7 +2794,9 @@ __global__ __launch_bounds__(kThreads, (topk_waves<KT, U>())) void topk_kernel(P
 }
 
 // Dynamic LDS above 64 KiB has to be allowed per kernel, once per device.
-template <typename K> hipError_t allow_lds(K kernel, size_t lds) {
+// Once per kernel and device (the flag is per template instance, that is
+// per kernel).
+template <auto Kernel> hipError_t allow_lds(size_t lds) {
     static std::atomic<uint64_t> done{0};
     if (lds <= 64 * 1024) return hipSuccess;
     int dev = 0;
@@ -2723,7 +2804,7 @@ template <typename K> hipError_t allow_lds(K kernel, size_t lds) {
     if (e != hipSuccess) return e;
     const uint64_t bit = dev < 64 ? (1ull << dev) : 0ull;
     if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
-    e = hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(Kernel),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxDynLds);
     if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_acq_rel);
     return e;
@@ -2732,8 +2813,16 @@ template <typename K> hipError_t allow_lds(K kernel, size_t lds) {
 template <int KT, bool LARGEST, int U, bool SLICED>
 hipError_t launch_u(const Params &p, uint32_t grid, size_t lds, hipStream_t st) {
     hipError_t e;
-    if ((e = allow_lds(topk_kernel<KT, LARGEST, U, SLICED>, lds)) != hipSuccess) return e;
+    if ((e = allow_lds<topk_kernel<KT, LARGEST, U, SLICED>>(lds)) != hipSuccess) return e;
     hipLaunchKernelGGL((topk_kernel<KT, LARGEST, U, SLICED>), dim3(grid), dim3(kThreads), lds, st, p);
+    return hipGetLastError();
+}
+
+template <int KT, bool LARGEST>
+hipError_t launch_small(const Params &p, uint32_t grid, size_t lds, hipStream_t st) {
+    hipError_t e;
+    if ((e = allow_lds<topk_small_kernel<KT, LARGEST>>(lds)) != hipSuccess) return e;
+    hipLaunchKernelGGL((topk_small_kernel<KT, LARGEST>), dim3(grid), dim3(kThreads), lds, st, p);
     return hipGetLastError();
 }
 
@@ -2742,6 +2831,8 @@ hipError_t launch_u(const Params &p, uint32_t grid, size_t lds, hipStream_t st) 
 template <int KT>
 hipError_t launch_topk(const Params &p, bool largest, int variant, uint32_t grid, size_t lds,
                        hipStream_t st) {
+    if (variant == kVariantSmall)
+        return largest ? launch_small<KT, true>(p, grid, lds, st) : launch_small<KT, false>(p, grid, lds, st);
     if (largest) {
         if (variant == kVariantSliced) return launch_u<KT, true, kSplitU, true>(p, grid, lds, st);
         return variant == kVariantSplit ? launch_u<KT, true, kSplitU, false>(p, grid, lds, st)

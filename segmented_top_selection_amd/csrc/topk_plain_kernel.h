@@ -318,7 +318,8 @@ __global__ __launch_bounds__(kThreads) void topk_plain_kernel(Params p) {
     }
 }
 
-template <typename K> hipError_t allow_lds_plain(K kernel, size_t lds) {
+// Once per kernel and device (the flag is per template instance).
+template <auto Kernel> hipError_t allow_lds_plain(size_t lds) {
     static std::atomic<uint64_t> done{0};
     if (lds <= 64 * 1024) return hipSuccess;
     int dev = 0;
@@ -326,7 +327,7 @@ template <typename K> hipError_t allow_lds_plain(K kernel, size_t lds) {
     if (e != hipSuccess) return e;
     const uint64_t bit = dev < 64 ? (1ull << dev) : 0ull;
     if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
-    e = hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(Kernel),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxDynLds);
     if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_acq_rel);
     return e;
@@ -339,10 +340,10 @@ hipError_t launch_topk_plain(const Params &p, bool largest, uint32_t grid, size_
                              hipStream_t st) {
     hipError_t e;
     if (largest) {
-        if ((e = allow_lds_plain(topk_plain_kernel<KT, true>, lds)) != hipSuccess) return e;
+        if ((e = allow_lds_plain<topk_plain_kernel<KT, true>>(lds)) != hipSuccess) return e;
         hipLaunchKernelGGL((topk_plain_kernel<KT, true>), dim3(grid), dim3(kThreads), lds, st, p);
     } else {
-        if ((e = allow_lds_plain(topk_plain_kernel<KT, false>, lds)) != hipSuccess) return e;
+        if ((e = allow_lds_plain<topk_plain_kernel<KT, false>>(lds)) != hipSuccess) return e;
         hipLaunchKernelGGL((topk_plain_kernel<KT, false>), dim3(grid), dim3(kThreads), lds, st, p);
     }
     return hipGetLastError();

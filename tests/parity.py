@@ -267,13 +267,13 @@ def check(keys, values, offsets, k, key_type, largest=True, determinism="gpu_to_
 
 def check_all_rows(keys, values, offsets, k, key_type, largest=True, determinism="gpu_to_gpu",
                    tie_break="prefer_smaller_index", ordering="stable_sorted", chunk_rows=1024,
-                   say=None):
+                   say=None, max_segment_size=None):
     """One GPU call over the whole batch, then EVERY row compared with the
     oracle, in blocks of ``chunk_rows`` consecutive rows so that host memory
     stays bounded (segments must be laid out in order, as every workload's
     are).  Returns the number of rows compared."""
     gk, gv = run_gpu(keys, values, offsets, k, key_type, largest, determinism, tie_break,
-                     ordering)
+                     ordering, max_segment_size=max_segment_size)
     off = offsets.cpu().numpy()
     s = off.shape[0] - 1
     for r0 in range(0, s, chunk_rows):

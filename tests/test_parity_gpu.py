@@ -124,6 +124,16 @@ def test_normal_f32_4096x4096_k64_full():
     _run_workload("normal_f32_4096x4096_k64")
 
 
+def test_normal_f32_4096x4096_k64_full_with_size_hint():
+    """The same workload with its segment length as the size hint (the
+    small-segment kernel): every row against the oracle."""
+    w, keys, vals, off = _workload("normal_f32_4096x4096_k64")
+    say(f"[headline with hint] segments={off.numel() - 1} keys={keys.numel()}")
+    n = check_all_rows(keys, vals, off, w["k"], w["key_type"], w["largest"], w["determinism"],
+                       w["tie_break"], w["ordering"], say=say, max_segment_size=4096)
+    assert n == 4096
+
+
 def test_quantized_reduced_multi_workgroup():
     # 96 segments -> several workgroups per long segment.
     _run_workload("quantized_f32_1024xU65536_k256", num_segments=96)

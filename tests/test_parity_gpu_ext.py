@@ -109,6 +109,73 @@ def test_max_segment_size_hint(hint_kind):
                       values_are="position", max_segment_size=hint)
 
 
+# Longest segment of the small-segment kernel (one load of four per lane in
+# each of four waves), per key type.
+SMALL = {"f32": 4096, "u32": 4096, "i32": 4096, "bf16": 8192, "f16": 8192, "u16": 8192,
+         "i16": 8192}
+
+
+@pytest.mark.parametrize("key_type", list(SMALL))
+def test_small_segment_kernel(key_type):
+    """A size hint within the small-segment limit selects the kernel with only
+    the one-load path: ragged sizes up to the hint in every mode and ordering,
+    tied levels (candidate lists past the stash), per-segment k, then
+    segments longer than the hint (counted and re-read by the same kernel)."""
+    lim = SMALL[key_type]
+    k = 50
+    sizes = [0, 1, 2, k - 1, k, k + 1, 3, 100, 257, 1000, lim // 2 + 1, lim - 1, lim, -5, 0,
+             33, 5, lim - 64, 4000]
+    off, total = offsets_from(sizes, 3)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(303)
+    vals = torch.arange(total, dtype=torch.int32, device=DEV)
+    say(f"[small kernel {key_type}] segments={len(sizes)} hint={lim}")
+    for levels in (None, 3):
+        keys = rand_keys(total, key_type, g, levels)
+        for largest in (True, False):
+            for det, tb in MODES:
+                for ordering in ("unsorted", "sorted", "stable_sorted"):
+                    check(keys, vals, off, k, key_type, largest, det, tb, ordering,
+                          values_are="position", max_segment_size=lim)
+    rng = np.random.default_rng(304)
+    kseg = torch.from_numpy(rng.integers(-2, k + 9, len(sizes)).astype(np.int32)).to(DEV)
+    keys = rand_keys(total, key_type, g, 6)
+    for det, tb in (MODES[0], MODES[3], MODES[4]):
+        check(keys, vals, off, k, key_type, True, det, tb, "stable_sorted", values_are="position",
+              k_per_segment=kseg, max_segment_size=lim)
+    say(f"[small kernel {key_type}] segments longer than the hint")
+    sizes = [lim + 1, 3 * lim + 17, 70000, 10, lim, 2 * lim]
+    off, total = offsets_from(sizes, 1)
+    vals = torch.arange(total, dtype=torch.int32, device=DEV)
+    for levels in (None, 5):
+        keys = rand_keys(total, key_type, g, levels)
+        for det, tb in (MODES[0], MODES[1], MODES[3], MODES[4]):
+            for ordering in ("unsorted", "stable_sorted"):
+                check(keys, vals, off, k, key_type, levels is None, det, tb, ordering,
+                      values_are="position", max_segment_size=lim)
+
+
+@pytest.mark.parametrize("key_type", ["f32", "bf16"])
+def test_small_segment_kernel_many_segments(key_type):
+    """Thousands of segments under the small-segment hint, several k."""
+    lim = SMALL[key_type]
+    rng = np.random.default_rng(305)
+    sizes = rng.choice([0, 1, 9, 64, 65, 300, 1000, lim // 2, lim - 1, lim, -2], size=3000)
+    off, total = offsets_from(sizes, 7)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(306)
+    vals = torch.arange(total, dtype=torch.int32, device=DEV)
+    for k in (1, 64, 256):
+        for levels in (None, 8):
+            keys = rand_keys(total, key_type, g, levels)
+            say(f"[small kernel many {key_type}] k={k} levels={levels}")
+            for det, tb in (MODES[0], MODES[3], MODES[4]):
+                check(keys, vals, off, k, key_type, True, det, tb, "stable_sorted",
+                      values_are="position", max_segment_size=lim)
+                check(keys, vals, off, k, key_type, False, det, tb, "unsorted",
+                      values_are="position", max_segment_size=lim)
+
+
 @pytest.mark.parametrize("plan", list(PLANS))
 def test_eight_byte_values(plan):
     rng = np.random.default_rng(55)
