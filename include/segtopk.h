@@ -191,9 +191,11 @@ int batched_topk(const segtopk_keys *keys, const segtopk_values *values,
  *   max_segment_size  host-side hint: no segment holds more keys than this;
  *                     <= 0 means unknown.  It only steers the launch plan
  *                     (whether segments are split over several workgroups,
- *                     scratch and stash sizes); a segment larger than the hint
- *                     is still served correctly, at the cost of a less suited
- *                     plan.
+ *                     scratch and stash sizes, and, at 4096 keys or fewer for
+ *                     4-byte keys and 8192 or fewer for 2-byte keys, a kernel
+ *                     built only for segments that fit one load per lane);
+ *                     a segment larger than the hint is still served
+ *                     correctly, at the cost of a less suited plan.
  *   the other arguments are batched_topk's.
  *
  * With value_bytes == 8 the selection writes each winner's source index into
