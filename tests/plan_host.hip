@@ -39,7 +39,7 @@ int main() {
     segtopk_values vals{reinterpret_cast<const void *>(0x30000), reinterpret_cast<void *>(0x40000)};
     const int64_t Ss[] = {1, 2, 3, 7, 8, 9, 100, 255, 256, 1000, 2047, 2048, 100000, INT32_MAX};
     const int64_t ks[] = {1, 2, 63, 64, 256, 4096, 4097, 65536, (1ll << 30) + 1, INT32_MAX};
-    const int64_t hints[] = {0, 1, 1000, 16384, 1ll << 20, 1ll << 40};
+    const int64_t hints[] = {0, 1, 1000, 4096, 4097, 8192, 8193, 16384, 1ll << 20, 1ll << 40};
     for (int kt : {SEGTOPK_KEY_F32, SEGTOPK_KEY_BF16, SEGTOPK_KEY_U64})
         for (int64_t S : Ss)
             for (int64_t k : ks)
@@ -91,6 +91,16 @@ int main() {
                             fail("scratch", S, k, ord, hint);
                         if (S >= 2048 && (pl.scratch_bytes != 0 || p.wg_per_seg != 1))
                             fail("many segments need no scratch", S, k, ord, hint);
+                        // The small-segment kernel: whenever the hint keeps every
+                        // segment within one load of four per lane in each wave.
+                        const uint64_t small = kt == SEGTOPK_KEY_BF16 ? kSmallKeys16 : kSmallKeys32;
+                        const bool want_small = hint > 0 && (uint64_t)hint <= small;
+                        if ((pl.variant == kVariantSmall) != want_small)
+                            fail("small-segment kernel choice", S, k, ord, hint);
+                        if (pl.variant == kVariantSmall &&
+                            (pl.grid != (uint64_t)S || pl.scratch_bytes || pl.order || pl.sliced ||
+                             p.wg_per_seg != 1 || pl.lds != 8 * ((size_t)p.stash_cap + p.out_cap)))
+                            fail("small-segment plan", S, k, ord, hint);
                         if (pl.sliced) {
                             // Zeroed words: merged histograms, shared histograms
                             // (one per XCD when spread), tickets; a spread plan
