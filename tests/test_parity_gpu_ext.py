@@ -130,7 +130,9 @@ def test_small_segment_kernel(key_type):
     g.manual_seed(303)
     vals = torch.arange(total, dtype=torch.int32, device=DEV)
     say(f"[small kernel {key_type}] segments={len(sizes)} hint={lim}")
-    for levels in (None, 3):
+    # levels=1: two values, so the k-th bucket overflows the stash and the
+    # finish reads the segment again.
+    for levels in (None, 3, 1):
         keys = rand_keys(total, key_type, g, levels)
         for largest in (True, False):
             for det, tb in MODES:
@@ -165,7 +167,7 @@ def test_small_segment_kernel_many_segments(key_type):
     g = torch.Generator(device=DEV)
     g.manual_seed(306)
     vals = torch.arange(total, dtype=torch.int32, device=DEV)
-    for k in (1, 64, 256):
+    for k in (1, 64, 256, 1000, 3000):
         for levels in (None, 8):
             keys = rand_keys(total, key_type, g, levels)
             say(f"[small kernel many {key_type}] k={k} levels={levels}")
