@@ -381,6 +381,10 @@ def main():
     ap.add_argument("--no-probe", action="store_true", help="skip the stream-read probe")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a 256 MiB device copy (counter calibration)")
+    ap.add_argument("--size-hint", type=int, default=None,
+                    help="pass this max_segment_size with the --workload calls (for "
+                         "instance its segment length, which selects the small-segment "
+                         "kernel at 4096 keys or fewer); the default passes none")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/traffic_<workload>.json from two rocprofv3 --pmc "
                          "runs of this script with --copy-probe, then exit")
@@ -403,6 +407,8 @@ def main():
     if a.copy_probe:
         copy_probe()
     probe = None if a.no_probe else stream_read_probe()
+    if a.size_hint is not None:
+        workloads.WORKLOADS[a.workload]["max_segment_size"] = a.size_hint
     head = measure(a.workload, a.steps, a.warmup)
     if probe:
         head["probe_frac"] = head["alg_gbs"] / probe["gbs"]
@@ -440,7 +446,7 @@ def main():
         "vs_baseline": None,
         "dtype": head["key_type"],
         "data": "synthetic",
-        "config": {"workload": a.workload, "segments": head["segments"],
+        "config": {"workload": a.workload, "size_hint": a.size_hint, "segments": head["segments"],
                    "segment_len": head["keys"] // max(1, head["segments"]), "k": head["k"],
                    "mode": head["mode"]},
         "hbm_single_read_roofline_frac": head["hbm_roof_frac"],
