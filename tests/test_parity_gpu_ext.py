@@ -82,6 +82,33 @@ def test_per_segment_k(plan, key_type):
                           values_are="position", k_per_segment=kseg_t)
 
 
+@pytest.mark.parametrize("key_type", ["bf16", "f32"])
+def test_slice_mode_repeated_calls_per_segment_k(key_type):
+    """Back-to-back slice-mode calls on one stream reuse the scratch that each
+    call leaves cleared (merged and shared histograms, tickets): repeated
+    calls with per-segment k (including k_i = 0 and 1) must each match the
+    oracle."""
+    rng = np.random.default_rng(111)
+    sizes = PLANS["sliced"](rng)
+    off, total = offsets_from(sizes, 3)
+    S = len(sizes)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(212)
+    vals = torch.arange(total, dtype=torch.int32, device=DEV)
+    k = 300
+    kseg = rng.integers(-5, k + 50, S).astype(np.int32)
+    kseg[:6] = [0, 1, k, k + 7, 1, 2]
+    kseg_t = torch.from_numpy(kseg).to(DEV)
+    for rep in range(4):
+        keys = rand_keys(total, key_type, g, None if rep % 2 == 0 else 6)
+        say(f"[slice mode repeated {key_type}] call group {rep}")
+        for largest in (True, False):
+            for det, tb in (MODES[0], MODES[3], MODES[4]):
+                check(keys, vals, off, k, key_type, largest, det, tb,
+                      "stable_sorted" if rep < 2 else "unsorted", values_are="position",
+                      k_per_segment=kseg_t)
+
+
 @pytest.mark.parametrize("hint_kind", ["exact", "too_small", "huge"])
 def test_max_segment_size_hint(hint_kind):
     """The hint only steers the plan: results are the same when it is exact,
