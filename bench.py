@@ -279,7 +279,7 @@ def traffic_from(fetch_csv, write_csv, name):
     w_kib, w_copy, n_w = per_kernel(write_csv, "WRITE_SIZE")
     f_scale = copy_bytes / (f_copy * 1024)
     w_scale = copy_bytes / (w_copy * 1024)
-    run = ("cd /tmp && rocprofv3 --pmc {c} --output-format csv -d gpurun_out/tr/{w}/{c} -o p -- "
+    run = ("cd /tmp && rocprofv3 --pmc {c} --output-format csv -d <out dir>/{w}/{c} -o p -- "
            "python3 /root/repo/bench.py --workload {w} --only-headline --no-cpu-baseline --no-probe "
            "--copy-probe --steps 5 --warmup 2")
     out = {
