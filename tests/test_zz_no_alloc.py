@@ -136,3 +136,21 @@ def test_noalloc_refuses_a_plan_larger_than_the_buffer():
     ref = reference(keys, vals, off, 2048, "max", "gpu_to_gpu", "prefer_smaller_index",
                     "unsorted")
     assert same((ok, ov), ref, "unsorted")
+
+
+def test_noalloc_small_segment_kernel_matches_general_kernel():
+    # A hint of at most 4096 keys selects the small-segment kernel (no
+    # scratch); its rows must equal those of the general kernel, which the
+    # same request without a hint takes.
+    for args, k, ordering in (((2100, 3000, 17), 64, "stable_sorted"),
+                              ((700, np.random.default_rng(5).integers(0, 4097, 700), 18, 9),
+                               300, "unsorted")):
+        keys, vals, off = problem(*args)
+        S = off.numel() - 1
+        ok, ov = outputs(S, k)
+        s = torch.cuda.current_stream().cuda_stream
+        assert call(st.raw_call_ex_noalloc, keys, vals, off, k, ok, ov, "max", "gpu_to_gpu",
+                    "prefer_smaller_index", ordering, s, hint=4096) == 0
+        torch.cuda.synchronize()
+        ref = reference(keys, vals, off, k, "max", "gpu_to_gpu", "prefer_smaller_index", ordering)
+        assert same((ok, ov), ref, ordering)
